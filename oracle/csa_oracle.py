@@ -1,0 +1,124 @@
+"""ctypes wrapper of oracle.c (test infrastructure; see oracle.c's header).
+
+The wrapper marshals numpy arrays only; every step of the computation is in
+oracle.c.  It does not import the product package: any object with the shape
+fields (batch, q_per_req, ratio, ...) is accepted.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+JOB_SCORE, JOB_TOPK, JOB_ATTN = 1, 2, 4
+
+_FIELDS = ("batch", "q_per_req", "ratio", "n_cap", "topk", "win", "w_cap", "heads",
+           "head_dim", "rope_dim", "idx_heads", "idx_dim", "out_groups", "max_len", "dtype")
+
+
+class _OShape(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in _FIELDS]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-pthread", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_n_vis.restype = ctypes.c_int32
+        lib.oracle_n_vis.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        lib.oracle_select_row.restype = ctypes.c_int32
+        lib.oracle_select_row.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p]
+        lib.oracle_round_bf16.restype = ctypes.c_float
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_run.restype = ctypes.c_int32
+        lib.oracle_run.argtypes = ([ctypes.POINTER(_OShape)] + [ctypes.c_int32] * 4
+                                   + [ctypes.c_void_p] * 13 + [ctypes.c_int32, ctypes.c_float,
+                                                               ctypes.c_void_p])
+        _lib = lib
+    return _lib
+
+
+def n_vis(p: int, ratio: int) -> int:
+    return int(_get().oracle_n_vis(int(p), int(ratio)))
+
+
+def round_bf16(x: float) -> float:
+    return float(_get().oracle_round_bf16(float(x)))
+
+
+def select_row(scores: np.ndarray, k: int, n: Optional[int] = None) -> np.ndarray:
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    n = s.shape[0] if n is None else n
+    out = np.empty(k, dtype=np.int32)
+    rc = _get().oracle_select_row(s.ctypes.data, n, k, out.ctypes.data)
+    if rc:
+        raise RuntimeError(f"oracle_select_row failed ({rc})")
+    return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def run(shape, inp: dict, jobs: int = JOB_SCORE | JOB_TOPK | JOB_ATTN, scale: Optional[float] = None,
+        scores: Optional[np.ndarray] = None, topk_idx: Optional[np.ndarray] = None,
+        tokens: Optional[tuple] = None, nthreads: int = 1) -> dict:
+    """Run the chosen steps over tokens [t0, t1) (all tokens by default).
+
+    `inp` is the dict from the seeded input generator.  `scores` / `topk_idx`
+    may be given to start from a later step; otherwise they are allocated
+    (scores filled with NaN, so untouched entries stay recognisable).
+    Returns dict(scores, topk_idx, out) with out as float32 [G, B*S, (H/G)*D].
+    """
+    sh = _OShape(*[int(getattr(shape, f)) for f in _FIELDS])
+    B, S, K, Nc = shape.batch, shape.q_per_req, shape.topk, shape.n_cap
+    H, D, G = shape.heads, shape.head_dim, shape.out_groups
+    if scores is None:
+        scores = np.full((B, S, Nc), np.nan, dtype=np.float32)
+    else:
+        scores = np.ascontiguousarray(scores, dtype=np.float32).copy()
+    if topk_idx is None:
+        topk_idx = inp.get("topk_idx")
+        topk_idx = (np.full((B, S, K), -7, dtype=np.int32) if topk_idx is None
+                    else np.ascontiguousarray(topk_idx, np.int32).copy())
+    else:
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32).copy()
+    out = np.full((G, B * S, (H // G) * D), np.nan, dtype=np.float32)
+    if scale is None:
+        scale = float(np.float32(1.0 / np.sqrt(D)))
+    t0, t1 = (0, B * S) if tokens is None else tokens
+    a = {k: (np.ascontiguousarray(v) if v is not None else None) for k, v in inp.items()}
+    rc = _get().oracle_run(
+        ctypes.byref(sh), int(jobs), int(t0), int(t1), int(nthreads),
+        _ptr(a.get("q_idx")), _ptr(a.get("w")), _ptr(a.get("k_idx")), _ptr(a["start_pos"]),
+        scores.ctypes.data, topk_idx.ctypes.data,
+        _ptr(a.get("q")), _ptr(a.get("k_win")), _ptr(a.get("v_win")), _ptr(a.get("k_cmp")),
+        _ptr(a.get("v_cmp")), _ptr(a.get("rope_cos")), _ptr(a.get("rope_sin")),
+        int(a["rope_cos"].shape[0]) if a.get("rope_cos") is not None else 0,
+        float(scale), out.ctypes.data)
+    if rc:
+        raise RuntimeError(f"oracle_run failed with code {rc}")
+    return dict(scores=scores, topk_idx=topk_idx, out=out)

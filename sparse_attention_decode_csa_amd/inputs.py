@@ -1,0 +1,323 @@
+"""Seeded synthetic inputs for the CSA sparse-attention decode step.
+
+This module only draws and lays out data: it holds none of the step's own
+arithmetic (no scoring, selection, softmax or rotation of outputs).  The CPU
+oracle and the HIP path both consume what it returns, so the two always see
+bit-identical inputs.
+
+Every tensor comes from its own child stream ``np.random.default_rng([seed,
+tensor_id])`` in a fixed tensor order, so one tensor can be regenerated
+without drawing the others.  Floating-point values are drawn in float32 and,
+for the bf16 configurations, rounded to bf16 with round-to-nearest-even;
+bf16 tensors are returned as ``np.uint16`` bit patterns.
+
+Workload shapes follow the pages' decode setting ("Perf: skip redundant CSA
+scoring and fuse gather unpack", description: ratio-4 compressed cache, Top-K
+with a bypass when the cache fits; "Perf: fuse HCA merge, inverse RoPE, and
+packing", description: B=16, S=8, 64 compressed rows, two output groups).
+No public dataset is involved: all structure (lengths, planted winners,
+duplicated rows, poison) is synthetic and documented per configuration.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+# Value written into every cache row the step must not read (compressed rows
+# past the causal horizon, ring slots outside the live window).  A leak of such
+# a row into a score or a softmax changes the result by orders of magnitude.
+POISON = 1.0e4
+
+F32 = 0
+BF16 = 1
+
+# tensor ids of the child streams (fixed order; never renumber)
+_T_START, _T_Q, _T_KWIN, _T_VWIN, _T_KCMP, _T_VCMP, _T_QIDX, _T_W, _T_KIDX, _T_STRUCT = range(10)
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    """Problem sizes of one decode step (field names match the C ABI)."""
+
+    batch: int          # B requests
+    q_per_req: int      # S query tokens per request (positions start_pos+0 .. start_pos+S-1)
+    ratio: int          # R raw tokens per compressed row
+    n_cap: int          # compressed rows allocated per request
+    topk: int           # K (IDX_TOPK)
+    win: int            # sliding-window length
+    w_cap: int          # ring capacity of the window cache
+    heads: int          # H query heads (one shared KV head)
+    head_dim: int       # D
+    rope_dim: int       # Dr: the last Dr dims carry interleaved RoPE pairs
+    idx_heads: int      # Hi indexer heads
+    idx_dim: int        # Di indexer head dim
+    out_groups: int     # G output head groups
+    max_len: int        # host bound: max_b start_pos[b] + S
+    dtype: int          # F32 or BF16
+
+    def replace(self, **kw) -> "Shape":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    shape: Shape
+    seed: int
+    lengths: str          # how start_pos is drawn (documentation + dispatch key)
+    structure: str        # extra structure planted into the indexer keys
+    supplied_topk: bool   # True: the harness supplies topk_idx (attention only)
+
+
+def _shape(**kw) -> Shape:
+    return Shape(**kw)
+
+
+CONFIGS: Dict[int, Config] = {
+    0: Config(
+        name="tiny_fp32",
+        shape=_shape(batch=1, q_per_req=1, ratio=4, n_cap=256, topk=64, win=64, w_cap=64,
+                     heads=4, head_dim=64, rope_dim=32, idx_heads=2, idx_dim=64,
+                     out_groups=1, max_len=1024, dtype=F32),
+        seed=0, lengths="fixed:1024", structure="none", supplied_topk=False),
+    1: Config(
+        name="bypass",
+        shape=_shape(batch=16, q_per_req=1, ratio=4, n_cap=256, topk=512, win=128, w_cap=128,
+                     heads=16, head_dim=128, rope_dim=64, idx_heads=4, idx_dim=128,
+                     out_groups=1, max_len=1024, dtype=BF16),
+        seed=1, lengths="start_uniform:0:1023", structure="none", supplied_topk=False),
+    2: Config(
+        name="hca_merge",
+        shape=_shape(batch=16, q_per_req=8, ratio=4, n_cap=64, topk=64, win=128, w_cap=256,
+                     heads=16, head_dim=128, rope_dim=64, idx_heads=4, idx_dim=128,
+                     out_groups=2, max_len=4096 + 8, dtype=BF16),
+        seed=2, lengths="start_uniform:0:4095", structure="none", supplied_topk=True),
+    3: Config(
+        name="long_context",
+        shape=_shape(batch=16, q_per_req=1, ratio=4, n_cap=16384, topk=512, win=128, w_cap=128,
+                     heads=16, head_dim=128, rope_dim=64, idx_heads=4, idx_dim=128,
+                     out_groups=1, max_len=65536, dtype=BF16),
+        seed=3, lengths="len_uniform:32768:65536", structure="planted:256", supplied_topk=False),
+    4: Config(
+        name="wide_topk",
+        shape=_shape(batch=64, q_per_req=2, ratio=4, n_cap=32768, topk=1024, win=256, w_cap=512,
+                     heads=16, head_dim=128, rope_dim=64, idx_heads=8, idx_dim=128,
+                     out_groups=1, max_len=131072, dtype=BF16),
+        seed=4, lengths="fixed:131072", structure="dup:0.01", supplied_topk=False),
+}
+
+
+# ----------------------------------------------------------------------------
+# dtype helpers (data formatting only)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    For finite inputs the biased sum stays below 2**32, so uint32 arithmetic
+    cannot wrap.
+    """
+    u = np.array(x, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def as_float(a: np.ndarray, dtype: int) -> np.ndarray:
+    """Values of an input tensor as float32 (exact for both storage types)."""
+    return bf16_bits_to_f32(a) if dtype == BF16 else np.asarray(a, dtype=np.float32)
+
+
+def _store(x: np.ndarray, dtype: int) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == BF16 else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _rng(seed: int, tid: int) -> np.random.Generator:
+    return np.random.default_rng([seed, tid])
+
+
+def _normal(seed: int, tid: int, shape) -> np.ndarray:
+    return _rng(seed, tid).standard_normal(size=shape, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# positions, RoPE tables
+# ----------------------------------------------------------------------------
+
+def draw_start_pos(cfg: Config, seed: int, shape: Shape) -> np.ndarray:
+    """start_pos[b]: position of request b's first query token."""
+    kind, *args = cfg.lengths.split(":")
+    B, S = shape.batch, shape.q_per_req
+    g = _rng(seed, _T_START)
+    if kind == "fixed":            # context L for every request: last token at L-1
+        L = int(args[0])
+        sp = np.full(B, L - S, dtype=np.int64)
+    elif kind == "start_uniform":  # start positions uniform on [lo, hi]
+        lo, hi = int(args[0]), int(args[1])
+        sp = g.integers(lo, hi + 1, size=B)
+    elif kind == "len_uniform":    # context lengths uniform on [lo, hi], last token at L-1
+        lo, hi = int(args[0]), int(args[1])
+        sp = g.integers(lo, hi + 1, size=B) - S
+    else:
+        raise ValueError(cfg.lengths)
+    return np.ascontiguousarray(sp, dtype=np.int32)
+
+
+def rope_tables(rows: int, rope_dim: int, base: float = 10000.0):
+    """cos/sin tables [rows][rope_dim/2] in float32 for interleaved RoPE pairs.
+
+    Pair i (dims 2i, 2i+1 of the RoPE block) turns by angle p * base^(-2i/rope_dim)
+    at position p.  Angles and trig are evaluated in float64 and rounded once.
+    """
+    half = rope_dim // 2
+    if half == 0:
+        z = np.zeros((rows, 0), dtype=np.float32)
+        return z, z.copy()
+    inv = base ** (-2.0 * np.arange(half, dtype=np.float64) / rope_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# the full input set
+# ----------------------------------------------------------------------------
+
+def visible_rows(p: np.ndarray, ratio: int) -> np.ndarray:
+    """Compressed rows whose whole raw-token block lies at or before position p.
+
+    Used only to decide which rows to poison; the oracle and the kernels derive
+    visibility themselves.
+    """
+    return (np.asarray(p, dtype=np.int64) + 1) // ratio
+
+
+def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
+                shape: Optional[Shape] = None, start_pos: Optional[np.ndarray] = None,
+                structure: Optional[str] = None) -> Dict[str, np.ndarray]:
+    """Draw every input of one decode step.
+
+    Returns a dict of contiguous numpy arrays:
+      start_pos [B] int32, q [B,S,H,D], k_win/v_win [B,W_cap,D],
+      k_cmp/v_cmp [B,N_cap,D], q_idx [B,S,Hi,Di], w [B,S,Hi] float32,
+      k_idx [B,N_cap,Di], rope_cos/rope_sin [max_len, Dr/2] float32 and,
+      for configurations whose harness supplies the selection,
+      topk_idx [B,S,K] int32.
+    Storage is uint16 (bf16 bits) or float32 according to shape.dtype.
+    """
+    cfg = CONFIGS[cfg_id_or_cfg] if isinstance(cfg_id_or_cfg, int) else cfg_id_or_cfg
+    sh = shape or cfg.shape
+    seed = cfg.seed if seed is None else seed
+    structure = cfg.structure if structure is None else structure
+    B, S, H, D = sh.batch, sh.q_per_req, sh.heads, sh.head_dim
+    Hi, Di, Nc, Wc = sh.idx_heads, sh.idx_dim, sh.n_cap, sh.w_cap
+    dt = sh.dtype
+
+    sp = draw_start_pos(cfg, seed, sh) if start_pos is None else np.ascontiguousarray(start_pos, np.int32)
+    assert sp.shape == (B,)
+    assert int(sp.min(initial=0)) >= 0 and int((sp + S).max(initial=0)) <= sh.max_len
+
+    # Independent child streams: drawing them on threads changes no value.
+    jobs = dict(q=(_T_Q, (B, S, H, D)), k_win=(_T_KWIN, (B, Wc, D)), v_win=(_T_VWIN, (B, Wc, D)),
+                k_cmp=(_T_KCMP, (B, Nc, D)), v_cmp=(_T_VCMP, (B, Nc, D)),
+                q_idx=(_T_QIDX, (B, S, Hi, Di)), k_idx=(_T_KIDX, (B, Nc, Di)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        futs = {k: ex.submit(_normal, seed, tid, shp) for k, (tid, shp) in jobs.items()}
+        drawn = {k: f.result() for k, f in futs.items()}
+    q, k_win, v_win = drawn["q"], drawn["k_win"], drawn["v_win"]
+    k_cmp, v_cmp, q_idx, k_idx = drawn["k_cmp"], drawn["v_cmp"], drawn["q_idx"], drawn["k_idx"]
+    w = _rng(seed, _T_W).random(size=(B, S, Hi), dtype=np.float32)
+
+    g = _rng(seed, _T_STRUCT)
+    last_vis = np.minimum(visible_rows(sp + S - 1, sh.ratio), Nc)   # rows visible to the last token
+    kind, _, arg = structure.partition(":")
+    if kind == "planted":
+        # Rows aligned with the request's weighted indexer query score far above
+        # the N(0,1) rows, so they must win Top-K wherever they sit.
+        n_plant = int(arg)
+        qi = as_float(_store(q_idx, dt), dt).astype(np.float64)
+        for b in range(B):
+            nv = int(last_vis[b])
+            if nv <= sh.topk:
+                continue
+            m = min(n_plant, nv)
+            pos = g.choice(nv, size=m, replace=False)
+            u = np.einsum("h,hc->c", w[b, 0].astype(np.float64), qi[b, 0])
+            u /= np.linalg.norm(u)
+            alpha = g.uniform(1.0, 2.0, size=m)
+            k_idx[b, pos] = (alpha[:, None] * np.sqrt(Di) * u[None, :]).astype(np.float32)
+    elif kind == "dup":
+        # A fraction of rows copy another row's indexer key, so exact score ties
+        # occur on both sides of every comparison.
+        frac = float(arg)
+        for b in range(B):
+            nv = int(last_vis[b])
+            nd = int(round(frac * nv))
+            if nd == 0 or nv < 2:
+                continue
+            dst = g.choice(nv, size=nd, replace=False)
+            src = g.integers(0, nv, size=nd)
+            k_idx[b, dst] = k_idx[b, src]
+    elif kind != "none":
+        raise ValueError(structure)
+
+    if poison:
+        for b in range(B):
+            nv = int(last_vis[b])
+            if not cfg.supplied_topk:
+                k_cmp[b, nv:] = POISON
+                v_cmp[b, nv:] = POISON
+            k_idx[b, nv:] = POISON
+            lo = max(0, int(sp[b]) - sh.win + 1)
+            hi = int(sp[b]) + S - 1
+            live = np.zeros(Wc, dtype=bool)
+            live[np.arange(lo, hi + 1) % Wc] = True
+            k_win[b, ~live] = POISON
+            v_win[b, ~live] = POISON
+
+    cos, sin = rope_tables(sh.max_len, sh.rope_dim)
+    raw = dict(q=q, k_win=k_win, v_win=v_win, k_cmp=k_cmp, v_cmp=v_cmp, q_idx=q_idx, k_idx=k_idx)
+    del q, k_win, v_win, k_cmp, v_cmp, q_idx, k_idx, drawn
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(raw)) as ex:
+        futs = {k: ex.submit(_store, v, dt) for k, v in raw.items()}
+        out = {k: f.result() for k, f in futs.items()}
+    del raw
+    out.update(start_pos=sp, w=np.ascontiguousarray(w, np.float32), rope_cos=cos, rope_sin=sin)
+    if cfg.supplied_topk:
+        # The HCA-shaped case attends every compressed row it is given.
+        K = sh.topk
+        ti = np.full((B, S, K), -1, dtype=np.int32)
+        n = min(K, Nc)
+        ti[:, :, :n] = np.arange(n, dtype=np.int32)
+        out["topk_idx"] = ti
+    return out
+
+
+def softmax_scale(shape: Shape) -> float:
+    """fp32(1/sqrt(D)), the scale every configuration uses."""
+    return float(np.float32(1.0 / np.sqrt(shape.head_dim)))
+
+
+def random_scores(seed: int, B: int, S: int, n_cap: int, kind: str = "normal") -> np.ndarray:
+    """Synthetic fp32 score rows for exercising selection on its own."""
+    g = np.random.default_rng([seed, 101])
+    if kind == "normal":
+        return g.standard_normal(size=(B, S, n_cap), dtype=np.float32)
+    if kind == "coarse":   # few distinct values: heavy ties
+        return (g.integers(-8, 9, size=(B, S, n_cap)) / 4.0).astype(np.float32)
+    if kind == "signed_zero":
+        s = g.integers(0, 3, size=(B, S, n_cap)).astype(np.float32) - 1.0
+        z = g.random(size=(B, S, n_cap)) < 0.5
+        s[(s == 0) & z] = -0.0
+        return s
+    raise ValueError(kind)

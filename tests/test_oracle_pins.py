@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one step of the oracle to brute force, a library routine, a
+closed form, an invariant, or the hand-worked golden case, chosen so that a
+plausible slip (a dropped term, a wrong sign or index, a transposed operand,
+an off-by-one in visibility, a wrong tie rule) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_csa_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small_shape(**kw):
+    base = dict(batch=3, q_per_req=2, ratio=4, n_cap=64, topk=8, win=8, w_cap=12, heads=4,
+                head_dim=16, rope_dim=8, idx_heads=3, idx_dim=16, out_groups=1, max_len=240,
+                dtype=I.F32)
+    base.update(kw)
+    return I.Shape(**base)
+
+
+def small_inputs(shape, seed=7, start_pos=None, **kw):
+    cfg = I.Config(name="t", shape=shape, seed=seed, lengths=f"start_uniform:0:{shape.max_len - shape.q_per_req}",
+                   structure="none", supplied_topk=False)
+    return I.make_inputs(cfg, start_pos=start_pos, **kw)
+
+
+def fvals(a, dt):
+    return I.as_float(a, dt).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# hand-worked golden case
+# --------------------------------------------------------------------------
+
+def _golden_inputs(g):
+    sh = I.Shape(**g["shape"])
+    gi = g["inputs"]
+
+    def arr(name):
+        return np.array([[[math.log(3.0) if v == "ln3" else v for v in row] for row in blk]
+                         for blk in gi[name]], dtype=np.float32)
+
+    inp = dict(start_pos=np.array(gi["start_pos"], np.int32),
+               q_idx=np.array(gi["q_idx"], np.float32), w=np.array(gi["w"], np.float32),
+               k_idx=arr("k_idx"), q=np.array(gi["q"], np.float32), k_win=arr("k_win"),
+               v_win=arr("v_win"), k_cmp=arr("k_cmp"), v_cmp=arr("v_cmp"))
+    cos = np.ones((sh.max_len, 1), np.float32)
+    sin = np.zeros((sh.max_len, 1), np.float32)
+    for p, (c, s) in gi["rope_rows"].items():
+        cos[int(p), 0], sin[int(p), 0] = c, s
+    inp["rope_cos"], inp["rope_sin"] = cos, sin
+    return sh, inp
+
+
+def test_golden_hand_worked():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked.json")))
+    sh, inp = _golden_inputs(g)
+    r = oracle.run(sh, inp, scale=g["softmax_scale"])
+    exp_s = np.array([[np.nan if v is None else v for v in row] for row in g["expected"]["scores"]],
+                     np.float32)
+    got_s = r["scores"][:, 0, :]
+    assert np.array_equal(np.isnan(got_s), np.isnan(exp_s))
+    assert np.array_equal(got_s[~np.isnan(exp_s)], exp_s[~np.isnan(exp_s)])
+    assert r["topk_idx"][:, 0, :].tolist() == g["expected"]["topk_idx"]
+    np.testing.assert_allclose(r["out"], np.array(g["expected"]["out"], np.float32), rtol=0, atol=2e-6)
+
+
+# --------------------------------------------------------------------------
+# visibility and bypass
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ratio", [1, 2, 4, 8])
+def test_visibility_brute_force(ratio):
+    for p in range(0, 4096):
+        # rows whose whole block [R*j, R*j+R-1] lies at or before p
+        brute = sum(1 for j in range(p // ratio + 2) if ratio * j + ratio - 1 <= p)
+        assert oracle.n_vis(p, ratio) == brute, (p, ratio)
+
+
+def test_bypass_boundary_and_equivalence():
+    # K = 8: n_vis = 8 bypasses, n_vis = 9 runs the selection.
+    sh = small_shape(batch=4, q_per_req=1, topk=8, n_cap=16, max_len=64)
+    sp = np.array([31, 32, 35, 0], np.int32)         # n_vis 8, 8, 9, 0
+    inp = small_inputs(sh, start_pos=sp)
+    sc = I.random_scores(3, sh.batch, 1, sh.n_cap)
+    r = oracle.run(sh, inp, jobs=oracle.JOB_TOPK, scores=sc)
+    ti = r["topk_idx"][:, 0, :]
+    assert ti[0].tolist() == list(range(8))
+    assert ti[1].tolist() == list(range(8))
+    assert ti[3].tolist() == [-1] * 8
+    # the selection on the same row with every visible row fitting gives the same list
+    for b, n in ((0, 8), (1, 8)):
+        assert oracle.select_row(sc[b, 0], 8, n=n).tolist() == ti[b].tolist()
+    # n_vis = 9 > K: the selection drops exactly the worst of the 9
+    worst = np.lexsort((-np.arange(9), sc[2, 0, :9]))[0]   # lowest score, higher index loses ties
+    assert sorted(set(range(9)) - {int(worst)}) == ti[2].tolist()
+    # scores of bypass tokens are not computed
+    r2 = oracle.run(sh, inp, jobs=oracle.JOB_SCORE)
+    assert np.isnan(r2["scores"][[0, 1, 3]]).all()
+    assert not np.isnan(r2["scores"][2, 0, :9]).any() and np.isnan(r2["scores"][2, 0, 9:]).all()
+
+
+# --------------------------------------------------------------------------
+# Top-K selection against a library sort
+# --------------------------------------------------------------------------
+
+def lexsort_topk(row, k):
+    order = np.lexsort((np.arange(row.size), -row.astype(np.float64)))
+    sel = np.sort(order[:k])
+    return np.concatenate([sel, -np.ones(k - sel.size, dtype=np.int64)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero"])
+@pytest.mark.parametrize("n,k", [(1, 1), (5, 3), (64, 64), (300, 7), (1000, 256), (1000, 257),
+                                 (3000, 1024), (40, 64)])
+def test_select_row_vs_lexsort(kind, n, k):
+    row = I.random_scores(n * 7 + k, 1, 1, n, kind)[0, 0]
+    assert oracle.select_row(row, k).tolist() == lexsort_topk(row, k).tolist()
+
+
+@pytest.mark.parametrize("k", [256, 257, 1024])
+def test_topk_winners_past_256(k):
+    # Winners planted beyond the first 256 candidates must be found (the merge
+    # stage past width 256 named in the prefill indexer fix).
+    g = np.random.default_rng(11)
+    n = 4096
+    row = g.standard_normal(n).astype(np.float32)
+    planted = g.choice(np.arange(257, n), size=min(k, 200), replace=False)
+    row[planted] = 50.0 + g.random(planted.size).astype(np.float32)
+    got = oracle.select_row(row, k)
+    assert set(planted.tolist()) <= set(got.tolist())
+    assert got.tolist() == lexsort_topk(row, k).tolist()
+
+
+def test_signed_zero_ties():
+    row = np.array([0.0, -0.0, 0.0, -0.0, -1.0, 1.0], np.float32)
+    # +0 and -0 are equal scores: the lower indices win
+    assert oracle.select_row(row, 3).tolist() == [0, 1, 5]
+
+
+# --------------------------------------------------------------------------
+# indexer scores
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", [I.F32, I.BF16])
+def test_scores_vs_einsum(dt):
+    sh = small_shape(dtype=dt, topk=4)
+    inp = small_inputs(sh)
+    r = oracle.run(sh, inp, jobs=oracle.JOB_SCORE)
+    q = fvals(inp["q_idx"], dt)
+    k = fvals(inp["k_idx"], dt)
+    d = np.einsum("bshc,bjc->bshj", q, k)
+    ref = np.einsum("bsh,bshj->bsj", inp["w"].astype(np.float64), np.maximum(d, 0.0))
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            n = oracle.n_vis(int(inp["start_pos"][b]) + s, sh.ratio)
+            got = r["scores"][b, s]
+            if n <= sh.topk:
+                assert np.isnan(got).all()
+                continue
+            np.testing.assert_allclose(got[:n], ref[b, s, :n], rtol=2e-7, atol=1e-6)
+            assert np.isnan(got[n:]).all()
+
+
+def test_scores_exact_grid():
+    # Values on a coarse dyadic grid make every partial sum exact in fp32, so
+    # the score equals the integer-arithmetic result exactly.
+    sh = small_shape(dtype=I.BF16, topk=2, idx_heads=4, idx_dim=16)
+    inp = small_inputs(sh)
+    g = np.random.default_rng(5)
+    qm = g.integers(-8, 9, size=inp["q_idx"].shape)
+    km = g.integers(-8, 9, size=inp["k_idx"].shape)
+    wm = g.integers(0, 17, size=inp["w"].shape)
+    inp["q_idx"] = I.f32_to_bf16_bits((qm / 4.0).astype(np.float32))
+    inp["k_idx"] = I.f32_to_bf16_bits((km / 4.0).astype(np.float32))
+    inp["w"] = (wm / 16.0).astype(np.float32)
+    r = oracle.run(sh, inp, jobs=oracle.JOB_SCORE)
+    d = np.einsum("bshc,bjc->bshj", qm, km)                          # integer, x16
+    ref = np.einsum("bsh,bshj->bsj", wm, np.maximum(d, 0)) / 256.0      # exact
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            n = oracle.n_vis(int(inp["start_pos"][b]) + s, sh.ratio)
+            if n > sh.topk:
+                assert np.array_equal(r["scores"][b, s, :n], ref[b, s, :n].astype(np.float32))
+
+
+# --------------------------------------------------------------------------
+# attention: library attention on the concatenated rows, closed forms
+# --------------------------------------------------------------------------
+
+def gather_rows(sh, inp, topk_idx, b, s, dt):
+    p = int(inp["start_pos"][b]) + s
+    pos = np.arange(max(0, p - sh.win + 1), p + 1)
+    kw = fvals(inp["k_win"], dt)[b, pos % sh.w_cap]
+    vw = fvals(inp["v_win"], dt)[b, pos % sh.w_cap]
+    sel = [j for j in topk_idx[b, s] if 0 <= j < sh.n_cap]
+    kc = fvals(inp["k_cmp"], dt)[b, sel]
+    vc = fvals(inp["v_cmp"], dt)[b, sel]
+    return p, np.concatenate([kw, kc]), np.concatenate([vw, vc])
+
+
+def sdpa_ref(sh, inp, topk_idx, dt, scale):
+    """torch fp64 attention over the concatenated window + selected rows."""
+    B, S, H, D = sh.batch, sh.q_per_req, sh.heads, sh.head_dim
+    res = np.zeros((B, S, H, D))
+    q = fvals(inp["q"], dt)
+    for b in range(B):
+        for s in range(S):
+            _, k, v = gather_rows(sh, inp, topk_idx, b, s, dt)
+            o = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b, s])[None, :, None, :].contiguous(),
+                torch.from_numpy(k)[None, None].expand(1, H, -1, -1).contiguous(),
+                torch.from_numpy(v)[None, None].expand(1, H, -1, -1).contiguous(),
+                scale=scale)
+            res[b, s] = o[0, :, 0].numpy()
+    return res
+
+
+def unpack(sh, out):
+    """[G, B*S, Hg*D] -> [B, S, H, D]"""
+    G, H, D = sh.out_groups, sh.heads, sh.head_dim
+    o = out.reshape(G, sh.batch * sh.q_per_req, H // G, D).transpose(1, 0, 2, 3)
+    return o.reshape(sh.batch, sh.q_per_req, H, D)
+
+
+@pytest.mark.parametrize("dt", [I.F32, I.BF16])
+def test_attention_vs_sdpa(dt):
+    sh = small_shape(dtype=dt, rope_dim=0)
+    # include early positions: empty compressed stream and partial windows
+    sp = np.array([0, 5, 200], np.int32)
+    inp = small_inputs(sh, start_pos=sp)
+    r = oracle.run(sh, inp)
+    ref = sdpa_ref(sh, inp, r["topk_idx"], dt, I.softmax_scale(sh))
+    got = unpack(sh, r["out"])
+    if dt == I.F32:
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+    else:   # one bf16 rounding of the result
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+def rope_forward(sh, inp, x_bshd):
+    """Apply forward RoPE (interleaved pairs of the last Dr dims) at each token's position."""
+    D, Dr = sh.head_dim, sh.rope_dim
+    y = x_bshd.astype(np.float64).copy()
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            p = int(inp["start_pos"][b]) + s
+            c = inp["rope_cos"][p].astype(np.float64)
+            sn = inp["rope_sin"][p].astype(np.float64)
+            xa = y[b, s, :, D - Dr::2].copy()
+            xb = y[b, s, :, D - Dr + 1::2].copy()
+            y[b, s, :, D - Dr::2] = xa * c - xb * sn
+            y[b, s, :, D - Dr + 1::2] = xa * sn + xb * c
+    return y
+
+
+def test_inverse_rope_roundtrip():
+    sh = small_shape(rope_dim=8)
+    sp = np.array([0, 17, 230], np.int32)
+    inp = small_inputs(sh, start_pos=sp)
+    with_rope = unpack(sh, oracle.run(sh, inp)["out"])
+    no_rope = unpack(sh, oracle.run(sh.replace(rope_dim=0), inp)["out"])
+    back = rope_forward(sh, inp, with_rope)
+    np.testing.assert_allclose(back, no_rope, rtol=0, atol=2e-6)
+    # the rotation is not the identity away from p = 0, only the last Dr dims move
+    assert np.abs(with_rope[1:, ..., -8:] - no_rope[1:, ..., -8:]).max() > 1e-2
+    assert np.array_equal(with_rope[..., :-8], no_rope[..., :-8])
+    # p = 0 is the identity
+    assert np.array_equal(with_rope[0, 0], no_rope[0, 0])
+
+
+def test_zero_query_gives_mean_of_values():
+    sh = small_shape(rope_dim=0)
+    inp = small_inputs(sh, start_pos=np.array([3, 60, 150], np.int32))
+    inp["q"] = np.zeros_like(inp["q"])
+    r = oracle.run(sh, inp)
+    got = unpack(sh, r["out"])
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            _, _, v = gather_rows(sh, inp, r["topk_idx"], b, s, sh.dtype)
+            np.testing.assert_allclose(got[b, s], np.broadcast_to(v.mean(0), got[b, s].shape),
+                                       rtol=1e-6, atol=1e-7)
+
+
+def test_identical_keys_give_mean_of_values():
+    sh = small_shape(rope_dim=0)
+    inp = small_inputs(sh, start_pos=np.array([40, 60, 150], np.int32))
+    r0 = oracle.run(sh, inp)       # selection from the real keys
+    key = np.random.default_rng(2).standard_normal(sh.head_dim).astype(np.float32)
+    inp["k_win"][:] = key
+    inp["k_cmp"][:] = key
+    r = oracle.run(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=r0["topk_idx"])
+    got = unpack(sh, r["out"])
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            _, _, v = gather_rows(sh, inp, r0["topk_idx"], b, s, sh.dtype)
+            np.testing.assert_allclose(got[b, s], np.broadcast_to(v.mean(0), got[b, s].shape),
+                                       rtol=1e-6, atol=1e-7)
+
+
+def test_empty_compressed_stream_is_window_only():
+    sh = small_shape(rope_dim=0)
+    inp = small_inputs(sh, start_pos=np.array([0, 1, 100], np.int32))
+    ti = np.full((sh.batch, sh.q_per_req, sh.topk), -1, np.int32)   # nothing selected
+    r = oracle.run(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=ti)
+    ref = sdpa_ref(sh, inp, ti, sh.dtype, I.softmax_scale(sh))
+    np.testing.assert_allclose(unpack(sh, r["out"]), ref, rtol=1e-6, atol=1e-7)
+
+
+def test_poison_is_never_read():
+    sh = small_shape(dtype=I.BF16)
+    inp = small_inputs(sh, start_pos=np.array([10, 77, 130], np.int32))
+    r1 = oracle.run(sh, inp)
+    big = I.f32_to_bf16_bits(np.array([I.POISON], np.float32))[0]
+    other = I.f32_to_bf16_bits(np.array([-3.0e3], np.float32))[0]
+    n_poison = 0
+    for name in ("k_idx", "k_cmp", "v_cmp", "k_win", "v_win"):
+        m = inp[name] == big
+        n_poison += int(m.sum())
+        inp[name][m] = other
+    assert n_poison > 0
+    r2 = oracle.run(sh, inp)
+    assert np.array_equal(r1["topk_idx"], r2["topk_idx"])
+    assert np.array_equal(r1["out"], r2["out"])
+    assert np.array_equal(np.isnan(r1["scores"]), np.isnan(r2["scores"]))
+
+
+def test_group_packing_is_a_permutation():
+    sh1 = small_shape(heads=4, out_groups=1)
+    inp = small_inputs(sh1)
+    o1 = oracle.run(sh1, inp)["out"]
+    o2 = oracle.run(sh1.replace(out_groups=2), inp)["out"]
+    # group g holds heads [2g, 2g+1] of every token, in the G = 1 order
+    T, D = sh1.batch * sh1.q_per_req, sh1.head_dim
+    a = o1.reshape(T, 2, 2 * D)
+    assert np.array_equal(o2[0], a[:, 0])
+    assert np.array_equal(o2[1], a[:, 1])
+
+
+def test_round_bf16_matches_library():
+    g = np.random.default_rng(3)
+    xs = np.concatenate([g.standard_normal(2000) * 10.0 ** g.integers(-5, 6, 2000),
+                         [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8)]])
+    # fp32-representable inputs, so a library rounding via fp32 is not a double rounding
+    for x in xs.astype(np.float32).astype(np.float64):
+        ref = torch.tensor([x], dtype=torch.float64).to(torch.bfloat16).item()
+        assert oracle.round_bf16(float(x)) == ref
+
+
+def test_thread_count_does_not_change_results():
+    sh = small_shape(batch=5)
+    inp = small_inputs(sh)
+    a = oracle.run(sh, inp, nthreads=1)
+    b = oracle.run(sh, inp, nthreads=4)
+    for k in ("topk_idx", "out"):
+        assert np.array_equal(a[k], b[k])
+    assert np.array_equal(a["scores"], b["scores"], equal_nan=True)
+
+
+def test_out_of_range_indices_are_padding():
+    # Entries outside [0, N_cap) in a Top-K list carry no row: the result equals
+    # the list with those entries replaced by -1.
+    sh = small_shape(rope_dim=0, batch=3)
+    inp = small_inputs(sh, start_pos=np.array([100, 120, 140], np.int32))
+    ti = oracle.run(sh, inp)["topk_idx"]
+    ti_bad = ti.copy()
+    ti_bad[0, :, :3] = [sh.n_cap, sh.n_cap + 1, -5]     # would read request 1's rows if used
+    ti_pad = ti.copy()
+    ti_pad[0, :, :3] = -1
+    a = oracle.run(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=ti_bad)["out"]
+    b = oracle.run(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=ti_pad)["out"]
+    c = oracle.run(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=ti)["out"]
+    assert np.array_equal(a, b)
+    assert not np.array_equal(a, c)
