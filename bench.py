@@ -1,0 +1,265 @@
+"""Benchmark of one CSA sparse-attention decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+
+A step is one pass of the whole path on one batch of seeded synthetic input
+already resident in HBM: indexer scoring, Top-K (with the fits-in-Top-K
+bypass), and two-stream attention with the fused merge / inverse RoPE /
+packing epilogue, issued through the C ABI on one stream.
+
+Prints ONE JSON line: query tokens per second over the timed steps, the
+roofline of the dominant kernel (algorithmic bytes / its HIP-event-timed
+average duration against 8 TB/s), per-stage figures, and the CPU oracle timed
+on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "sparse_attention_decode_csa_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash(name: str) -> str:
+    h = hashlib.sha256()
+    for f in (name, "device_common.h"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# algorithmic work (what the method must move), per SURVEY-style accounting
+# --------------------------------------------------------------------------
+
+def n_vis(p, ratio, n_cap):
+    return min((p + 1) // ratio, n_cap)
+
+
+def score_bytes(sh, sp):
+    """k_idx rows read once per request + scores written + q_idx + w."""
+    es = 2 if sh.dtype == 1 else 4
+    total = 0
+    for b in range(sh.batch):
+        nv = [n_vis(int(sp[b]) + s, sh.ratio, sh.n_cap) for s in range(sh.q_per_req)]
+        scored = [n for n in nv if n > sh.topk]
+        if not scored:
+            continue
+        total += max(scored) * sh.idx_dim * es          # keys, shared by the request's tokens
+        total += sum(scored) * 4                        # fp32 scores
+        total += sh.q_per_req * sh.idx_heads * (sh.idx_dim * es + 4)
+    return total
+
+
+def score_flops(sh, sp):
+    f = 0
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            n = n_vis(int(sp[b]) + s, sh.ratio, sh.n_cap)
+            if n > sh.topk:
+                f += 2 * sh.idx_dim * sh.idx_heads * n
+    return f
+
+
+def topk_bytes(sh, sp):
+    total = 0
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            n = n_vis(int(sp[b]) + s, sh.ratio, sh.n_cap)
+            total += sh.topk * 4 + (n * 4 if n > sh.topk else 0)
+    return total
+
+
+def attn_bytes(sh, sp, topk_idx):
+    """Distinct K+V rows per request (window union + selected union) + q + lists + out."""
+    es = 2 if sh.dtype == 1 else 4
+    row = 2 * sh.head_dim * es
+    total = 0
+    rows_attended = 0
+    for b in range(sh.batch):
+        win_rows, cmp_rows = set(), set()
+        for s in range(sh.q_per_req):
+            p = int(sp[b]) + s
+            lo = max(0, p - sh.win + 1)
+            win_rows.update(t % sh.w_cap for t in range(lo, p + 1))
+            sel = topk_idx[b, s]
+            sel = sel[(sel >= 0) & (sel < sh.n_cap)]
+            cmp_rows.update(sel.tolist())
+            rows_attended += (p + 1 - lo) + sel.size
+        total += (len(win_rows) + len(cmp_rows)) * row
+    T = sh.batch * sh.q_per_req
+    total += T * sh.heads * sh.head_dim * es * 2            # q in, out
+    total += T * sh.topk * 4
+    return total, rows_attended
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import oracle
+    from sparse_attention_decode_csa_amd import csa as C
+    from sparse_attention_decode_csa_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    C.lib()  # fail loudly if the HIP library is missing
+    cfg = I.CONFIGS[args.config]
+    sh = cfg.shape
+    t0 = time.time()
+    inp = I.make_inputs(args.config)
+    t_gen = time.time() - t0
+    dev = C.to_device(inp, sh)
+    bufs = C.alloc_outputs(sh)
+    scale = I.softmax_scale(sh)
+    stream = torch.cuda.current_stream()
+    print(f"# config {args.config} ({cfg.name}) inputs drawn in {t_gen:.1f}s, uploaded", file=sys.stderr,
+          flush=True)
+
+    def run_step(ev=None):
+        if not cfg.supplied_topk:
+            if ev: ev[0].record(stream)
+            C.indexer_score(sh, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
+                            bufs["scores"], stream)
+            if ev: ev[1].record(stream)
+            C.topk(sh, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
+            ti = bufs["topk_idx"]
+        else:
+            if ev: ev[0].record(stream); ev[1].record(stream)
+            ti = dev["topk_idx"]
+        if ev: ev[2].record(stream)
+        C.sparse_attn_decode(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
+                             ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], scale,
+                             bufs["out"], bufs["attn_ws"], stream)
+        if ev: ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, events per stage on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1000.0 / args.steps
+    t_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+    t_event_step = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e-3
+
+    sp = inp["start_pos"]
+    ti = (bufs["topk_idx"] if not cfg.supplied_topk else dev["topk_idx"]).cpu().numpy()
+    sb, sf = score_bytes(sh, sp), score_flops(sh, sp)
+    tb = topk_bytes(sh, sp)
+    ab, rows_att = attn_bytes(sh, sp, ti)
+    T = sh.batch * sh.q_per_req
+
+    def stage(bytes_, t):
+        gbs = bytes_ / t / 1e9 if t > 0 else 0.0
+        return {"us": round(t * 1e6, 2), "alg_bytes": int(bytes_), "GB_s": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    stages = {"indexer_score": stage(sb, t_score), "topk": stage(tb, t_topk),
+              "sparse_attn": stage(ab, t_attn)}
+    stages["indexer_score"]["TFLOP_s"] = round(sf / t_score / 1e12, 2) if t_score else 0.0
+    stages["sparse_attn"]["rows_attended"] = rows_att
+
+    dominant = "indexer_score" if sb >= ab else "sparse_attn"
+    dom_bytes, dom_t = (sb, t_score) if dominant == "indexer_score" else (ab, t_attn)
+    achieved = dom_bytes / dom_t / 1e9
+    traffic = None
+    tfile = os.path.join(PROFILES, f"traffic_{dominant}_config{args.config}.json")
+    if os.path.exists(tfile):
+        tj = json.load(open(tfile))
+        src = "indexer_score.hip" if dominant == "indexer_score" else "sparse_attn.hip"
+        if tj.get("kernel_source_hash") == kernel_source_hash(src):
+            traffic = tj.get("hbm_bytes_per_launch")
+
+    # CPU baseline: the oracle as it stands, whole step, on the host's cores
+    cpu = None
+    if not args.no_cpu_baseline:
+        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+        times = []
+        for _ in range(max(1, args.cpu_reps)):
+            t0 = time.perf_counter()
+            oracle.run(sh, inp, nthreads=nthreads,
+                       jobs=(oracle.JOB_ATTN if cfg.supplied_topk else 7))
+            times.append(time.perf_counter() - t0)
+            if times[-1] > 60:
+                break
+        tc = float(np.median(times))
+        cpu = {"value": round(T / tc, 2), "unit": "query-tokens/s", "cores": nthreads,
+               "kind": "oracle",
+               "sample": f"the full step of this workload ({T} query tokens), median of "
+                         f"{len(times)} runs, {tc:.2f} s each, fp64 oracle"}
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    line = {
+        "metric": "decode query-tokens/sec for CSA sparse attn step; achieved HBM GB/s vs peak",
+        "value": round(T / (ms_per_step * 1e-3), 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == 1 else "f32",
+        "data": "synthetic (seeded N(0,1) caches and queries, structure per configuration)",
+        "config": {"workload": f"{cfg.name}: B={sh.batch} S={sh.q_per_req} context->"
+                               f"{sh.n_cap} compressed rows (ratio {sh.ratio}) K={sh.topk} "
+                               f"WIN={sh.win} H={sh.heads} D={sh.head_dim} Dr={sh.rope_dim} "
+                               f"Hi={sh.idx_heads} Di={sh.idx_dim} G={sh.out_groups}",
+                   "batch": sh.batch, "q_per_req": sh.q_per_req, "topk": sh.topk,
+                   "max_len": sh.max_len, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "stages": stages,
+        "event_step_us": round(t_event_step * 1e6, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * csa.h - C ABI of the CSA sparse-attention decode step on MI355X (gfx950).
+ *
+ * One decode step of compressed sparse attention, in three calls issued in
+ * order on one HIP stream:
+ *
+ *   csa_indexer_score      score every causally visible compressed row
+ *   csa_topk               pick the Top-K rows per query token (or bypass)
+ *   csa_sparse_attn_decode attend the raw window plus the picked rows, merge
+ *                          the two softmax streams, undo RoPE, pack heads
+ *
+ * The step is the one described on the pages "Perf: skip redundant CSA
+ * scoring and fuse gather unpack" (description and changes table: scoring and
+ * sorting skipped when the ratio-4 cache fits IDX_TOPK, causal visibility
+ * kept, bounded Top-K indices emitted) and "Perf: fuse HCA merge, inverse
+ * RoPE, and packing" (description and changes table: the raw and compressed
+ * softmax merge, inverse RoPE and grouped packing in one pass, written into a
+ * preallocated grouped output).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is a DEVICE pointer to a contiguous, row-major,
+ *   16-byte aligned buffer owned by the caller.  The shape pointer is HOST
+ *   memory.  The library allocates nothing, keeps no pointer after a call
+ *   returns and holds no state: calls are reentrant.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   Calls only enqueue work; ordering is the stream order.
+ * - Element type of q, k_win, v_win, k_cmp, v_cmp, q_idx, k_idx and out is
+ *   shape->dtype (CSA_DTYPE_BF16 or CSA_DTYPE_F32).  w, scores, rope tables
+ *   and workspace are float32; start_pos and topk_idx are int32.
+ * - Errors are returned as status codes, never by aborting or printing.  All
+ *   argument checks run on the host before anything is enqueued, so on any
+ *   error other than CSA_ERR_LAUNCH no output has been touched.
+ * - An empty problem (batch == 0 or q_per_req == 0) is valid and does nothing.
+ *
+ * Positions and visibility
+ * ------------------------
+ * Query token s of request b sits at position p = start_pos[b] + s.  A
+ * compressed row j summarises raw tokens R*j .. R*j+R-1 and is visible to p
+ * once all of them are at or before p: n_vis(p) = floor((p+1)/R).  A token
+ * "fits" when n_vis(p) <= K; then it is not scored and its Top-K list is
+ * simply every visible row.  The device trusts start_pos but clamps p to
+ * [0, max_len-1], so a start_pos outside the contract cannot make it read out
+ * of bounds.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                       */
+  CSA_ERR_BAD_SHAPE = 2,   /* a size is negative, zero where it must not be,
+                              or inconsistent (H % G, odd Dr, Dr > D, ...)     */
+  CSA_ERR_BAD_DTYPE = 3,   /* dtype is not CSA_DTYPE_F32 / CSA_DTYPE_BF16      */
+  CSA_ERR_CAPACITY = 4,    /* n_cap, w_cap or rope_rows too small for max_len  */
+  CSA_ERR_ALIGNMENT = 5,   /* a tensor pointer is not 16-byte aligned          */
+  CSA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the query says    */
+  CSA_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch                 */
+  CSA_ERR_UNSUPPORTED = 8  /* valid but outside what the kernels are built for
+                              (see csa_shape_t for the supported ranges)       */
+} csa_status_t;
+
+typedef enum { CSA_DTYPE_F32 = 0, CSA_DTYPE_BF16 = 1 } csa_dtype_t;
+
+/* Sizes of one decode step.  Supported ranges (CSA_ERR_UNSUPPORTED outside):
+ *   head_dim, idx_dim in {64, 128}; 1 <= heads <= 16;
+ *   1 <= q_per_req * idx_heads <= 64; 1 <= topk <= 4096; win >= 1. */
+typedef struct {
+  int32_t batch;      /* B: requests                                          */
+  int32_t q_per_req;  /* S: query tokens per request (p = start_pos[b] + s)    */
+  int32_t ratio;      /* R: raw tokens per compressed row (the pages use 4)    */
+  int32_t n_cap;      /* compressed rows allocated per request                 */
+  int32_t topk;       /* K: IDX_TOPK                                           */
+  int32_t win;        /* WIN: raw sliding-window length (includes token p)     */
+  int32_t w_cap;      /* ring capacity of the window cache, >= win + S - 1     */
+  int32_t heads;      /* H: query heads; one KV head shared by all of them     */
+  int32_t head_dim;   /* D                                                     */
+  int32_t rope_dim;   /* Dr: even, <= D; the last Dr dims hold RoPE pairs      */
+  int32_t idx_heads;  /* Hi: indexer heads                                     */
+  int32_t idx_dim;    /* Di: indexer head dim                                  */
+  int32_t out_groups; /* G: output head groups, H % G == 0                     */
+  int32_t max_len;    /* host bound: max over b of start_pos[b] + S            */
+  int32_t dtype;      /* csa_dtype_t                                           */
+} csa_shape_t;
+
+/* Indexer scores of every visible compressed row.
+ *
+ * For each query token (b,s) that does not fit (n_vis(p) > K) and each
+ * visible row j < n_vis(p):
+ *   scores[b][s][j] = sum_{h < Hi} w[b][s][h] * relu(q_idx[b][s][h] . k_idx[b][j])
+ * The indexer and its skipping for cache-fitting requests are described on
+ * "Perf: skip redundant CSA scoring and fuse gather unpack" (description); the
+ * weighted-relu form is the indexer formula of the decode workloads.
+ * Products use the input type, sums are float32 (bf16 MFMA, fp32 accumulate).
+ *
+ *   q_idx  [B][S][Hi][Di]  dtype
+ *   w      [B][S][Hi]      float32
+ *   k_idx  [B][n_cap][Di]  dtype  (rows >= n_vis are never read)
+ *   start_pos [B]          int32
+ *   scores [B][S][n_cap]   float32, written only at (non-fitting token, j < n_vis);
+ *                          every other entry is left as the caller had it.
+ * Requires n_cap >= floor(max_len / R) (else CSA_ERR_CAPACITY).
+ */
+csa_status_t csa_indexer_score(const csa_shape_t* shape, const void* q_idx, const float* w,
+                               const void* k_idx, const int32_t* start_pos, float* scores,
+                               void* stream);
+
+/* Workspace bytes csa_topk needs for this shape (0 means none). */
+size_t csa_topk_workspace_bytes(const csa_shape_t* shape);
+
+/* Causal Top-K selection, with the fits-in-Top-K bypass.
+ *
+ * For a token with n_vis(p) <= K (it fits): topk_idx = 0, 1, ..., n_vis-1,
+ * then -1 up to K; scores are not read.  Otherwise: the K rows j < n_vis with
+ * the largest scores, where equal scores (compared as values, so -0 == +0)
+ * go to the lower index; the chosen indices are written in ascending order.
+ * The bypass is the one on "Perf: skip redundant CSA scoring and fuse gather
+ * unpack" (description: bounded indices instead of scoring and sorting); the
+ * need to hold for widths past 256 is stated on "Fix: port the DeepSeek-V4
+ * MoE, hc_pre and prefill fixes to DSpark" (description, indexer top-k item).
+ * The result is bit-exact: it depends on the score values only.
+ * NaN scores are outside the contract.
+ *
+ *   scores   [B][S][n_cap] float32 (read only at j < n_vis of non-fitting tokens)
+ *   topk_idx [B][S][K]     int32 output
+ * ws may be NULL when csa_topk_workspace_bytes() returns 0.
+ * Requires n_cap >= floor(max_len / R).
+ */
+csa_status_t csa_topk(const csa_shape_t* shape, const float* scores, const int32_t* start_pos,
+                      int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes csa_sparse_attn_decode needs for this shape (split partials). */
+size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* shape);
+
+/* Two-stream sparse attention of every query token, merged, RoPE undone, packed.
+ *
+ * For token (b,s) at position p and each head h (one KV head shared by all):
+ *   window stream:     raw positions max(0, p-WIN+1) .. p, read from the ring
+ *                      slot pos mod w_cap of k_win / v_win;
+ *   compressed stream: every entry j of topk_idx[b][s][:] with 0 <= j < n_cap
+ *                      (other entries are padding), rows of k_cmp / v_cmp;
+ *   each stream: logits l = softmax_scale * (q[b][s][h] . k), its own max and
+ *   sum; the two are merged by their maxima and sums (an empty stream weighs
+ *   nothing); the output o = merged sum / merged denominator.
+ * Then the last Dr dims, taken as pairs (D-Dr+2i, D-Dr+2i+1), are turned back
+ * by the position's angle: x' = x*cos + y*sin, y' = -x*sin + y*cos with
+ * cos = rope_cos[p][i], sin = rope_sin[p][i]; the value is rounded once to
+ * dtype and head h is written to group g = h / (H/G) at slot h mod (H/G).
+ * The merge, inverse RoPE and grouped packing follow "Perf: fuse HCA merge,
+ * inverse RoPE, and packing" (description, changes table); the window and the
+ * bounded row count WIN + min(n_vis, K) follow "Fix: port the DeepSeek-V4 MoE,
+ * hc_pre and prefill fixes to DSpark" (description, last item).
+ * Every reduction is in a fixed order (no floating-point atomics), so two
+ * calls on the same inputs give bitwise identical outputs.
+ *
+ *   q        [B][S][H][D]        dtype (RoPE already applied upstream)
+ *   k_win, v_win [B][w_cap][D]   dtype
+ *   k_cmp, v_cmp [B][n_cap][D]   dtype
+ *   topk_idx [B][S][K]           int32 (ascending or not; duplicates count twice)
+ *   rope_cos, rope_sin [rope_rows][Dr/2] float32, rope_rows >= max_len
+ *   out      [G][B*S][(H/G)*D]   dtype output
+ *   ws       at least csa_sparse_attn_workspace_bytes(shape) bytes
+ * Requires w_cap >= win + S - 1.
+ */
+csa_status_t csa_sparse_attn_decode(const csa_shape_t* shape, const void* q, const void* k_win,
+                                    const void* v_win, const void* k_cmp, const void* v_cmp,
+                                    const int32_t* topk_idx, const int32_t* start_pos,
+                                    const float* rope_cos, const float* rope_sin,
+                                    int32_t rope_rows, float softmax_scale, void* out, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* csa_status_string(csa_status_t status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t csa_abi_version(void);
+
+#define CSA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H_ */

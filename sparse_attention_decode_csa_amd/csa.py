@@ -1,0 +1,198 @@
+"""Python binding of libcsa (ctypes).  Argument marshalling only.
+
+Every function takes device tensors (torch, on a ROCm GPU), passes their
+device pointers and sizes through the C ABI declared in include/csa.h and
+raises if the library returns an error.  There is no CPU path: a missing
+library, a CPU tensor or a non-contiguous tensor is an error.
+
+Names match the C ABI: indexer_score, topk, sparse_attn_decode, plus the
+workspace queries and step(), which issues the three calls in order on one
+stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+from .inputs import BF16, F32, Shape
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+
+_FIELDS = ("batch", "q_per_req", "ratio", "n_cap", "topk", "win", "w_cap", "heads",
+           "head_dim", "rope_dim", "idx_heads", "idx_dim", "out_groups", "max_len", "dtype")
+
+STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL_PTR", 2: "CSA_ERR_BAD_SHAPE", 3: "CSA_ERR_BAD_DTYPE",
+          4: "CSA_ERR_CAPACITY", 5: "CSA_ERR_ALIGNMENT", 6: "CSA_ERR_WORKSPACE",
+          7: "CSA_ERR_LAUNCH", 8: "CSA_ERR_UNSUPPORTED"}
+
+EXPORTS = ("csa_indexer_score", "csa_topk_workspace_bytes", "csa_topk",
+           "csa_sparse_attn_workspace_bytes", "csa_sparse_attn_decode", "csa_status_string",
+           "csa_abi_version")
+
+
+class CShape(ctypes.Structure):
+    """Mirror of csa_shape_t."""
+    _fields_ = [(f, ctypes.c_int32) for f in _FIELDS]
+
+    @classmethod
+    def of(cls, shape) -> "CShape":
+        return cls(*[int(getattr(shape, f)) for f in _FIELDS])
+
+
+class CsaError(RuntimeError):
+    def __init__(self, fn: str, code: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({text})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcsa.so (built in-tree by build.py); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m sparse_attention_decode_csa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        sp = ctypes.POINTER(CShape)
+        L.csa_indexer_score.restype = i32
+        L.csa_indexer_score.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.csa_topk_workspace_bytes.restype = sz
+        L.csa_topk_workspace_bytes.argtypes = [sp]
+        L.csa_topk.restype = i32
+        L.csa_topk.argtypes = [sp, vp, vp, vp, vp, sz, vp]
+        L.csa_sparse_attn_workspace_bytes.restype = sz
+        L.csa_sparse_attn_workspace_bytes.argtypes = [sp]
+        L.csa_sparse_attn_decode.restype = i32
+        L.csa_sparse_attn_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
+                                             vp, sz, vp]
+        L.csa_status_string.restype = ctypes.c_char_p
+        L.csa_status_string.argtypes = [i32]
+        L.csa_abi_version.restype = i32
+        L.csa_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().csa_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise CsaError(fn, code, status_string(code))
+
+
+def _dev(t: Optional[torch.Tensor], name: str):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor must live on the GPU (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def torch_dtype(shape) -> torch.dtype:
+    return torch.bfloat16 if shape.dtype == BF16 else torch.float32
+
+
+def topk_workspace_bytes(shape) -> int:
+    return int(lib().csa_topk_workspace_bytes(ctypes.byref(CShape.of(shape))))
+
+
+def sparse_attn_workspace_bytes(shape) -> int:
+    return int(lib().csa_sparse_attn_workspace_bytes(ctypes.byref(CShape.of(shape))))
+
+
+def indexer_score(shape, q_idx, w, k_idx, start_pos, scores, stream=None) -> None:
+    cs = CShape.of(shape)
+    _check("csa_indexer_score", lib().csa_indexer_score(
+        ctypes.byref(cs), _dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"),
+        _dev(start_pos, "start_pos"), _dev(scores, "scores"), _stream(stream)))
+
+
+def topk(shape, scores, start_pos, topk_idx, ws=None, stream=None) -> None:
+    cs = CShape.of(shape)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa_topk", lib().csa_topk(
+        ctypes.byref(cs), _dev(scores, "scores"), _dev(start_pos, "start_pos"),
+        _dev(topk_idx, "topk_idx"), _dev(ws, "ws"), nbytes, _stream(stream)))
+
+
+def sparse_attn_decode(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos, rope_cos,
+                       rope_sin, softmax_scale, out, ws, stream=None) -> None:
+    cs = CShape.of(shape)
+    rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa_sparse_attn_decode", lib().csa_sparse_attn_decode(
+        ctypes.byref(cs), _dev(q, "q"), _dev(k_win, "k_win"), _dev(v_win, "v_win"),
+        _dev(k_cmp, "k_cmp"), _dev(v_cmp, "v_cmp"), _dev(topk_idx, "topk_idx"),
+        _dev(start_pos, "start_pos"), _dev(rope_cos, "rope_cos"), _dev(rope_sin, "rope_sin"),
+        rope_rows, float(softmax_scale), _dev(out, "out"), _dev(ws, "ws"), nbytes,
+        _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# convenience: device buffers for one step
+# ----------------------------------------------------------------------------
+
+def to_device(inp: dict, shape, device="cuda") -> dict:
+    """Upload a seeded input dict: bf16 bit patterns become torch.bfloat16."""
+    out = {}
+    for k, v in inp.items():
+        if v.dtype == np.uint16:
+            t = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(v))
+        out[k] = t.to(device, non_blocking=False).contiguous()
+    return out
+
+
+def alloc_outputs(shape, device="cuda", scores_fill=float("nan")) -> dict:
+    """Output and workspace buffers of one step."""
+    B, S, Nc, K = shape.batch, shape.q_per_req, shape.n_cap, shape.topk
+    G, H, D = shape.out_groups, shape.heads, shape.head_dim
+    dt = torch_dtype(shape)
+    tw = topk_workspace_bytes(shape)
+    aw = sparse_attn_workspace_bytes(shape)
+    return dict(
+        scores=torch.full((B, S, Nc), scores_fill, dtype=torch.float32, device=device),
+        topk_idx=torch.full((B, S, K), -7, dtype=torch.int32, device=device),
+        out=torch.empty((G, B * S, (H // G) * D), dtype=dt, device=device),
+        topk_ws=torch.empty(max(tw, 1), dtype=torch.uint8, device=device) if tw else None,
+        attn_ws=torch.empty(max(aw, 16), dtype=torch.uint8, device=device),
+    )
+
+
+def step(shape, dev: dict, bufs: dict, softmax_scale: float, stream=None,
+         supplied_topk: bool = False) -> None:
+    """One decode step: score, select, attend (or attend only, when the
+    caller supplies the Top-K lists in dev['topk_idx'])."""
+    if supplied_topk:
+        ti = dev["topk_idx"]
+    else:
+        indexer_score(shape, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
+                      bufs["scores"], stream)
+        topk(shape, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
+        ti = bufs["topk_idx"]
+    sparse_attn_decode(shape, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
+                       ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], softmax_scale,
+                       bufs["out"], bufs["attn_ws"], stream)

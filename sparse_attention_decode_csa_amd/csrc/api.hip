@@ -1,0 +1,167 @@
+// extern "C" surface of libcsa: host-side argument checks, workspace sizing
+// and dispatch to the kernels.  Every check runs before anything is enqueued,
+// so a refused call leaves every output untouched; none of them touches the
+// GPU, so they behave the same on a machine without one.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/csa.h"
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks every call shares.  Sets *empty when there is no query token.
+csa_status_t check_common(const csa_shape_t* sh, bool* empty) {
+  if (!sh) return CSA_ERR_NULL_PTR;
+  if (sh->dtype != CSA_DTYPE_F32 && sh->dtype != CSA_DTYPE_BF16) return CSA_ERR_BAD_DTYPE;
+  if (sh->batch < 0 || sh->q_per_req < 0) return CSA_ERR_BAD_SHAPE;
+  *empty = sh->batch == 0 || sh->q_per_req == 0;
+  if (*empty) return CSA_OK;
+  if (sh->ratio < 1 || sh->n_cap < 1 || sh->topk < 1 || sh->win < 1 || sh->w_cap < 1 ||
+      sh->heads < 1 || sh->head_dim < 1 || sh->rope_dim < 0 || sh->idx_heads < 1 ||
+      sh->idx_dim < 1 || sh->out_groups < 1 || sh->max_len < sh->q_per_req)
+    return CSA_ERR_BAD_SHAPE;
+  if (sh->topk > 4096) return CSA_ERR_UNSUPPORTED;
+  // int32 index arithmetic inside the kernels
+  if ((int64_t)sh->batch * sh->q_per_req * sh->topk > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+csa_status_t check_selection(const csa_shape_t* sh) {
+  if (sh->n_cap < sh->max_len / sh->ratio) return CSA_ERR_CAPACITY;
+  return CSA_OK;
+}
+
+csa_status_t to_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_indexer_score(const csa_shape_t* sh, const void* q_idx, const float* w,
+                               const void* k_idx, const int32_t* start_pos, float* scores,
+                               void* stream) {
+  bool empty = false;
+  csa_status_t st = check_common(sh, &empty);
+  if (st != CSA_OK || empty) return st;
+  if (!q_idx || !w || !k_idx || !start_pos || !scores) return CSA_ERR_NULL_PTR;
+  if (sh->idx_dim != 64 && sh->idx_dim != 128) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)sh->q_per_req * sh->idx_heads > 64) return CSA_ERR_UNSUPPORTED;
+  if ((st = check_selection(sh)) != CSA_OK) return st;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(start_pos) ||
+      !aligned16(scores))
+    return CSA_ERR_ALIGNMENT;
+  csa::ScoreArgs a{q_idx, w, k_idx, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype};
+  (void)hipGetLastError();  // report only what these launches cause
+  return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_topk_workspace_bytes(const csa_shape_t* sh) {
+  (void)sh;
+  return 0;  // the selection keeps its state in LDS / registers
+}
+
+csa_status_t csa_topk(const csa_shape_t* sh, const float* scores, const int32_t* start_pos,
+                      int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  bool empty = false;
+  csa_status_t st = check_common(sh, &empty);
+  if (st != CSA_OK || empty) return st;
+  if (!scores || !start_pos || !topk_idx) return CSA_ERR_NULL_PTR;
+  if ((st = check_selection(sh)) != CSA_OK) return st;
+  if (!aligned16(scores) || !aligned16(start_pos) || !aligned16(topk_idx)) return CSA_ERR_ALIGNMENT;
+  csa::TopkArgs a{scores, start_pos, topk_idx, sh->batch, sh->q_per_req, sh->n_cap, sh->topk,
+                  sh->ratio, sh->max_len};
+  (void)hipGetLastError();
+  return to_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* sh) {
+  bool empty = false;
+  if (check_common(sh, &empty) != CSA_OK || empty) return 0;
+  return csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk).ws_bytes;
+}
+
+csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const void* k_win,
+                                    const void* v_win, const void* k_cmp, const void* v_cmp,
+                                    const int32_t* topk_idx, const int32_t* start_pos,
+                                    const float* rope_cos, const float* rope_sin,
+                                    int32_t rope_rows, float softmax_scale, void* out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  bool empty = false;
+  csa_status_t st = check_common(sh, &empty);
+  if (st != CSA_OK || empty) return st;
+  if (!q || !k_win || !v_win || !k_cmp || !v_cmp || !topk_idx || !start_pos || !out)
+    return CSA_ERR_NULL_PTR;
+  if (sh->rope_dim > 0 && (!rope_cos || !rope_sin)) return CSA_ERR_NULL_PTR;
+  if ((sh->rope_dim & 1) || sh->rope_dim > sh->head_dim || sh->heads % sh->out_groups != 0)
+    return CSA_ERR_BAD_SHAPE;
+  if (!std::isfinite(softmax_scale)) return CSA_ERR_BAD_SHAPE;
+  if (sh->head_dim != 64 && sh->head_dim != 128) return CSA_ERR_UNSUPPORTED;
+  if (sh->heads > 16) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)sh->w_cap < (int64_t)sh->win + sh->q_per_req - 1) return CSA_ERR_CAPACITY;
+  if (sh->rope_dim > 0 && rope_rows < sh->max_len) return CSA_ERR_CAPACITY;
+  const csa::AttnPlan pl =
+      csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk);
+  if (!ws || ws_bytes < pl.ws_bytes) return CSA_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_win) || !aligned16(v_win) || !aligned16(k_cmp) ||
+      !aligned16(v_cmp) || !aligned16(topk_idx) || !aligned16(start_pos) || !aligned16(out) ||
+      !aligned16(ws) || (rope_cos && !aligned16(rope_cos)) || (rope_sin && !aligned16(rope_sin)))
+    return CSA_ERR_ALIGNMENT;
+  float* wsf = static_cast<float*>(ws);
+  const size_t o_floats = (pl.ws_o_floats * 4 + 255) / 256 * 256 / 4;
+  csa::AttnArgs a{};
+  a.q = q;
+  a.k_win = k_win;
+  a.v_win = v_win;
+  a.k_cmp = k_cmp;
+  a.v_cmp = v_cmp;
+  a.topk_idx = topk_idx;
+  a.start_pos = start_pos;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.out = out;
+  a.ws_o = wsf;
+  a.ws_ml = wsf + o_floats;
+  a.batch = sh->batch;
+  a.q_per_req = sh->q_per_req;
+  a.n_cap = sh->n_cap;
+  a.topk = sh->topk;
+  a.win = sh->win;
+  a.w_cap = sh->w_cap;
+  a.heads = sh->heads;
+  a.head_dim = sh->head_dim;
+  a.rope_dim = sh->rope_dim;
+  a.out_groups = sh->out_groups;
+  a.max_len = sh->max_len;
+  a.dtype = sh->dtype;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.tiles_per_wave = pl.tiles_per_wave;
+  a.n_split_win = pl.n_split_win;
+  a.n_split_cmp = pl.n_split_cmp;
+  (void)hipGetLastError();
+  return to_status(csa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* csa_status_string(csa_status_t s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case CSA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
+    case CSA_ERR_BAD_DTYPE: return "unknown dtype";
+    case CSA_ERR_CAPACITY: return "cache, ring or RoPE table capacity too small for max_len";
+    case CSA_ERR_ALIGNMENT: return "a tensor pointer is not 16-byte aligned";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case CSA_ERR_UNSUPPORTED: return "sizes outside the range the kernels are built for";
+  }
+  return "unknown status";
+}
+
+int32_t csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+}  // extern "C"

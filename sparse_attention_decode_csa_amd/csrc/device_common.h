@@ -1,0 +1,115 @@
+// Device helpers shared by the CSA decode kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA operand convention used throughout (v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32): lane l supplies row (l % 16) of A and column
+// (l % 16) of B; its k-slots are chosen by g = l / 16.  The result tile
+// D[16][16] lands with lane l holding column (l % 16), rows 4g .. 4g+3.
+// Because the contraction is a plain sum, any assignment of real k indices to
+// (g, element) slots works as long as A and B use the same one; the kernels
+// pick assignments that make each lane's global loads 16-byte contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// 16-byte global load / store (one dwordx4 per lane).
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Streaming load for data read exactly once (hint: do not keep in cache).
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Reinterpret 32 bits as a float.  Takes a scalar on purpose: applying
+// __builtin_bit_cast directly to an ext-vector element (v[e]) was compiled as
+// a cast of element 0 for every e, so vector elements must be extracted to a
+// scalar first.
+__device__ __forceinline__ float u32_as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One 64-byte k-chunk of a row, i.e. each lane's 16 bytes: the bf16 form is a
+// single 16x16x32 MFMA; the fp32 form is four 16x16x4 MFMAs, one per element.
+template <typename T>
+__device__ __forceinline__ f32x4_t mma_chunk(u32x4_t a, u32x4_t b, f32x4_t c);
+
+template <>
+__device__ __forceinline__ f32x4_t mma_chunk<__bf16>(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return mfma_bf16(as_bf16x8(a), as_bf16x8(b), c);
+}
+
+template <>
+__device__ __forceinline__ f32x4_t mma_chunk<float>(u32x4_t a, u32x4_t b, f32x4_t c) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    c = mfma_f32(u32_as_float(a[e]), u32_as_float(b[e]), c);
+  return c;
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int popc_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Keeps the compiler from moving LDS accesses of one wave across this point.
+// LDS serves one wave's requests in issue order, so a wave that writes LDS and
+// then reads what other lanes of the same wave wrote needs no s_barrier.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin by dispatch order.  This maps
+// a dispatch index to a logical index such that each XCD receives one
+// contiguous run of logical indices, so neighbouring logical work items share
+// an XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int xcd = bid % kXcd, slot = bid / kXcd;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Causally visible compressed rows at position p (rows summarise R raw
+// tokens each; a row is visible once its whole block is at or before p).
+__device__ __forceinline__ int n_visible(int p, int ratio) { return (p + 1) / ratio; }
+
+__device__ __forceinline__ int clamp_pos(int p, int max_len) {
+  return p < 0 ? 0 : (p >= max_len ? max_len - 1 : p);
+}
+
+}  // namespace csa

@@ -1,0 +1,141 @@
+// Indexer scoring over the ratio-4 compressed cache.
+//
+//   score[b][s][j] = sum_h w[b][s][h] * relu(q_idx[b][s][h] . k_idx[b][j])
+//
+// for every causally visible row j of every token that does not fit Top-K
+// (the indexer of "Perf: skip redundant CSA scoring and fuse gather unpack",
+// description; its scoring is skipped for tokens whose visible cache fits).
+//
+// Design: the step streams k_idx once per request (every token of a request
+// shares it), so it is HBM-bound; the contraction runs on MFMA with the
+// request's S*Hi query rows as the M dimension (zero-padded to 16) and 16 keys
+// as N.  Each lane loads 16 contiguous bytes of one key row per 64-byte chunk
+// straight into the MFMA B operand, so a wave reads whole 256-byte rows with
+// no LDS staging and no reuse to exploit.  The per-head relu and weighted sum
+// runs through a small per-wave LDS tile in a fixed head order.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace csa {
+namespace {
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreTilesPerWave = 8;                                      // 16-key tiles
+constexpr int kScoreUnroll = 4;                                            // tiles in flight
+constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 512
+
+template <typename T, int DI, int MT>
+__global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
+  constexpr int ES = sizeof(T);
+  constexpr int CH = DI * ES / 64;   // 64-byte chunks per row; a lane holds 16 B of each
+  static_assert(CH >= 1 && DI * ES % 64 == 0, "row must be a whole number of 64-byte chunks");
+  constexpr int ROWS = MT * 16;      // padded query rows
+  constexpr int RP = 17;             // padded LDS row length (floats)
+
+  __shared__ float red[kScoreWaves][ROWS][RP];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int b = blockIdx.y;
+  const int S = a.q_per_req, Hi = a.idx_heads, SH = S * Hi;
+  const int sp = a.start_pos[b];
+
+  // Rows scored for this request: the largest visible count among its tokens
+  // that do not fit Top-K.
+  int nmax = 0;
+  for (int s = 0; s < S; ++s) {
+    const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
+    if (nv > a.topk) nmax = max(nmax, nv);
+  }
+  const int key0 = blockIdx.x * kScoreKeysPerBlock;
+  if (key0 >= nmax) return;  // whole workgroup: nothing visible in this chunk
+
+  // A operand: query row qr = mt*16 + n16 (token qr / Hi, head qr % Hi).
+  u32x4_t qa[MT][CH];
+  float wv[MT][4];
+  const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * DI * ES;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int qr = mt * 16 + n16;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      qa[mt][c] = qr < SH ? ld16(qbase + (size_t)qr * DI * ES + c * 64 + g * 16) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = mt * 16 + 4 * g + i;   // result rows this lane holds
+      wv[mt][i] = row < SH ? a.w[(size_t)b * SH + row] : 0.0f;
+    }
+  }
+
+  const char* kbase = static_cast<const char*>(a.k_idx) + (size_t)b * a.n_cap * DI * ES;
+  float* srow = a.scores + (size_t)b * S * a.n_cap;
+
+  for (int it = 0; it < kScoreTilesPerWave; it += kScoreUnroll) {
+    u32x4_t kb[kScoreUnroll][CH];
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int tile = (it + u) * kScoreWaves + wave;
+      const int j = min(key0 + tile * 16 + n16, nmax - 1);   // clamp: always a real row
+      const char* rp = kbase + (size_t)j * DI * ES + g * 16;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) kb[u][c] = ld16_stream(rp + c * 64);
+    }
+#pragma unroll
+    for (int u = 0; u < kScoreUnroll; ++u) {
+      const int tkey0 = key0 + ((it + u) * kScoreWaves + wave) * 16;
+      if (tkey0 >= nmax) continue;  // wave-uniform
+      f32x4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[mt] = mma_chunk<T>(qa[mt][c], kb[u][c], acc[mt]);
+      }
+      // lane holds dot(query row mt*16+4g+i, key tkey0+n16)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float d = acc[mt][i];
+          red[wave][mt * 16 + 4 * g + i][n16] = wv[mt][i] * (d > 0.0f ? d : 0.0f);
+        }
+      wave_lds_fence();
+      for (int e = lane; e < S * 16; e += kWave) {
+        const int s = e >> 4, n = e & 15;
+        const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
+        float sum = 0.0f;
+        for (int h = 0; h < Hi; ++h) sum += red[wave][s * Hi + h][n];
+        const int j = tkey0 + n;
+        if (nv > a.topk && j < nv) srow[(size_t)s * a.n_cap + j] = sum;
+      }
+      wave_lds_fence();
+    }
+  }
+}
+
+template <typename T, int DI>
+hipError_t launch_mt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  const int mt = (a.q_per_req * a.idx_heads + 15) / 16;
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 4>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_score(const ScoreArgs& a, hipStream_t st) {
+  const int n_bound = std::min(a.n_cap, a.max_len / a.ratio);
+  if (n_bound <= a.topk) return hipSuccess;  // every token fits Top-K: nothing to score
+  dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch);
+  if (a.dtype == 1) {
+    return a.idx_dim == 128 ? launch_mt<__bf16, 128>(a, grid, st) : launch_mt<__bf16, 64>(a, grid, st);
+  }
+  return a.idx_dim == 128 ? launch_mt<float, 128>(a, grid, st) : launch_mt<float, 64>(a, grid, st);
+}
+
+}  // namespace csa

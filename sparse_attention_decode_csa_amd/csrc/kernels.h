@@ -1,0 +1,62 @@
+// Launch entry points of the CSA decode kernels (internal to libcsa).
+// Host-side argument checking happens in api.hip before any of these run;
+// each launcher only picks a kernel instantiation and enqueues it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct ScoreArgs {
+  const void* q_idx;        // [B][S][Hi][Di]
+  const float* w;           // [B][S][Hi]
+  const void* k_idx;        // [B][n_cap][Di]
+  const int32_t* start_pos; // [B]
+  float* scores;            // [B][S][n_cap]
+  int batch, q_per_req, idx_heads, idx_dim, n_cap, topk, ratio, max_len, dtype;
+};
+
+struct TopkArgs {
+  const float* scores;      // [B][S][n_cap]
+  const int32_t* start_pos; // [B]
+  int32_t* topk_idx;        // [B][S][K]
+  int batch, q_per_req, n_cap, topk, ratio, max_len;
+};
+
+struct AttnArgs {
+  const void* q;            // [B][S][H][D]
+  const void* k_win;        // [B][w_cap][D]
+  const void* v_win;
+  const void* k_cmp;        // [B][n_cap][D]
+  const void* v_cmp;
+  const int32_t* topk_idx;  // [B][S][K]
+  const int32_t* start_pos; // [B]
+  const float* rope_cos;    // [rope_rows][Dr/2]
+  const float* rope_sin;
+  void* out;                // [G][B*S][(H/G)*D]
+  float* ws_o;              // [B*S][n_split][H][D]   split partial sums
+  float* ws_ml;             // [B*S][n_split][H][2]   split (max, sum), base-2 logits
+  int batch, q_per_req, n_cap, topk, win, w_cap, heads, head_dim, rope_dim, out_groups,
+      max_len, dtype;
+  float scale_log2;         // softmax_scale * log2(e)
+  int tiles_per_wave, n_split_win, n_split_cmp;
+};
+
+// Split plan of the attention kernel; a function of the shape only, so the
+// workspace query and the launch always agree.
+struct AttnPlan {
+  int tiles_per_wave;   // 32-row tiles each of the 4 waves of a workgroup takes
+  int rows_per_split;   // 4 * 32 * tiles_per_wave
+  int n_split_win, n_split_cmp;
+  size_t ws_o_floats, ws_ml_floats, ws_bytes;
+};
+
+AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk);
+
+hipError_t launch_indexer_score(const ScoreArgs& a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace csa

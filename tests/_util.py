@@ -1,0 +1,103 @@
+"""Helpers shared by the parity tests: tolerances and comparisons.
+
+The expected values always come from the CPU oracle (or from the pages'
+mathematics); GPU results are only ever compared, never fed to the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from sparse_attention_decode_csa_amd import inputs as I
+
+# max-abs tolerance for bf16 outputs with fp32 accumulation
+BF16_ATOL = 2e-2
+# fp32 configuration: per (token, head) row, max |gpu - ref| <= 1e-5 * max |ref|
+F32_ROW_RTOL = 1e-5
+U32 = 2.0 ** -24
+
+
+def score_error_bound(shape, inp, tok_rows):
+    """Bound on |gpu score - exact score| for every (b, s, j) scored.
+
+    The dot of each head is a sum of Di exactly representable products (bf16)
+    or rounded fp32 products; then relu, one product with w and Hi-1 additions
+    in fp32, plus the oracle's own final rounding.  With u = 2^-24 the error of
+    any summation order is at most (Di + Hi + 3) u sum_h w_h sum_c |q_hc k_jc|.
+    """
+    dt = shape.dtype
+    q = np.abs(I.as_float(inp["q_idx"], dt).astype(np.float64))
+    k = np.abs(I.as_float(inp["k_idx"], dt).astype(np.float64))
+    w = inp["w"].astype(np.float64)
+    bound = {}
+    for (b, s, n) in tok_rows:
+        mag = np.einsum("h,hc,jc->j", w[b, s], q[b, s], k[b, :n])
+        bound[(b, s)] = (shape.idx_dim + shape.idx_heads + 3) * U32 * mag
+    return bound
+
+
+def token_rows(shape, start_pos):
+    """(b, s, n_vis) of every token that is scored (does not fit Top-K)."""
+    out = []
+    for b in range(shape.batch):
+        for s in range(shape.q_per_req):
+            p = int(start_pos[b]) + s
+            n = min((p + 1) // shape.ratio, shape.n_cap)
+            if n > shape.topk:
+                out.append((b, s, n))
+    return out
+
+
+def compare_outputs(shape, got: np.ndarray, ref: np.ndarray, tokens=None):
+    """Assert the attention output matches to the stated tolerance.
+
+    got/ref: [G, B*S, (H/G)*D] float arrays.  `tokens` restricts the check to
+    a subset of flat token indices.
+    """
+    G, H, D = shape.out_groups, shape.heads, shape.head_dim
+    T = shape.batch * shape.q_per_req
+    g4 = got.reshape(G, T, H // G, D)
+    r4 = ref.reshape(G, T, H // G, D)
+    if tokens is not None:
+        g4, r4 = g4[:, tokens], r4[:, tokens]
+    assert np.isfinite(g4).all(), "non-finite GPU output"
+    err = np.abs(g4.astype(np.float64) - r4.astype(np.float64))
+    if shape.dtype == I.BF16:
+        worst = float(err.max(initial=0.0))
+        assert worst <= BF16_ATOL, f"max abs error {worst} > {BF16_ATOL}"
+        return worst
+    row_err = err.max(axis=-1)
+    row_mag = np.abs(r4).max(axis=-1)
+    ratio = row_err / np.maximum(row_mag, 1e-30)
+    worst = float(ratio.max(initial=0.0))
+    assert worst <= F32_ROW_RTOL, f"row-relative error {worst} > {F32_ROW_RTOL}"
+    return worst
+
+
+def topk_exemptions(shape, gpu_idx, ref_idx, ref_scores, bound, start_pos):
+    """Compare end-to-end Top-K lists; return the (b, s) tokens that differ.
+
+    A difference is allowed only at the selection boundary: every row in the
+    symmetric difference must have an oracle score within the score error
+    bound (on both sides) of the oracle's K-th largest score.
+    """
+    exempt = []
+    K = shape.topk
+    for b in range(shape.batch):
+        for s in range(shape.q_per_req):
+            gi, ri = gpu_idx[b, s], ref_idx[b, s]
+            if np.array_equal(gi, ri):
+                continue
+            p = int(start_pos[b]) + s
+            n = min((p + 1) // shape.ratio, shape.n_cap)
+            assert n > K, f"bypass token {(b, s)} differs"
+            assert len(set(gi.tolist())) == K and (gi >= 0).all() and (gi < n).all()
+            assert np.all(np.diff(gi) > 0), "GPU list not ascending"
+            sc = ref_scores[b, s, :n].astype(np.float64)
+            kth = np.sort(sc)[::-1][K - 1]
+            bd = bound[(b, s)]
+            diff = set(gi.tolist()) ^ set(ri.tolist())
+            for j in diff:
+                assert abs(sc[j] - kth) <= bd[j] + bd.max(), (
+                    f"token {(b, s)} row {j}: score {sc[j]} far from boundary {kth}")
+            exempt.append((b, s, len(diff)))
+    return exempt

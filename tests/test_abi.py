@@ -1,0 +1,151 @@
+"""The C-ABI library on the CPU: it loads, exports what include/csa.h declares,
+and its host-side checks refuse bad arguments before any GPU work.
+
+No call here reaches a kernel launch: every call is refused by validation (or
+is the empty problem, which returns before touching the GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_decode_csa_amd import csa as C
+from sparse_attention_decode_csa_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced (calls are refused first)
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(csa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_exports_agree():
+    decl = declared_functions()
+    assert set(decl) == set(C.EXPORTS), decl
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (csa_\w+)", out))
+    assert set(decl) <= exported, set(decl) - exported
+    lib = C.lib()
+    for name in decl:
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings():
+    assert C.lib().csa_abi_version() == 1
+    for code in range(9):
+        assert C.status_string(code)
+    assert C.status_string(99) == "unknown status"
+
+
+def shape(**kw):
+    return I.CONFIGS[1].shape.replace(**kw)
+
+
+def call_score(sh, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return C.lib().csa_indexer_score(None if sh is None else ctypes.byref(C.CShape.of(sh)),
+                                     *p, None)
+
+
+def call_topk(sh, ptrs=None):
+    p = ptrs or [FAKE] * 3
+    return C.lib().csa_topk(ctypes.byref(C.CShape.of(sh)), *p, None, 0, None)
+
+
+def call_attn(sh, ptrs=None, rope_rows=1 << 20, ws_bytes=1 << 40, scale=0.1):
+    p = ptrs or [FAKE] * 10
+    return C.lib().csa_sparse_attn_decode(ctypes.byref(C.CShape.of(sh)), *p[:9], rope_rows, scale,
+                                          p[9], FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(dtype=5), 3),
+    (dict(batch=-1), 2),
+    (dict(ratio=0), 2),
+    (dict(topk=0), 2),
+    (dict(topk=5000), 8),
+    (dict(idx_dim=96), 8),
+    (dict(q_per_req=8, idx_heads=16), 8),
+    (dict(n_cap=200), 4),            # floor(1024 / 4) = 256 rows needed
+    (dict(max_len=0), 2),
+])
+def test_indexer_score_refusals(case, code):
+    assert call_score(shape(**case)) == code
+
+
+def test_indexer_score_null_and_alignment():
+    assert call_score(None) == 1
+    assert call_score(shape(), [FAKE, None, FAKE, FAKE, FAKE]) == 1
+    assert call_score(shape(), [FAKE, FAKE, MISALIGNED, FAKE, FAKE]) == 5
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(n_cap=255), 4),
+    (dict(win=0), 2),
+    (dict(dtype=-1), 3),
+])
+def test_topk_refusals(case, code):
+    assert call_topk(shape(**case)) == code
+
+
+def test_topk_null():
+    assert call_topk(shape(), [FAKE, None, FAKE]) == 1
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(head_dim=96, rope_dim=32), 8),
+    (dict(heads=32), 8),
+    (dict(rope_dim=63), 2),
+    (dict(rope_dim=256), 2),
+    (dict(heads=16, out_groups=3), 2),
+    (dict(w_cap=127), 4),            # needs win + S - 1 = 128
+    (dict(q_per_req=2, w_cap=128), 4),
+])
+def test_attn_refusals(case, code):
+    assert call_attn(shape(**case)) == code
+
+
+def test_attn_capacity_workspace_alignment():
+    sh = shape()
+    assert call_attn(sh, rope_rows=1000) == 4            # max_len = 1024 rows needed
+    assert call_attn(sh, ws_bytes=C.sparse_attn_workspace_bytes(sh) - 1) == 6
+    assert call_attn(sh, scale=float("nan")) == 2
+    p = [FAKE] * 10
+    p[2] = MISALIGNED
+    assert call_attn(sh, p) == 5
+    p = [FAKE] * 10
+    p[0] = None
+    assert call_attn(sh, p) == 1
+    p = [FAKE] * 10
+    p[7] = None                                          # rope table with rope_dim > 0
+    assert call_attn(sh, p) == 1
+    assert call_attn(shape(rope_dim=0), [FAKE] * 7 + [None, None, FAKE], ws_bytes=1 << 40) != 1
+
+
+def test_empty_problem_is_ok_without_gpu_work():
+    sh = shape(batch=0)
+    assert call_score(sh) == 0 and call_topk(sh) == 0 and call_attn(sh) == 0
+    assert C.sparse_attn_workspace_bytes(sh) == 0
+
+
+def test_workspace_queries():
+    for cid, cfg in I.CONFIGS.items():
+        sh = cfg.shape
+        assert C.topk_workspace_bytes(sh) == 0
+        ws = C.sparse_attn_workspace_bytes(sh)
+        T = sh.batch * sh.q_per_req
+        assert ws >= T * 2 * sh.heads * (sh.head_dim + 2) * 4     # at least one split per stream
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        C.topk(shape(), t, t, t)

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every expected value comes from the oracle run on the same seeded inputs.
+Top-K lists must be bit-exact when both sides select from the same scores;
+scores must lie within the fp32 error bound; attention outputs within max-abs
+2e-2 (bf16) or 1e-5 row-relative (fp32).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_decode_csa_amd import csa as C
+from sparse_attention_decode_csa_amd import inputs as I
+from tests import _util as U
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    C.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def small_cfg(name="edge", seed=21, structure="none", lengths=None, **kw):
+    base = dict(batch=4, q_per_req=2, ratio=4, n_cap=256, topk=64, win=64, w_cap=96, heads=16,
+                head_dim=128, rope_dim=64, idx_heads=4, idx_dim=128, out_groups=1, max_len=1024,
+                dtype=I.BF16)
+    base.update(kw)
+    sh = I.Shape(**base)
+    return I.Config(name=name, shape=sh, seed=seed,
+                    lengths=lengths or f"start_uniform:0:{sh.max_len - sh.q_per_req}",
+                    structure=structure, supplied_topk=False)
+
+
+def gpu_step(shape, inp, supplied=False, topk_idx=None, scores=None, jobs=("score", "topk", "attn")):
+    """Run chosen steps on the GPU; returns numpy copies of scores, topk_idx, out."""
+    d = C.to_device(inp, shape)
+    bufs = C.alloc_outputs(shape)
+    scale = I.softmax_scale(shape)
+    if scores is not None:
+        bufs["scores"].copy_(torch.from_numpy(scores))
+    if "score" in jobs:
+        C.indexer_score(shape, d["q_idx"], d["w"], d["k_idx"], d["start_pos"], bufs["scores"])
+    if "topk" in jobs:
+        C.topk(shape, bufs["scores"], d["start_pos"], bufs["topk_idx"], bufs["topk_ws"])
+    ti = bufs["topk_idx"]
+    if topk_idx is not None:
+        ti = torch.from_numpy(np.ascontiguousarray(topk_idx, np.int32)).cuda()
+    elif supplied:
+        ti = d["topk_idx"]
+    if "attn" in jobs:
+        C.sparse_attn_decode(shape, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"], ti,
+                             d["start_pos"], d["rope_cos"], d["rope_sin"], scale, bufs["out"],
+                             bufs["attn_ws"])
+    torch.cuda.synchronize()
+    return dict(scores=bufs["scores"].cpu().numpy(), topk_idx=bufs["topk_idx"].cpu().numpy(),
+                out=bufs["out"].float().cpu().numpy())
+
+
+def oracle_step(cfg_shape, inp, **kw):
+    return oracle.run(cfg_shape, inp, nthreads=NTHREADS, **kw)
+
+
+# --------------------------------------------------------------------------
+# attention on the oracle's own Top-K lists
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [0, 1, 2])
+def test_attention_matches_oracle(cid, config_inputs):
+    cfg = I.CONFIGS[cid]
+    sh, inp = cfg.shape, config_inputs(cid)
+    ref = oracle_step(sh, inp, jobs=(oracle.JOB_ATTN if cfg.supplied_topk
+                                     else oracle.JOB_SCORE | oracle.JOB_TOPK | oracle.JOB_ATTN))
+    got = gpu_step(sh, inp, topk_idx=ref["topk_idx"], jobs=("attn",))
+    worst = U.compare_outputs(sh, got["out"], ref["out"])
+    print(f"config {cid}: worst error {worst:.3g}")
+
+
+# --------------------------------------------------------------------------
+# indexer scores
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [0, 3])
+def test_scores_match_oracle(cid, config_inputs):
+    cfg = I.CONFIGS[cid]
+    sh, inp = cfg.shape, config_inputs(cid)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE)
+    got = gpu_step(sh, inp, jobs=("score",))
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, inp, rows)
+    assert rows, "configuration scores nothing"
+    scored = np.zeros(got["scores"].shape, dtype=bool)
+    for (b, s, n) in rows:
+        err = np.abs(got["scores"][b, s, :n].astype(np.float64) - ref["scores"][b, s, :n])
+        assert np.all(err <= bound[(b, s)]), f"token {(b, s)}: score error above bound"
+        scored[b, s, :n] = True
+    assert np.isnan(got["scores"][~scored]).all(), "entries outside the scored set were written"
+
+
+@pytest.mark.parametrize("S,Hi,Di", [(1, 4, 128), (2, 8, 128), (4, 8, 64), (8, 8, 128), (3, 5, 64)])
+def test_scores_exact_grid(S, Hi, Di):
+    # Dyadic-grid inputs make every fp32 partial sum exact: bitwise equality.
+    cfg = small_cfg(q_per_req=S, idx_heads=Hi, idx_dim=Di, n_cap=600, topk=32, max_len=2400)
+    inp = I.make_inputs(cfg)
+    g = np.random.default_rng(S * 100 + Hi)
+    inp["q_idx"] = I.f32_to_bf16_bits((g.integers(-8, 9, inp["q_idx"].shape) / 4.0).astype(np.float32))
+    kg = I.f32_to_bf16_bits((g.integers(-8, 9, inp["k_idx"].shape) / 4.0).astype(np.float32))
+    inp["k_idx"] = np.where(inp["k_idx"] == I.f32_to_bf16_bits(np.float32([I.POISON]))[0],
+                            inp["k_idx"], kg)
+    inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    sh = cfg.shape
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE)
+    got = gpu_step(sh, inp, jobs=("score",))
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+
+
+# --------------------------------------------------------------------------
+# Top-K: bit-exact on the same scores
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [0, 3, 4])
+def test_topk_exact_on_oracle_scores(cid, config_inputs):
+    cfg = I.CONFIGS[cid]
+    sh, inp = cfg.shape, config_inputs(cid)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    got = gpu_step(sh, inp, scores=ref["scores"], jobs=("topk",))
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+
+
+@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero"])
+@pytest.mark.parametrize("n_cap,topk", [(300, 64), (4096, 256), (4096, 257), (9000, 1024),
+                                        (32768, 1024), (32768, 4096), (40000, 2048), (1000, 999)])
+def test_topk_exact_synthetic(kind, n_cap, topk):
+    # rows of several visible lengths, including n_vis == K and K + 1
+    B, S = 3, 2
+    sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=16, heads=1,
+                 head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1,
+                 max_len=4 * n_cap, dtype=I.BF16)
+    sp = np.array([4 * n_cap - S, 4 * topk - 1, 4 * (topk + 1) - 1 - 1], np.int32)
+    sp = np.minimum(sp, 4 * n_cap - S).astype(np.int32)
+    scores = I.random_scores(n_cap + topk, B, S, n_cap, kind)
+    inp = dict(start_pos=sp)
+    ref = oracle.run(sh, inp, jobs=oracle.JOB_TOPK, scores=scores)
+    d_scores = torch.from_numpy(scores).cuda()
+    d_sp = torch.from_numpy(sp).cuda()
+    out = torch.full((B, S, topk), -7, dtype=torch.int32, device="cuda")
+    C.topk(sh, d_scores, d_sp, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
+
+
+@pytest.mark.parametrize("topk", [256, 257, 1024])
+def test_topk_winners_past_256(topk):
+    n_cap = 8192
+    sh = I.Shape(batch=1, q_per_req=1, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=16, heads=1,
+                 head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1,
+                 max_len=4 * n_cap, dtype=I.BF16)
+    g = np.random.default_rng(topk)
+    scores = g.standard_normal((1, 1, n_cap)).astype(np.float32)
+    planted = g.choice(np.arange(257, n_cap), size=200, replace=False)
+    scores[0, 0, planted] = 40.0 + g.random(200).astype(np.float32)
+    sp = np.array([4 * n_cap - 1], np.int32)
+    ref = oracle.run(sh, dict(start_pos=sp), jobs=oracle.JOB_TOPK, scores=scores)
+    out = torch.empty((1, 1, topk), dtype=torch.int32, device="cuda")
+    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out)
+    got = out.cpu().numpy()
+    assert set(planted.tolist()) <= set(got[0, 0].tolist())
+    assert np.array_equal(got, ref["topk_idx"])
+
+
+# --------------------------------------------------------------------------
+# end to end: score -> Top-K -> attention
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [0, 1, 3, 4])
+def test_end_to_end(cid, config_inputs):
+    cfg = I.CONFIGS[cid]
+    sh, inp = cfg.shape, config_inputs(cid)
+    ref = oracle_step(sh, inp)
+    got = gpu_step(sh, inp)
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, inp, rows)
+    exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
+                               inp["start_pos"])
+    print(f"config {cid}: {len(exempt)} boundary exemptions {exempt}")
+    assert len(exempt) <= max(1, sh.batch * sh.q_per_req // 32)
+    ex = {b * sh.q_per_req + s for (b, s, _) in exempt}
+    keep = [t for t in range(sh.batch * sh.q_per_req) if t not in ex]
+    U.compare_outputs(sh, got["out"], ref["out"], tokens=keep)
+
+
+def test_determinism(config_inputs):
+    cid = 3
+    sh, inp = I.CONFIGS[cid].shape, config_inputs(cid)
+    a = gpu_step(sh, inp)
+    b = gpu_step(sh, inp)
+    for k in ("scores", "topk_idx", "out"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+EDGE = {
+    # early positions: empty compressed stream, partial windows, bypass
+    "early": dict(batch=6, q_per_req=1, topk=64, win=64, w_cap=64, start=[0, 1, 2, 3, 63, 64]),
+    # n_vis == K and K + 1 in one batch (bypass boundary), S = 3 causal tokens
+    "bypass_edge": dict(batch=4, q_per_req=3, topk=64, win=32, w_cap=40,
+                        start=[4 * 64 - 3, 4 * 64 - 2, 4 * 65 - 3, 900]),
+    # ring wrap with spare capacity, two groups, 8 heads
+    "ring_groups": dict(batch=3, q_per_req=4, win=48, w_cap=53, heads=8, out_groups=2,
+                        start=[5, 700, 1019]),
+    # head_dim 64 bf16, no RoPE, four groups
+    "d64_norope": dict(batch=3, q_per_req=2, head_dim=64, rope_dim=0, heads=12, out_groups=4,
+                       idx_dim=64, start=[10, 400, 1000]),
+    # fp32, head_dim 128, one head
+    "f32_one_head": dict(batch=2, q_per_req=2, dtype=I.F32, heads=1, rope_dim=16,
+                         start=[300, 1021]),
+    # wide Top-K relative to the window, many splits
+    "many_splits": dict(batch=2, q_per_req=1, topk=600, win=300, w_cap=300, n_cap=1024,
+                        max_len=4096, start=[4095, 3000]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_cases(name):
+    kw = dict(EDGE[name])
+    start = np.array(kw.pop("start"), np.int32)
+    cfg = small_cfg(name=name, **kw)
+    sh = cfg.shape
+    inp = I.make_inputs(cfg, start_pos=start)
+    ref = oracle_step(sh, inp)
+    got = gpu_step(sh, inp)
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, inp, rows)
+    exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
+                               inp["start_pos"])
+    assert not exempt
+    U.compare_outputs(sh, got["out"], ref["out"])
+    # attention alone on the oracle's lists
+    got2 = gpu_step(sh, inp, topk_idx=ref["topk_idx"], jobs=("attn",))
+    U.compare_outputs(sh, got2["out"], ref["out"])
+
+
+def test_padding_and_out_of_range_indices():
+    cfg = small_cfg(batch=2, q_per_req=1)
+    sh = cfg.shape
+    inp = I.make_inputs(cfg, start_pos=np.array([800, 1000], np.int32))
+    ti = oracle_step(sh, inp)["topk_idx"]
+    bad = ti.copy()
+    bad[0, 0, :5] = [-1, sh.n_cap, sh.n_cap + 100, -100, 2 ** 30]
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=bad)
+    got = gpu_step(sh, inp, topk_idx=bad, jobs=("attn",))
+    U.compare_outputs(sh, got["out"], ref["out"])
+
+
+def test_empty_batch_is_a_noop():
+    sh = small_cfg().shape.replace(batch=0)
+    z = torch.zeros(16, dtype=torch.int32, device="cuda")
+    f = torch.zeros(16, dtype=torch.float32, device="cuda")
+    C.indexer_score(sh, f, f, f, z, f)
+    C.topk(sh, f, z, z)
+    C.sparse_attn_decode(sh, f, f, f, f, f, z, z, f, f, 0.1, f, f)
+    torch.cuda.synchronize()
+    assert int(z.abs().sum()) == 0 and float(f.abs().sum()) == 0.0
+
+
+def test_refused_call_leaves_outputs_untouched():
+    cfg = small_cfg(batch=2, q_per_req=1)
+    sh = cfg.shape
+    inp = I.make_inputs(cfg)
+    d = C.to_device(inp, sh)
+    bufs = C.alloc_outputs(sh)
+    bufs["out"].fill_(3.0)
+    small_ws = bufs["attn_ws"][:16]
+    with pytest.raises(C.CsaError) as e:
+        C.sparse_attn_decode(sh, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"],
+                             bufs["topk_idx"], d["start_pos"], d["rope_cos"], d["rope_sin"], 0.1,
+                             bufs["out"], small_ws)
+    assert e.value.code == 6
+    torch.cuda.synchronize()
+    assert bool((bufs["out"] == 3.0).all())
