@@ -140,7 +140,7 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   a.max_len = sh->max_len;
   a.dtype = sh->dtype;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.tiles_per_wave = pl.tiles_per_wave;
+  a.waves_per_split = pl.waves_per_split;
   a.n_split_win = pl.n_split_win;
   a.n_split_cmp = pl.n_split_cmp;
   (void)hipGetLastError();

@@ -21,7 +21,8 @@ namespace {
 
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTilesPerWave = 8;                                      // 16-key tiles
-constexpr int kScoreUnroll = 4;                                            // tiles in flight
+constexpr int kScoreUnroll = 4;                                            // tiles per load group
+constexpr int kScoreGroups = kScoreTilesPerWave / kScoreUnroll;
 constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 512
 
 template <typename T, int DI, int MT>
@@ -50,46 +51,58 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   const int key0 = blockIdx.x * kScoreKeysPerBlock;
   if (key0 >= nmax) return;  // whole workgroup: nothing visible in this chunk
 
-  // A operand: query row qr = mt*16 + n16 (token qr / Hi, head qr % Hi).
+  // A operand: query row qr = mt*16 + n16 (token qr / Hi, head qr % Hi);
+  // padded rows load a real row and are zeroed, so the loads stay unconditional.
   u32x4_t qa[MT][CH];
   float wv[MT][4];
   const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * DI * ES;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int qr = mt * 16 + n16;
+    const char* qp = qbase + (size_t)min(qr, SH - 1) * DI * ES + g * 16;
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
-      qa[mt][c] = qr < SH ? ld16(qbase + (size_t)qr * DI * ES + c * 64 + g * 16) : u32x4_t{0, 0, 0, 0};
+    for (int c = 0; c < CH; ++c) {
+      const u32x4_t v = ld16(qp + c * 64);
+      qa[mt][c] = qr < SH ? v : u32x4_t{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = mt * 16 + 4 * g + i;   // result rows this lane holds
-      wv[mt][i] = row < SH ? a.w[(size_t)b * SH + row] : 0.0f;
+      const float wr = a.w[(size_t)b * SH + min(row, SH - 1)];
+      wv[mt][i] = row < SH ? wr : 0.0f;
     }
   }
 
   const char* kbase = static_cast<const char*>(a.k_idx) + (size_t)b * a.n_cap * DI * ES;
   float* srow = a.scores + (size_t)b * S * a.n_cap;
 
-  for (int it = 0; it < kScoreTilesPerWave; it += kScoreUnroll) {
-    u32x4_t kb[kScoreUnroll][CH];
+  // Tiles are interleaved over the 4 waves so that at each step the block
+  // reads 4 consecutive 16-row tiles (16 KiB contiguous for Di = 128 bf16).
+  auto tile_key0 = [&](int t) { return key0 + (t * kScoreWaves + wave) * 16; };
+  auto load_group = [&](int grp, u32x4_t (&dst)[kScoreUnroll][CH]) {
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      const int tile = (it + u) * kScoreWaves + wave;
-      const int j = min(key0 + tile * 16 + n16, nmax - 1);   // clamp: always a real row
+      const int j = min(tile_key0(grp * kScoreUnroll + u) + n16, nmax - 1);  // clamp: a real row
       const char* rp = kbase + (size_t)j * DI * ES + g * 16;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) kb[u][c] = ld16_stream(rp + c * 64);
+      for (int c = 0; c < CH; ++c) dst[u][c] = ld16_stream(rp + c * 64);
     }
+  };
+
+  u32x4_t kb[2][kScoreUnroll][CH];
+  load_group(0, kb[0]);
+#pragma unroll
+  for (int grp = 0; grp < kScoreGroups; ++grp) {
+    if (grp + 1 < kScoreGroups) load_group(grp + 1, kb[(grp + 1) & 1]);  // prefetch
 #pragma unroll
     for (int u = 0; u < kScoreUnroll; ++u) {
-      const int tkey0 = key0 + ((it + u) * kScoreWaves + wave) * 16;
-      if (tkey0 >= nmax) continue;  // wave-uniform
+      const int tkey0 = tile_key0(grp * kScoreUnroll + u);
       f32x4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < CH; ++c) acc[mt] = mma_chunk<T>(qa[mt][c], kb[u][c], acc[mt]);
+        for (int c = 0; c < CH; ++c) acc[mt] = mma_chunk<T>(qa[mt][c], kb[grp & 1][u][c], acc[mt]);
       }
       // lane holds dot(query row mt*16+4g+i, key tkey0+n16)
 #pragma unroll

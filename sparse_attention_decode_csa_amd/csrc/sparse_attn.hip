@@ -14,15 +14,14 @@
 // fixes to DSpark", description, last item).
 //
 // Design on gfx950:
-//   attn_split_kernel  A workgroup (4 waves) owns one (token, split): up to
-//     rows_per_split consecutive rows of ONE stream.  Each wave takes 32-row
-//     tiles.  K rows go straight from HBM into the MFMA A operand (16-byte
+//   attn_split_kernel  A workgroup (4 or 8 waves) owns one (token, split): up
+//     to 32 rows per wave of ONE stream, one 32-row tile per wave.  K rows go straight from HBM into the MFMA A operand (16-byte
 //     contiguous loads per lane); logits^T = K q^T puts heads on the lane axis,
 //     so the online-softmax statistics of a head live in the 4 lanes that share
 //     its column and need only two xor-shuffles.  V needs rows on the k axis
 //     of the PV MFMA, so each wave stages its 32xD V tile in LDS transposed
 //     (4 rows x 8 dims per lane, packed into 64-bit LDS writes) and reads it
-//     back as 16-byte operand fragments.  The 4 waves then merge their
+//     back as 16-byte operand fragments.  The waves then merge their
 //     (max, sum, partial O) in a fixed order through LDS and write one split
 //     partial.  No floating-point atomics anywhere.
 //   attn_merge_kernel  One workgroup per token merges the window splits in
@@ -37,8 +36,8 @@
 namespace csa {
 namespace {
 
-constexpr int kAttnWaves = 4;
 constexpr int kTileRows = 32;
+constexpr int kMaxWaves = 8;
 
 template <typename T>
 struct AttnTraits;
@@ -51,7 +50,7 @@ struct AttnTraits<float> {
   static constexpr int kDtype = 0;
 };
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 struct AttnLayout {
   static constexpr int ES = sizeof(T);
   static constexpr int CH = D * ES / 64;   // 64-byte chunks per row (K fragments)
@@ -62,8 +61,8 @@ struct AttnLayout {
   static constexpr int RS = 32 * ES + 16;  // LDS bytes per transposed V d-row (32 rows + pad)
   static constexpr int VT_BYTES = D * RS;
   static constexpr int MO_STRIDE = D + 1;  // floats per (wave, head) row in the merge area
-  static constexpr int MERGE_BYTES = (kAttnWaves * 16 * MO_STRIDE + kAttnWaves * 16 * 2) * 4;
-  static constexpr int SMEM = (kAttnWaves * VT_BYTES > MERGE_BYTES) ? kAttnWaves * VT_BYTES : MERGE_BYTES;
+  static constexpr int MERGE_BYTES = (NW * 16 * MO_STRIDE + NW * 16 * 2) * 4;
+  static constexpr int SMEM = (NW * VT_BYTES > MERGE_BYTES) ? NW * VT_BYTES : MERGE_BYTES;
   static_assert(UPL >= 1 && NP % 8 == 0, "head_dim too small for the V staging layout");
 };
 
@@ -72,9 +71,9 @@ struct AttnLayout {
 // {4g..4g+3, 16+4g..16+4g+3}, sit contiguously at 8g .. 8g+7.
 __device__ __forceinline__ int vt_pos_of_quad(int quad) { return 8 * (quad & 3) + 4 * (quad >> 2); }
 
-template <typename T, int D, int TPW>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
-  using L = AttnLayout<T, D>;
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a) {
+  using L = AttnLayout<T, D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[L::SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   const int b = logical / (S * NS);
   const int tok = b * S + s;
   const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
-  const int RPS = kAttnWaves * kTileRows * TPW;
+  const int RPS = NW * kTileRows;
 
   const bool win = split < NSW;
   int e_begin, e_end, first_pos = 0;
@@ -147,9 +146,10 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   for (int dt = 0; dt < L::DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   char* vt = smem + wave * L::VT_BYTES;
 
-  for (int it = 0; it < TPW; ++it) {
-    const int e0 = e_begin + (it * kAttnWaves + wave) * kTileRows;
-    if (e0 >= e_end) break;  // wave-uniform
+  // One 32-row tile per wave: all of its index and row loads are issued
+  // together, so the wave waits for one index round trip and one row round trip.
+  const int e0 = e_begin + wave * kTileRows;
+  if (e0 < e_end) {  // wave-uniform
 
     // K rows e0 + 16t + n16 as the A operand (16 bytes of each 64-byte chunk)
     u32x4_t kf[2][L::CH];
@@ -225,64 +225,57 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    if (m_new == -INFINITY) {  // no row seen yet (wave-uniform: masks are per row)
-      wave_lds_fence();
-      continue;
-    }
-    const float alpha = exp2f(m_run - m_new);
-    float pr[2][4];
-    float psum = 0.0f;
+    if (tmax != -INFINITY) {  // some row is valid (wave-uniform: masks are per row)
+      float pr[2][4];
+      float psum = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[t][i] = x[t][i] == -INFINITY ? 0.0f : exp2f(x[t][i] - m_new);
-        psum += pr[t][i];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < L::DT; ++dt) acc[dt] *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          pr[t][i] = x[t][i] == -INFINITY ? 0.0f : exp2f(x[t][i] - tmax);
+          psum += pr[t][i];
+        }
+      m_run = tmax;
+      l_run = psum;
 
-    // O^T += V^T P^T: A = V^T (row d, rows of the tile on k), B = P^T (column = head)
-    if constexpr (L::ES == 2) {
-      u32x4_t pw;
+      // O^T = V^T P^T: A = V^T (row d, tile rows on k), B = P^T (column = head)
+      if constexpr (L::ES == 2) {
+        u32x4_t pw;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int t = w >> 1, i0 = 2 * (w & 1);
-        pw[w] = float_to_bf16_bits(pr[t][i0]) | (float_to_bf16_bits(pr[t][i0 + 1]) << 16);
-      }
-      const bf16x8_t pf = as_bf16x8(pw);
+        for (int w = 0; w < 4; ++w) {
+          const int t = w >> 1, i0 = 2 * (w & 1);
+          pw[w] = float_to_bf16_bits(pr[t][i0]) | (float_to_bf16_bits(pr[t][i0 + 1]) << 16);
+        }
+        const bf16x8_t pf = as_bf16x8(pw);
 #pragma unroll
-      for (int dt = 0; dt < L::DT; ++dt) {
-        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vt + (16 * dt + n16) * L::RS + g * 16);
-        acc[dt] = mfma_bf16(as_bf16x8(vf), pf, acc[dt]);
-      }
-    } else {
+        for (int dt = 0; dt < L::DT; ++dt) {
+          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vt + (16 * dt + n16) * L::RS + g * 16);
+          acc[dt] = mfma_bf16(as_bf16x8(vf), pf, acc[dt]);
+        }
+      } else {
 #pragma unroll
-      for (int dt = 0; dt < L::DT; ++dt) {
-        const char* src = vt + (16 * dt + n16) * L::RS + g * 32;
-        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
-        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
+        for (int dt = 0; dt < L::DT; ++dt) {
+          const char* src = vt + (16 * dt + n16) * L::RS + g * 32;
+          const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
+          const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[dt] = mfma_f32(u32_as_float(v0[j]), pr[0][j], acc[dt]);
-          acc[dt] = mfma_f32(u32_as_float(v1[j]), pr[1][j], acc[dt]);
+          for (int j = 0; j < 4; ++j) {
+            acc[dt] = mfma_f32(u32_as_float(v0[j]), pr[0][j], acc[dt]);
+            acc[dt] = mfma_f32(u32_as_float(v1[j]), pr[1][j], acc[dt]);
+          }
         }
       }
     }
-    wave_lds_fence();
   }
 
   // per-head sum over the 4 lanes that share a head column
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
-  // ---- fixed-order merge of the 4 waves, one split partial out
+  // ---- fixed-order merge of the NW waves, one split partial out
   __syncthreads();  // every wave is done with its V tile; reuse LDS
   float* mo = reinterpret_cast<float*>(smem);                   // [wave][head][MO_STRIDE]
-  float* mml = mo + kAttnWaves * 16 * L::MO_STRIDE;             // [wave][head][2]
+  float* mml = mo + NW * 16 * L::MO_STRIDE;                     // [wave][head][2]
 #pragma unroll
   for (int dt = 0; dt < L::DT; ++dt)
 #pragma unroll
@@ -292,15 +285,15 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     mml[(wave * 16 + n16) * 2 + 1] = l_tot;
   }
   __syncthreads();
-  for (int item = tid; item < H * D; item += 256) {
+  for (int item = tid; item < H * D; item += NW * 64) {
     const int h = item / D, d = item - h * D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mml[(w * 16 + h) * 2]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mml[(w * 16 + h) * 2]);
     float Lsum = 0.0f, o = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float lw = mml[(w * 16 + h) * 2 + 1];
         if (lw > 0.0f) {
           const float f = exp2f(mml[(w * 16 + h) * 2] - M);
@@ -317,65 +310,84 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   }
 }
 
-// Merge a stream's splits [lo, hi) in ascending order for dims (d, d+1).
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int tok, int NS, int h, int d, int D,
-                                             int lo, int hi, float& M, float& Lsum, float& o0,
-                                             float& o1) {
-  M = -INFINITY;
-  Lsum = 0.0f;
-  o0 = o1 = 0.0f;
-  for (int sp = lo; sp < hi; ++sp) {
-    const size_t r = ((size_t)tok * NS + sp) * a.heads + h;
-    const float m = a.ws_ml[2 * r], l = a.ws_ml[2 * r + 1];
-    if (!(l > 0.0f)) continue;  // empty split
-    const float mn = fmaxf(M, m);
-    const float fo = exp2f(M - mn), fn = exp2f(m - mn);
-    const float2 ov = *reinterpret_cast<const float2*>(a.ws_o + r * D + d);
-    Lsum = Lsum * fo + l * fn;
-    o0 = o0 * fo + ov.x * fn;
-    o1 = o1 * fo + ov.y * fn;
-    M = mn;
+// Split partials of one stream, merged in ascending split order.  Loads of
+// up to kMergeBatch splits are issued before any of them is used.
+constexpr int kMergeBatch = 8;
+
+struct StreamState {
+  float m, l, o0, o1;
+};
+
+__device__ __forceinline__ StreamState merge_splits(const AttnArgs& a, int tok, int NS, int h, int d,
+                                                    int D, int lo, int hi) {
+  StreamState st{-INFINITY, 0.0f, 0.0f, 0.0f};
+  for (int b0 = lo; b0 < hi; b0 += kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch];
+    float2 ov[kMergeBatch];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int sp = min(b0 + k, hi - 1);
+      const size_t r = ((size_t)tok * NS + sp) * a.heads + h;
+      const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * r);
+      m[k] = ml.x;
+      l[k] = b0 + k < hi ? ml.y : 0.0f;
+      ov[k] = *reinterpret_cast<const float2*>(a.ws_o + r * D + d);
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      if (!(l[k] > 0.0f)) continue;  // empty split: its partial sum was never written
+      const float mn = fmaxf(st.m, m[k]);
+      const float fo = exp2f(st.m - mn), fn = exp2f(m[k] - mn);
+      st.l = st.l * fo + l[k] * fn;
+      st.o0 = st.o0 * fo + ov[k].x * fn;
+      st.o1 = st.o1 * fo + ov[k].y * fn;
+      st.m = mn;
+    }
   }
+  return st;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int tok = blockIdx.x;
+  const int item = blockIdx.y * 256 + threadIdx.x;  // (head, dim pair)
+  const int H = a.heads;
+  if (item >= H * (D / 2)) return;
   const int S = a.q_per_req, b = tok / S, s = tok % S;
   const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
-  const int H = a.heads, G = a.out_groups, Hg = H / G;
+  const int G = a.out_groups, Hg = H / G;
   const int NSW = a.n_split_win, NS = a.n_split_win + a.n_split_cmp;
   const int T_ = a.batch * S;
   const int r0 = D - a.rope_dim;
-  for (int item = threadIdx.x; item < H * (D / 2); item += 256) {
-    const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
-    float Mw, Lw, w0, w1, Mc, Lc, c0, c1;
-    merge_splits(a, tok, NS, h, d, D, 0, NSW, Mw, Lw, w0, w1);
-    merge_splits(a, tok, NS, h, d, D, NSW, NS, Mc, Lc, c0, c1);
-    // stream merge: an empty stream (sum 0) carries no weight
-    const float M = fmaxf(Mw, Mc);
-    const float fw = Lw > 0.0f ? exp2f(Mw - M) : 0.0f;
-    const float fc = Lc > 0.0f ? exp2f(Mc - M) : 0.0f;
-    const float inv = 1.0f / (fw * Lw + fc * Lc);
-    float x = (fw * w0 + fc * c0) * inv;
-    float y = (fw * w1 + fc * c1) * inv;
-    if (d >= r0) {  // inverse RoPE: turn the pair back by the position's angle
-      const int i = (d - r0) >> 1;
-      const float cs = a.rope_cos[(size_t)p * (a.rope_dim >> 1) + i];
-      const float sn = a.rope_sin[(size_t)p * (a.rope_dim >> 1) + i];
-      const float xr = x * cs + y * sn;
-      const float yr = y * cs - x * sn;
-      x = xr;
-      y = yr;
-    }
-    const int grp = h / Hg, hl = h - grp * Hg;
-    const size_t o = ((size_t)grp * T_ + tok) * Hg * D + (size_t)hl * D + d;
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t packed = float_to_bf16_bits(x) | (float_to_bf16_bits(y) << 16);
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o) = packed;
-    } else {
-      *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(x, y);
-    }
+  const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
+  float cs = 1.0f, sn = 0.0f;
+  if (d >= r0) {  // issue the table loads early
+    const int i = (d - r0) >> 1;
+    cs = a.rope_cos[(size_t)p * (a.rope_dim >> 1) + i];
+    sn = a.rope_sin[(size_t)p * (a.rope_dim >> 1) + i];
+  }
+  const StreamState w = merge_splits(a, tok, NS, h, d, D, 0, NSW);
+  const StreamState c = merge_splits(a, tok, NS, h, d, D, NSW, NS);
+  // stream merge: an empty stream (sum 0) carries no weight
+  const float M = fmaxf(w.m, c.m);
+  const float fw = w.l > 0.0f ? exp2f(w.m - M) : 0.0f;
+  const float fc = c.l > 0.0f ? exp2f(c.m - M) : 0.0f;
+  const float inv = 1.0f / (fw * w.l + fc * c.l);
+  float x = (fw * w.o0 + fc * c.o0) * inv;
+  float y = (fw * w.o1 + fc * c.o1) * inv;
+  if (d >= r0) {  // inverse RoPE: turn the pair back by the position's angle
+    const float xr = x * cs + y * sn;
+    const float yr = y * cs - x * sn;
+    x = xr;
+    y = yr;
+  }
+  const int grp = h / Hg, hl = h - grp * Hg;
+  const size_t o = ((size_t)grp * T_ + tok) * Hg * D + (size_t)hl * D + d;
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t packed = float_to_bf16_bits(x) | (float_to_bf16_bits(y) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o) = packed;
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(x, y);
   }
 }
 
@@ -384,15 +396,15 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   const int tokens = a.batch * a.q_per_req;
   const int NS = a.n_split_win + a.n_split_cmp;
   const dim3 grid(tokens * NS);
-  switch (a.tiles_per_wave) {
-    case 1: hipLaunchKernelGGL((attn_split_kernel<T, D, 1>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_split_kernel<T, D, 2>), grid, dim3(256), 0, st, a); break;
+  switch (a.waves_per_split) {
     case 4: hipLaunchKernelGGL((attn_split_kernel<T, D, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_split_kernel<T, D, 8>), grid, dim3(512), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<T, D>), dim3(tokens), dim3(256), 0, st, a);
+  const dim3 mgrid(tokens, (a.heads * (D / 2) + 255) / 256);
+  hipLaunchKernelGGL((attn_merge_kernel<T, D>), mgrid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -400,12 +412,12 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
 
 AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk) {
   AttnPlan pl{};
-  // Enough workgroups to fill 256 CUs several times over before growing the
-  // per-wave row count (which amortises the per-split partial traffic).
-  // (2048 waves at two tiles each before switching to two tiles per wave).
+  // Workgroups of 8 waves (256 rows per split) once there are enough rows to
+  // fill the 256 CUs several times over; 4 waves (128 rows) below that, so
+  // small batches still spread over many CUs.
   const long long rows = (long long)batch * q_per_req * (win + topk);
-  pl.tiles_per_wave = rows >= 2048LL * kTileRows * 2 ? 2 : 1;
-  pl.rows_per_split = kAttnWaves * kTileRows * pl.tiles_per_wave;
+  pl.waves_per_split = rows >= 65536 ? 8 : 4;
+  pl.rows_per_split = pl.waves_per_split * kTileRows;
   pl.n_split_win = (win + pl.rows_per_split - 1) / pl.rows_per_split;
   pl.n_split_cmp = (topk + pl.rows_per_split - 1) / pl.rows_per_split;
   const size_t parts = (size_t)batch * q_per_req * (pl.n_split_win + pl.n_split_cmp) * heads;
