@@ -19,9 +19,15 @@
 namespace csa {
 namespace {
 
+#ifndef CSA_SCORE_TILES_PER_WAVE
+#define CSA_SCORE_TILES_PER_WAVE 8
+#endif
+#ifndef CSA_SCORE_UNROLL
+#define CSA_SCORE_UNROLL 4
+#endif
 constexpr int kScoreWaves = 4;
-constexpr int kScoreTilesPerWave = 8;                                      // 16-key tiles
-constexpr int kScoreUnroll = 4;                                            // tiles per load group
+constexpr int kScoreTilesPerWave = CSA_SCORE_TILES_PER_WAVE;               // 16-key tiles
+constexpr int kScoreUnroll = CSA_SCORE_UNROLL;                             // tiles per load group
 constexpr int kScoreGroups = kScoreTilesPerWave / kScoreUnroll;
 constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 512
 
@@ -85,7 +91,13 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
       const int j = min(tile_key0(grp * kScoreUnroll + u) + n16, nmax - 1);  // clamp: a real row
       const char* rp = kbase + (size_t)j * DI * ES + g * 16;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) dst[u][c] = ld16_stream(rp + c * 64);
+      for (int c = 0; c < CH; ++c) {
+#if CSA_SCORE_STREAMING_LOADS
+        dst[u][c] = ld16_stream(rp + c * 64);
+#else
+        dst[u][c] = ld16(rp + c * 64);  // plain loads measured faster than the non-temporal hint
+#endif
+      }
     }
   };
 

@@ -58,10 +58,11 @@ struct AttnLayout {
   static constexpr int EP = 16 / ES;       // elements per piece
   static constexpr int DT = D / 16;        // output d tiles
   static constexpr int UPL = NP / 8;       // V staging units (4 rows x 1 piece) per lane
-  static constexpr int RS = 32 * ES + 16;  // LDS bytes per transposed V d-row (32 rows + pad)
+  static constexpr int RS = 32 * ES;       // LDS bytes per transposed V d-row (32 tile rows)
+  static constexpr int NCH = RS / 16;      // 16-byte chunks per d-row
   static constexpr int VT_BYTES = D * RS;
   static constexpr int MO_STRIDE = D + 1;  // floats per (wave, head) row in the merge area
-  static constexpr int MERGE_BYTES = (NW * 16 * MO_STRIDE + NW * 16 * 2) * 4;
+  static constexpr int MERGE_BYTES = (NW * 16 * MO_STRIDE + NW * 16) * 4;
   static constexpr int SMEM = (NW * VT_BYTES > MERGE_BYTES) ? NW * VT_BYTES : MERGE_BYTES;
   static_assert(UPL >= 1 && NP % 8 == 0, "head_dim too small for the V staging layout");
 };
@@ -71,10 +72,21 @@ struct AttnLayout {
 // {4g..4g+3, 16+4g..16+4g+3}, sit contiguously at 8g .. 8g+7.
 __device__ __forceinline__ int vt_pos_of_quad(int quad) { return 8 * (quad & 3) + 4 * (quad >> 2); }
 
+// Byte address of position `pos` of d-row `d` in a wave's transposed V tile.
+// The 16-byte chunk index is XOR-swizzled by d / 8, so the staging writes of
+// lanes that differ in d by multiples of 8 fall in different banks; a lane's
+// operand read stays one contiguous 16-byte chunk.
+template <int RS, int NCH, int ES>
+__device__ __forceinline__ int vt_off(int d, int pos) {
+  const int byte = pos * ES;
+  return d * RS + (((byte >> 4) ^ ((d >> 3) & (NCH - 1))) << 4) + (byte & 15);
+}
+
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a) {
   using L = AttnLayout<T, D, NW>;
   __shared__ __attribute__((aligned(16))) char smem[L::SMEM];
+  __shared__ float wmax[NW][16];   // per-wave tile maxima, one per head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
@@ -140,16 +152,18 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a) {
     for (int c = 0; c < L::CH; ++c) qf[c] = n16 < H ? ld16(qp + c * 64) : u32x4_t{0, 0, 0, 0};
   }
 
-  float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t acc[L::DT];
 #pragma unroll
   for (int dt = 0; dt < L::DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   char* vt = smem + wave * L::VT_BYTES;
+  float lg[2][4];  // base-2 logits of this wave's tile
+  float tmax = -INFINITY;
 
   // One 32-row tile per wave: all of its index and row loads are issued
   // together, so the wave waits for one index round trip and one row round trip.
   const int e0 = e_begin + wave * kTileRows;
-  if (e0 < e_end) {  // wave-uniform
+  const bool has_tile = e0 < e_end;  // wave-uniform
+  if (has_tile) {
 
     // K rows e0 + 16t + n16 as the A operand (16 bytes of each 64-byte chunk)
     u32x4_t kf[2][L::CH];
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a) {
 #pragma unroll
       for (int x = 0; x < L::EP; ++x) {
         const int d = pc * L::EP + x;
-        char* dst = vt + d * L::RS + pos * L::ES;
+        char* dst = vt + vt_off<L::RS, L::NCH, L::ES>(d, pos);
         if constexpr (L::ES == 2) {
           const int w = x >> 1;
           uint32_t lo, hi;
@@ -210,59 +224,63 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a) {
     }
     wave_lds_fence();
 
-    // online softmax over this tile (base-2 logits)
+    // base-2 logits of this tile; rows past the stream or without a row are masked
     const uint32_t vm0 = (uint32_t)__ballot(kval[0]) & 0xFFFFu;  // lanes 0..15: rows 0..15
     const uint32_t vm1 = (uint32_t)__ballot(kval[1]) & 0xFFFFu;  // rows 16..31
-    float x[2][4];
-    float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = ((t ? vm1 : vm0) >> (4 * g + i)) & 1u;
-        x[t][i] = ok ? sc[t][i] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[t][i]);
+        lg[t][i] = ok ? sc[t][i] * a.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, lg[t][i]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (tmax != -INFINITY) {  // some row is valid (wave-uniform: masks are per row)
-      float pr[2][4];
-      float psum = 0.0f;
+  }
+  // One softmax max per head for the whole workgroup, so the waves' partial
+  // sums can later be added without rescaling.
+  if (g == 0) wmax[wave][n16] = tmax;
+  __syncthreads();
+  float M = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[t][i] = x[t][i] == -INFINITY ? 0.0f : exp2f(x[t][i] - tmax);
-          psum += pr[t][i];
-        }
-      m_run = tmax;
-      l_run = psum;
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, wmax[w][n16]);
 
-      // O^T = V^T P^T: A = V^T (row d, tile rows on k), B = P^T (column = head)
-      if constexpr (L::ES == 2) {
-        u32x4_t pw;
+  float l_run = 0.0f;
+  if (has_tile && M != -INFINITY) {  // wave-uniform
+    float pr[2][4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int t = w >> 1, i0 = 2 * (w & 1);
-          pw[w] = float_to_bf16_bits(pr[t][i0]) | (float_to_bf16_bits(pr[t][i0 + 1]) << 16);
-        }
-        const bf16x8_t pf = as_bf16x8(pw);
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int dt = 0; dt < L::DT; ++dt) {
-          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(vt + (16 * dt + n16) * L::RS + g * 16);
-          acc[dt] = mfma_bf16(as_bf16x8(vf), pf, acc[dt]);
-        }
-      } else {
+      for (int i = 0; i < 4; ++i) {
+        pr[t][i] = lg[t][i] == -INFINITY ? 0.0f : exp2f(lg[t][i] - M);
+        l_run += pr[t][i];
+      }
+    // O^T = V^T P^T: A = V^T (row d, tile rows on k), B = P^T (column = head)
+    if constexpr (L::ES == 2) {
+      u32x4_t pw;
 #pragma unroll
-        for (int dt = 0; dt < L::DT; ++dt) {
-          const char* src = vt + (16 * dt + n16) * L::RS + g * 32;
-          const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(src);
-          const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(src + 16);
+      for (int w = 0; w < 4; ++w) {
+        const int t = w >> 1, i0 = 2 * (w & 1);
+        pw[w] = float_to_bf16_bits(pr[t][i0]) | (float_to_bf16_bits(pr[t][i0 + 1]) << 16);
+      }
+      const bf16x8_t pf = as_bf16x8(pw);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[dt] = mfma_f32(u32_as_float(v0[j]), pr[0][j], acc[dt]);
-            acc[dt] = mfma_f32(u32_as_float(v1[j]), pr[1][j], acc[dt]);
-          }
+      for (int dt = 0; dt < L::DT; ++dt) {
+        const u32x4_t vf =
+            *reinterpret_cast<const u32x4_t*>(vt + vt_off<L::RS, L::NCH, L::ES>(16 * dt + n16, 8 * g));
+        acc[dt] = mfma_bf16(as_bf16x8(vf), pf, acc[dt]);
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < L::DT; ++dt) {
+        const int d = 16 * dt + n16;
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(vt + vt_off<L::RS, L::NCH, L::ES>(d, 8 * g));
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(vt + vt_off<L::RS, L::NCH, L::ES>(d, 8 * g + 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[dt] = mfma_f32(u32_as_float(v0[j]), pr[0][j], acc[dt]);
+          acc[dt] = mfma_f32(u32_as_float(v1[j]), pr[1][j], acc[dt]);
         }
       }
     }
@@ -272,41 +290,37 @@ __global__ __launch_bounds__(NW * 64) void attn_split_kernel(AttnArgs a) {
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
-  // ---- fixed-order merge of the NW waves, one split partial out
+  // ---- the waves share M, so the split partial is a plain sum over waves,
+  // taken in fixed wave order
   __syncthreads();  // every wave is done with its V tile; reuse LDS
-  float* mo = reinterpret_cast<float*>(smem);                   // [wave][head][MO_STRIDE]
-  float* mml = mo + NW * 16 * L::MO_STRIDE;                     // [wave][head][2]
+  float* mo = reinterpret_cast<float*>(smem);          // [wave][head][MO_STRIDE]
+  float* ml = mo + NW * 16 * L::MO_STRIDE;             // [wave][head]
 #pragma unroll
   for (int dt = 0; dt < L::DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mo[(wave * 16 + n16) * L::MO_STRIDE + 16 * dt + 4 * g + i] = acc[dt][i];
-  if (g == 0) {
-    mml[(wave * 16 + n16) * 2] = m_run;
-    mml[(wave * 16 + n16) * 2 + 1] = l_tot;
-  }
+  if (g == 0) ml[wave * 16 + n16] = l_tot;
   __syncthreads();
   for (int item = tid; item < H * D; item += NW * 64) {
     const int h = item / D, d = item - h * D;
-    float M = -INFINITY;
+    float part[NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, mml[(w * 16 + h) * 2]);
-    float Lsum = 0.0f, o = 0.0f;
-    if (M != -INFINITY) {
+    for (int w = 0; w < NW; ++w) part[w] = mo[(w * 16 + h) * L::MO_STRIDE + d];
+    float o = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float lw = mml[(w * 16 + h) * 2 + 1];
-        if (lw > 0.0f) {
-          const float f = exp2f(mml[(w * 16 + h) * 2] - M);
-          Lsum += f * lw;
-          o += f * mo[(w * 16 + h) * L::MO_STRIDE + d];
-        }
-      }
-    }
+    for (int w = 0; w < NW; ++w) o += part[w];
     o_out[(size_t)h * D + d] = o;
-    if (d == 0) {
-      ml_out[2 * h] = M;
-      ml_out[2 * h + 1] = Lsum;
+  }
+  if (tid < H) {
+    const int h = tid;
+    float Lsum = 0.0f, Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      Lsum += ml[w * 16 + h];
+      Mh = fmaxf(Mh, wmax[w][h]);
     }
+    ml_out[2 * h] = Mh;
+    ml_out[2 * h + 1] = Lsum;
   }
 }
 
@@ -416,7 +430,10 @@ AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, i
   // fill the 256 CUs several times over; 4 waves (128 rows) below that, so
   // small batches still spread over many CUs.
   const long long rows = (long long)batch * q_per_req * (win + topk);
-  pl.waves_per_split = rows >= 65536 ? 8 : 4;
+#ifndef CSA_ATTN_WAVES8_ROWS
+#define CSA_ATTN_WAVES8_ROWS 65536
+#endif
+  pl.waves_per_split = rows >= CSA_ATTN_WAVES8_ROWS ? 8 : 4;
   pl.rows_per_split = pl.waves_per_split * kTileRows;
   pl.n_split_win = (win + pl.rows_per_split - 1) / pl.rows_per_split;
   pl.n_split_cmp = (topk + pl.rows_per_split - 1) / pl.rows_per_split;

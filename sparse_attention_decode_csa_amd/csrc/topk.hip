@@ -11,18 +11,19 @@
 // Design (one 1024-thread workgroup per query token):
 //   1. Map each score to an unsigned key whose integer order is the float
 //      order (-0 folded onto +0).  Rows of up to 32768 candidates are held in
-//      registers: thread t keeps keys t, t+1024, t+2048, ..., all loads issued
-//      before any use, so the row is fetched in one memory round trip.
-//   2. Find the exact K-th largest key with four 8-bit MSB-first radix
-//      passes: per-wave 256-bin LDS histograms of the keys that still match
-//      the decided prefix, a suffix scan, and the bin where the running count
-//      crosses the remaining rank.  This yields the threshold key T and how
-//      many keys equal to T are taken (the lowest-indexed ones).
-//   3. Emit in ascending index order: slice r (keys 1024r .. 1024r+1023) is
-//      spread over the 16 waves in index order, so ballots give each (slice,
-//      wave) its count of keys above T and equal to T; one wave scans those
-//      counts in index order into output offsets and tie ranks, and a second
-//      ballot walk writes the indices.
+//      registers, thread t owning a contiguous slice, all loads issued at once.
+//   2. Exact K-th largest key by MSB-first 8-bit radix select over LDS
+//      histograms.  For long rows the select first runs on a strided sample
+//      of 1024 keys, to a sample rank that keeps somewhat more than K rows;
+//      the rows at or above that threshold are compacted, and the exact
+//      select runs on those candidates only.  When the sample misleads (fewer
+//      than K rows kept, or more than the candidate buffer holds) the exact
+//      select runs on the whole row instead, so only the speed depends on the
+//      data.  The result is the threshold key T and how many keys equal to T
+//      are taken (the lowest-indexed ones).
+//   3. Emit in ascending index order: each thread counts its keys above and
+//      equal to T, one block scan turns the counts into output offsets and
+//      tie ranks, and each thread writes its slice.
 //   Longer rows (more than 32768 candidates) use the same selection with the
 //   keys re-read from global memory in every pass.
 // The selection never depends on a floating-point operation, so it is exact
@@ -178,15 +179,116 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[kHistWords];        // [16 waves][256 bins]
-  __shared__ uint32_t cnt[256];
-  __shared__ int misc[2];
-  __shared__ int seg_gt[KPT * kTopkWaves], seg_eq[KPT * kTopkWaves];     // [slice][wave]
-  __shared__ int seg_off[KPT * kTopkWaves], seg_eqoff[KPT * kTopkWaves];
+// Exclusive prefix sum of one int per thread over the block, in thread order;
+// also returns the block total.  `red` holds one int per wave.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) red[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int t = red[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + inc - v;
+}
 
+// Histograms of the block-wide selections, double buffered by pass parity so
+// that zeroing the next pass's histogram needs no barrier of its own.
+constexpr int kHistStride = 257;   // per-wave copies sit off the bank period
+struct SelectSmem {
+  uint32_t hist[2][kTopkWaves * kHistStride];
+  uint32_t cnt[2][256];
+  int res[2][3];   // per pass parity: (bin, keys above the bin, keys in the bin)
+  int red[kTopkWaves];
+};
+
+// Exact selection over keys spread across the block: thread t holds NK keys
+// with a validity predicate.  Finds the k-th largest key T, how many keys
+// equal to T belong to the top k (keq; the rest of the top k is strictly
+// above T) and how many keys equal T in all (eq_total).  Four MSB-first
+// 8-bit radix passes; PER_WAVE selects one histogram per wave (many keys)
+// or one shared histogram (few keys).  No floating point anywhere.
+template <bool PER_WAVE, int NK, typename Valid>
+__device__ void block_radix_select(const uint32_t (&keys)[NK], Valid valid, int k, SelectSmem& sm,
+                                   uint32_t& T, int& keq, int& eq_total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWords = PER_WAVE ? kTopkWaves * kHistStride : 256;
+  uint32_t prefix = 0u, pmask = 0u;
+  int krem = k;
+  for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[0][i] = 0u;
+  __syncthreads();
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass, par = pass & 1;
+    uint32_t* h = sm.hist[par];
+    uint32_t* wh = PER_WAVE ? h + wave * kHistStride : h;
+#pragma unroll
+    for (int r = 0; r < NK; ++r)
+      if (valid(r) && (keys[r] & pmask) == prefix) atomicAdd(&wh[(keys[r] >> shift) & 255u], 1u);
+    // the other buffer was last read before the previous pass's final barrier
+    for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[par ^ 1][i] = 0u;
+    __syncthreads();
+    const uint32_t* c = h;
+    if (PER_WAVE) {
+      if (tid < 256) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) t += h[w * kHistStride + tid];
+        sm.cnt[par][tid] = t;
+      }
+      __syncthreads();
+      c = sm.cnt[par];
+    }
+    if (wave == 0) {
+      // lane owns bins 4*lane .. 4*lane+3; keys in higher bins by a suffix scan
+      const uint32_t c0 = c[4 * lane], c1 = c[4 * lane + 1], c2 = c[4 * lane + 2],
+                     c3 = c[4 * lane + 3];
+      const uint32_t local = c0 + c1 + c2 + c3;
+      uint32_t suf = local;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t t = __shfl_down(suf, off);
+        if (lane + off < kWave) suf += t;
+      }
+      uint32_t run = suf - local;
+      const uint32_t cs[4] = {c3, c2, c1, c0};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        if (run < (uint32_t)krem && (uint32_t)krem <= run + cs[d]) {
+          sm.res[par][0] = 4 * lane + 3 - d;
+          sm.res[par][1] = (int)run;
+          sm.res[par][2] = (int)cs[d];
+        }
+        run += cs[d];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sm.res[par][0] << shift;
+    pmask |= 0xFFu << shift;
+    krem -= sm.res[par][1];
+    eq_total = sm.res[par][2];
+  }
+  T = prefix;
+  keq = krem;
+}
+
+// Candidate buffer: rows whose key clears the sampled threshold.
+constexpr int kCandCap = 8192;
+constexpr int kCandPerThread = kCandCap / kTopkThreads;
+
+// Thread t owns the contiguous slice [t*KPT, t*KPT + KPT) of the row; with
+// VEC4 the slice is read with 16-byte loads (rows 16-byte aligned).
+template <int KPT, bool VEC4>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
+  __shared__ SelectSmem sm;
+  __shared__ uint32_t cand[kCandCap];
+
+  const int tid = threadIdx.x;
   const int tok = blockIdx.x;
   const int S = a.q_per_req, b = tok / S, s = tok % S;
   const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
@@ -199,106 +301,97 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     return;
   }
 
-  // ---- the row, in registers (invalid slots read a real entry and are masked)
+  // ---- the row, in registers: slots past n are masked, never past n_cap read
   const float* row = a.scores + (size_t)tok * a.n_cap;
+  const int i0 = tid * KPT;
   uint32_t key[KPT];
+  if (VEC4 && i0 + KPT <= a.n_cap) {
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) key[r] = order_key(row[min(r * kTopkThreads + tid, n - 1)]);
-  auto valid = [&](int r) { return r * kTopkThreads + tid < n; };
+    for (int j = 0; j < KPT; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i0 + j);
+      key[j] = order_key(v.x);
+      key[j + 1] = order_key(v.y);
+      key[j + 2] = order_key(v.z);
+      key[j + 3] = order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = order_key(row[min(i0 + j, n - 1)]);
+  }
+  auto valid = [&](int j) { return i0 + j < n; };
 
-  // ---- exact K-th largest key by MSB-first radix select
-  uint32_t prefix = 0u, pmask = 0u;
-  int krem = K;
-  uint32_t* wh = hist + wave * 256;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kHistWords; i += kTopkThreads) hist[i] = 0u;
-    if (tid == 0) misc[0] = misc[1] = 0;
-    __syncthreads();
+  uint32_t T = 0u;
+  int keq = 0, eq_total = 0;
+  bool done = false;
+  if (n > kCandCap) {
+    // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT
+    const int js = tid % KPT;
+    uint32_t sk = 0u;  // key[js] without a dynamic register index
 #pragma unroll
-    for (int r = 0; r < KPT; ++r)
-      if (valid(r) && (key[r] & pmask) == prefix) atomicAdd(&wh[(key[r] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t t = 0u;
+    for (int j = 0; j < KPT; ++j) sk = j == js ? key[j] : sk;
+    const uint32_t skey[1] = {sk};
+    const bool sval = valid(js);
+    int m;
+    (void)block_exclusive_scan(sval ? 1 : 0, sm.red, m);
+    // sample rank expected at row rank K, plus three standard deviations, so
+    // that the threshold keeps at least K rows
+    const int ks0 = (int)(((long long)K * m + n - 1) / n);
+    const int ks = min(m, ks0 + 3 * (int)sqrtf((float)ks0) + 4);
+    uint32_t tau;
+    int u0, u1;
+    block_radix_select<false>(skey, [&](int) { return sval; }, ks, sm, tau, u0, u1);
+    // ---- rows at or above the threshold, compacted (thread order)
+    int mine = 0;
 #pragma unroll
-      for (int w = 0; w < kTopkWaves; ++w) t += hist[w * 256 + tid];
-      cnt[tid] = t;
+    for (int j = 0; j < KPT; ++j) mine += (valid(j) && key[j] >= tau) ? 1 : 0;
+    int c;
+    int pos = block_exclusive_scan(mine, sm.red, c);
+    if (c >= K && c <= kCandCap) {  // block-uniform
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (valid(j) && key[j] >= tau) cand[pos++] = key[j];
+      __syncthreads();
+      uint32_t ck[kCandPerThread];
+#pragma unroll
+      for (int r = 0; r < kCandPerThread; ++r) ck[r] = cand[min(r * kTopkThreads + tid, c - 1)];
+      block_radix_select<true>(ck, [&](int r) { return r * kTopkThreads + tid < c; }, K, sm, T, keq,
+                               eq_total);
+      done = true;
     }
-    __syncthreads();
-    if (wave == 0) {
-      const uint32_t c0 = cnt[4 * lane], c1 = cnt[4 * lane + 1], c2 = cnt[4 * lane + 2],
-                     c3 = cnt[4 * lane + 3];
-      const uint32_t local = c0 + c1 + c2 + c3;
-      uint32_t suf = local;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = __shfl_down(suf, off);
-        if (lane + off < kWave) suf += t;
-      }
-      uint32_t run = suf - local;  // keys in higher bins
-      const uint32_t cs[4] = {c3, c2, c1, c0};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        if (run < (uint32_t)krem && (uint32_t)krem <= run + cs[d]) {
-          misc[0] = 4 * lane + 3 - d;
-          misc[1] = (int)run;
-        }
-        run += cs[d];
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)misc[0] << shift;
-    pmask |= 0xFFu << shift;
-    krem -= misc[1];
   }
-  const uint32_t T = prefix;  // the K-th largest key
-  const int keq = krem;       // keys equal to T that are taken
+  if (!done) block_radix_select<true>(key, valid, K, sm, T, keq, eq_total);
 
-  // ---- counts per (slice, wave), in index order
+  // ---- ascending-index emission: per-thread (above, equal) counts packed in
+  // one int (each < 2^16), one block scan, then each thread writes its slice
+  int gt = 0, eq = 0;
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const int cg = __popcll(__ballot(valid(r) && key[r] > T));
-    const int ce = __popcll(__ballot(valid(r) && key[r] == T));
-    if (lane == 0) {
-      seg_gt[r * kTopkWaves + wave] = cg;
-      seg_eq[r * kTopkWaves + wave] = ce;
-    }
+  for (int j = 0; j < KPT; ++j) {
+    gt += (valid(j) && key[j] > T) ? 1 : 0;
+    eq += (valid(j) && key[j] == T) ? 1 : 0;
   }
-  __syncthreads();
-  if (wave == 0) {
-    constexpr int PL = KPT * kTopkWaves / kWave;  // entries per lane, contiguous
-    const int e0 = lane * PL;
-    int le = 0;
+  int tot;
+  const int before = block_exclusive_scan(gt | (eq << 16), sm.red, tot);
+  const int gt_before = before & 0xFFFF, eq_before = before >> 16;
+  // every key above T is taken; of the keys equal to T, the keq lowest-indexed
+  int eq_rank = eq_before;
+  int dst = gt_before + min(eq_before, keq);
 #pragma unroll
-    for (int k = 0; k < PL; ++k) le += seg_eq[e0 + k];
-    int E = wave_inclusive_scan(le) - le;
-    int sel[PL], ls = 0;
-#pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      const int eq = seg_eq[e0 + k];
-      seg_eqoff[e0 + k] = E;
-      sel[k] = seg_gt[e0 + k] + min(eq, max(0, keq - E));
-      E += eq;
-      ls += sel[k];
-    }
-    int O = wave_inclusive_scan(ls) - ls;
-#pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      seg_off[e0 + k] = O;
-      O += sel[k];
-    }
+  for (int j = 0; j < KPT; ++j) {
+    const bool is_eq = valid(j) && key[j] == T;
+    const bool take = (valid(j) && key[j] > T) || (is_eq && eq_rank < keq);
+    eq_rank += is_eq ? 1 : 0;
+    if (take && dst < K) out[dst] = i0 + j;  // exactly K are taken; bound is a safeguard
+    dst += take ? 1 : 0;
   }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const bool gt = valid(r) && key[r] > T;
-    const bool eq = valid(r) && key[r] == T;
-    const uint64_t meq = __ballot(eq);
-    const bool take = gt || (eq && seg_eqoff[r * kTopkWaves + wave] + popc_below(meq) < keq);
-    const uint64_t msel = __ballot(take);
-    const int dst = seg_off[r * kTopkWaves + wave] + popc_below(msel);
-    if (take && dst < K) out[dst] = r * kTopkThreads + tid;  // exactly K are taken; bound is a safeguard
-  }
+  (void)eq_total;
+}
+
+template <int KPT>
+void launch_reg(const TopkArgs& a, bool vec4, dim3 grid, dim3 block, hipStream_t st) {
+  if (vec4)
+    hipLaunchKernelGGL((topk_reg_kernel<KPT, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((topk_reg_kernel<KPT, false>), grid, block, 0, st, a);
 }
 
 }  // namespace
@@ -306,14 +399,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int n_bound = std::min(a.n_cap, a.max_len / a.ratio);
   const dim3 grid(a.batch * a.q_per_req), block(kTopkThreads);
+  // rows start 16-byte aligned when n_cap is a multiple of 4 floats
+#ifndef CSA_TOPK_VEC4_MAX_KPT
+#define CSA_TOPK_VEC4_MAX_KPT 32
+#endif
+  const bool vec4 = (a.n_cap & 3) == 0 && n_bound <= CSA_TOPK_VEC4_MAX_KPT * kTopkThreads;
   if (n_bound <= 4 * kTopkThreads) {
-    hipLaunchKernelGGL(topk_reg_kernel<4>, grid, block, 0, st, a);
+    launch_reg<4>(a, vec4, grid, block, st);
   } else if (n_bound <= 8 * kTopkThreads) {
-    hipLaunchKernelGGL(topk_reg_kernel<8>, grid, block, 0, st, a);
+    launch_reg<8>(a, vec4, grid, block, st);
   } else if (n_bound <= 16 * kTopkThreads) {
-    hipLaunchKernelGGL(topk_reg_kernel<16>, grid, block, 0, st, a);
+    launch_reg<16>(a, vec4, grid, block, st);
   } else if (n_bound <= 32 * kTopkThreads) {
-    hipLaunchKernelGGL(topk_reg_kernel<32>, grid, block, 0, st, a);
+    launch_reg<32>(a, vec4, grid, block, st);
   } else {
     hipLaunchKernelGGL(topk_global_kernel, grid, block, 0, st, a);
   }

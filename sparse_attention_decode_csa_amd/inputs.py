@@ -315,6 +315,14 @@ def random_scores(seed: int, B: int, S: int, n_cap: int, kind: str = "normal") -
         return g.standard_normal(size=(B, S, n_cap), dtype=np.float32)
     if kind == "coarse":   # few distinct values: heavy ties
         return (g.integers(-8, 9, size=(B, S, n_cap)) / 4.0).astype(np.float32)
+    if kind.startswith("spiked"):
+        # large values exactly at row positions i with (i // 1024) == (i % 1024) % m:
+        # a strided sample of the row then sees only the spikes
+        m = int(kind[len("spiked"):])
+        v = g.standard_normal(size=(B, S, n_cap), dtype=np.float32)
+        i = np.arange(n_cap)
+        v[..., (i // 1024) == (i % 1024) % m] += 100.0
+        return v
     if kind == "signed_zero":
         s = g.integers(0, 3, size=(B, S, n_cap)).astype(np.float32) - 1.0
         z = g.random(size=(B, S, n_cap)) < 0.5

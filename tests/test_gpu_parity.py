@@ -135,10 +135,14 @@ def test_topk_exact_on_oracle_scores(cid, config_inputs):
     assert np.array_equal(got["topk_idx"], ref["topk_idx"])
 
 
-@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero"])
+@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero", "spiked16", "spiked32"])
 @pytest.mark.parametrize("n_cap,topk", [(300, 64), (4096, 256), (4096, 257), (9000, 1024),
-                                        (32768, 1024), (32768, 4096), (40000, 2048), (1000, 999)])
+                                        (16384, 512), (32768, 1024), (32768, 4096), (40000, 2048),
+                                        (1000, 999), (20000, 4000)])
 def test_topk_exact_synthetic(kind, n_cap, topk):
+    # "spiked" rows put their largest values exactly where the selection's
+    # strided sample looks, so the sampled threshold keeps too few rows and
+    # the full-row selection must take over; "coarse" rows tie heavily.
     # rows of several visible lengths, including n_vis == K and K + 1
     B, S = 3, 2
     sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=16, heads=1,
