@@ -168,15 +168,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_global_kernel(TopkArgs a) {
   }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: four
+// row_shr steps scan each 16-lane row (lanes shifted in from outside the row
+// read 0), then each row adds the totals of the rows below it, read with
+// readlane.  No LDS round trip.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Exclusive prefix sum of one int per thread over the block, in thread order;
@@ -204,32 +210,69 @@ constexpr int kHistStride = 257;   // per-wave copies sit off the bank period
 struct SelectSmem {
   uint32_t hist[2][kTopkWaves * kHistStride];
   uint32_t cnt[2][256];
-  int res[2][3];   // per pass parity: (bin, keys above the bin, keys in the bin)
-  int red[kTopkWaves];
+  int res[2][2];   // per pass parity: (bin, keys above the bin)
+  int red[2 * kTopkWaves];
 };
 
-// Exact selection over keys spread across the block: thread t holds NK keys
-// with a validity predicate.  Finds the k-th largest key T, how many keys
-// equal to T belong to the top k (keq; the rest of the top k is strictly
-// above T) and how many keys equal T in all (eq_total).  Four MSB-first
-// 8-bit radix passes; PER_WAVE selects one histogram per wave (many keys)
-// or one shared histogram (few keys).  No floating point anywhere.
-template <bool PER_WAVE, int NK, typename Valid>
-__device__ void block_radix_select(const uint32_t (&keys)[NK], Valid valid, int k, SelectSmem& sm,
-                                   uint32_t& T, int& keq, int& eq_total) {
+// Block-wide minimum and maximum of one key per thread (invalid threads pass
+// UINT32_MAX / 0).  `red` holds two ints per wave.
+__device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red, uint32_t& mn,
+                                              uint32_t& mx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+  }
+  if (lane == 0) {
+    red[2 * wave] = (int)lo;
+    red[2 * wave + 1] = (int)hi;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    mn = min(mn, (uint32_t)red[2 * w]);
+    mx = max(mx, (uint32_t)red[2 * w + 1]);
+  }
+  __syncthreads();
+}
+
+// Exact selection over keys spread across the block: thread t holds NK keys,
+// read through key(r) with validity valid(r).  Every valid key lies in
+// [lo, hi].  Finds the k-th largest key T, how many keys equal to T belong to
+// the top k (keq; the rest of the top k is strictly above T).  MSB-first
+// radix passes of up to 8 bits over only the bits below the common prefix of
+// lo and hi (keys in a narrow range share their leading bits, and those are
+// exactly the digits on which histogram atomics would pile up on one bin).
+// PER_WAVE selects one histogram per wave (many keys) or one shared
+// histogram (few keys).  With max_passes < 4 the select stops early and T is
+// the lower edge of the bin holding the k-th key (at least k keys are >= T).
+// No floating point anywhere.
+template <bool PER_WAVE, int NK, typename Key, typename Valid>
+__device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uint32_t hi,
+                                   SelectSmem& sm, uint32_t& T, int& keq, int max_passes = 4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kWords = PER_WAVE ? kTopkWaves * kHistStride : 256;
-  uint32_t prefix = 0u, pmask = 0u;
+  const int nb = lo == hi ? 0 : 32 - __clz(lo ^ hi);   // bits still to decide
+  uint32_t pmask = nb == 32 ? 0u : ~((1u << nb) - 1u);
+  uint32_t prefix = lo & pmask;
   int krem = k;
   for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[0][i] = 0u;
   __syncthreads();
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass, par = pass & 1;
+  int pass = 0;
+  for (int top = nb; top > 0; top -= 8, ++pass) {
+    const int shift = top > 8 ? top - 8 : 0;
+    const uint32_t dmask = (1u << (top - shift)) - 1u;
+    const int par = pass & 1;
     uint32_t* h = sm.hist[par];
     uint32_t* wh = PER_WAVE ? h + wave * kHistStride : h;
 #pragma unroll
-    for (int r = 0; r < NK; ++r)
-      if (valid(r) && (keys[r] & pmask) == prefix) atomicAdd(&wh[(keys[r] >> shift) & 255u], 1u);
+    for (int r = 0; r < NK; ++r) {
+      const uint32_t kv = key(r);
+      if (valid(r) && (kv & pmask) == prefix) atomicAdd(&wh[(kv >> shift) & dmask], 1u);
+    }
     // the other buffer was last read before the previous pass's final barrier
     for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[par ^ 1][i] = 0u;
     __syncthreads();
@@ -245,48 +288,76 @@ __device__ void block_radix_select(const uint32_t (&keys)[NK], Valid valid, int 
       c = sm.cnt[par];
     }
     if (wave == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; keys in higher bins by a suffix scan
-      const uint32_t c0 = c[4 * lane], c1 = c[4 * lane + 1], c2 = c[4 * lane + 2],
-                     c3 = c[4 * lane + 3];
-      const uint32_t local = c0 + c1 + c2 + c3;
-      uint32_t suf = local;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t t = __shfl_down(suf, off);
-        if (lane + off < kWave) suf += t;
-      }
-      uint32_t run = suf - local;
-      const uint32_t cs[4] = {c3, c2, c1, c0};
+      // lane owns bins 255-4*lane down to 252-4*lane, so a prefix scan over
+      // lanes counts the keys in all higher bins
+      const int b0 = 255 - 4 * lane;
+      const int cs[4] = {(int)c[b0], (int)c[b0 - 1], (int)c[b0 - 2], (int)c[b0 - 3]};
+      const int local = cs[0] + cs[1] + cs[2] + cs[3];
+      int run = wave_inclusive_scan(local) - local;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        if (run < (uint32_t)krem && (uint32_t)krem <= run + cs[d]) {
-          sm.res[par][0] = 4 * lane + 3 - d;
-          sm.res[par][1] = (int)run;
-          sm.res[par][2] = (int)cs[d];
+        if (run < krem && krem <= run + cs[d]) {
+          sm.res[par][0] = b0 - d;
+          sm.res[par][1] = run;
         }
         run += cs[d];
       }
     }
     __syncthreads();
     prefix |= (uint32_t)sm.res[par][0] << shift;
-    pmask |= 0xFFu << shift;
+    pmask |= dmask << shift;
     krem -= sm.res[par][1];
-    eq_total = sm.res[par][2];
+    if (pass + 1 == max_passes) break;
   }
   T = prefix;
   keq = krem;
 }
 
-// Candidate buffer: rows whose key clears the sampled threshold.
+// Candidate buffer: rows whose key clears the sampled threshold, kept as
+// (key, row index) pairs in ascending row order.
 constexpr int kCandCap = 8192;
 constexpr int kCandPerThread = kCandCap / kTopkThreads;
+
+// Ascending-index emission of the selection {key > T} plus the keq
+// lowest-indexed keys equal to T, over items that thread t holds as a
+// contiguous run in index order: item(j) for j < cnt gives (key, row index).
+template <int NJ, typename Item>
+__device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, int keq,
+                                               int32_t* out, int K, int* red) {
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (j < cnt) {
+      const uint32_t kv = item(j).x;
+      gt += kv > T ? 1 : 0;
+      eq += kv == T ? 1 : 0;
+    }
+  }
+  int tot;
+  // both counts packed in one int: each block total is at most 32768 < 2^16
+  const int before = block_exclusive_scan(gt | (eq << 16), red, tot);
+  int eq_rank = before >> 16;
+  int dst = (before & 0xFFFF) + min(eq_rank, keq);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (j < cnt) {
+      const uint2 it = item(j);
+      const bool is_eq = it.x == T;
+      const bool take = it.x > T || (is_eq && eq_rank < keq);
+      eq_rank += is_eq ? 1 : 0;
+      if (take && dst < K) out[dst] = (int32_t)it.y;  // exactly K are taken; bound is a safeguard
+      dst += take ? 1 : 0;
+    }
+  }
+}
 
 // Thread t owns the contiguous slice [t*KPT, t*KPT + KPT) of the row; with
 // VEC4 the slice is read with 16-byte loads (rows 16-byte aligned).
 template <int KPT, bool VEC4>
 __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
   __shared__ SelectSmem sm;
-  __shared__ uint32_t cand[kCandCap];
+  __shared__ uint32_t cand_key[kCandCap];
+  __shared__ uint32_t cand_idx[kCandCap];
 
   const int tid = threadIdx.x;
   const int tok = blockIdx.x;
@@ -301,7 +372,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     return;
   }
 
-  // ---- the row, in registers: slots past n are masked, never past n_cap read
+  // ---- the row, in registers.  Slots past n hold a copy of a valid key of
+  // the same thread (or of row n-1), so they never widen the key range;
+  // nothing past n_cap is read.
   const float* row = a.scores + (size_t)tok * a.n_cap;
   const int i0 = tid * KPT;
   uint32_t key[KPT];
@@ -314,22 +387,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
       key[j + 2] = order_key(v.z);
       key[j + 3] = order_key(v.w);
     }
+    if (i0 + KPT > n) {  // the one thread straddling n
+      const uint32_t last = i0 < n ? key[0] : order_key(row[n - 1]);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) key[j] = i0 + j < n ? key[j] : last;
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = order_key(row[min(i0 + j, n - 1)]);
   }
   auto valid = [&](int j) { return i0 + j < n; };
+  uint32_t kmin = key[0], kmax = key[0];
+#pragma unroll
+  for (int j = 1; j < KPT; ++j) {
+    kmin = min(kmin, key[j]);
+    kmax = max(kmax, key[j]);
+  }
+  uint32_t row_min, row_max;
+  block_min_max(kmin, kmax, sm.red, row_min, row_max);
 
-  uint32_t T = 0u;
-  int keq = 0, eq_total = 0;
-  bool done = false;
   if (n > kCandCap) {
-    // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT
+    // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT.
+    // Two 8-bit passes are enough: the threshold is the lower edge of the
+    // 16-bit bin holding the sample rank, which only keeps a few more rows.
     const int js = tid % KPT;
     uint32_t sk = 0u;  // key[js] without a dynamic register index
 #pragma unroll
     for (int j = 0; j < KPT; ++j) sk = j == js ? key[j] : sk;
-    const uint32_t skey[1] = {sk};
     const bool sval = valid(js);
     int m;
     (void)block_exclusive_scan(sval ? 1 : 0, sm.red, m);
@@ -338,9 +422,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     const int ks0 = (int)(((long long)K * m + n - 1) / n);
     const int ks = min(m, ks0 + 3 * (int)sqrtf((float)ks0) + 4);
     uint32_t tau;
-    int u0, u1;
-    block_radix_select<false>(skey, [&](int) { return sval; }, ks, sm, tau, u0, u1);
-    // ---- rows at or above the threshold, compacted (thread order)
+    int unused;
+    block_radix_select<false, 1>([&](int) { return sk; }, [&](int) { return sval; }, ks, row_min,
+                                 row_max, sm, tau, unused, 2);
+    // ---- rows at or above the threshold, compacted in row order
     int mine = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) mine += (valid(j) && key[j] >= tau) ? 1 : 0;
@@ -349,41 +434,35 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     if (c >= K && c <= kCandCap) {  // block-uniform
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if (valid(j) && key[j] >= tau) cand[pos++] = key[j];
+        if (valid(j) && key[j] >= tau && pos < kCandCap) {
+          cand_key[pos] = key[j];
+          cand_idx[pos] = (uint32_t)(i0 + j);
+          ++pos;
+        }
       __syncthreads();
-      uint32_t ck[kCandPerThread];
-#pragma unroll
-      for (int r = 0; r < kCandPerThread; ++r) ck[r] = cand[min(r * kTopkThreads + tid, c - 1)];
-      block_radix_select<true>(ck, [&](int r) { return r * kTopkThreads + tid < c; }, K, sm, T, keq,
-                               eq_total);
-      done = true;
+      // every candidate lies in [tau, row max]
+      uint32_t T;
+      int keq;
+      block_radix_select<true, kCandPerThread>(
+          [&](int r) { return cand_key[min(r * kTopkThreads + tid, c - 1)]; },
+          [&](int r) { return r * kTopkThreads + tid < c; }, K, tau, row_max, sm, T, keq);
+      // emission over the candidates only: thread t takes a contiguous run
+      const int cpt = (c + kTopkThreads - 1) / kTopkThreads;
+      const int c0 = min(c, tid * cpt), cnt = min(c, c0 + cpt) - c0;
+      emit_selection<kCandPerThread>(
+          [&](int j) { return make_uint2(cand_key[c0 + j], cand_idx[c0 + j]); }, cnt, T, keq, out, K,
+          sm.red);
+      return;
     }
   }
-  if (!done) block_radix_select<true>(key, valid, K, sm, T, keq, eq_total);
-
-  // ---- ascending-index emission: per-thread (above, equal) counts packed in
-  // one int (each < 2^16), one block scan, then each thread writes its slice
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    gt += (valid(j) && key[j] > T) ? 1 : 0;
-    eq += (valid(j) && key[j] == T) ? 1 : 0;
-  }
-  int tot;
-  const int before = block_exclusive_scan(gt | (eq << 16), sm.red, tot);
-  const int gt_before = before & 0xFFFF, eq_before = before >> 16;
-  // every key above T is taken; of the keys equal to T, the keq lowest-indexed
-  int eq_rank = eq_before;
-  int dst = gt_before + min(eq_before, keq);
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const bool is_eq = valid(j) && key[j] == T;
-    const bool take = (valid(j) && key[j] > T) || (is_eq && eq_rank < keq);
-    eq_rank += is_eq ? 1 : 0;
-    if (take && dst < K) out[dst] = i0 + j;  // exactly K are taken; bound is a safeguard
-    dst += take ? 1 : 0;
-  }
-  (void)eq_total;
+  // ---- whole-row selection and emission
+  uint32_t T;
+  int keq;
+  block_radix_select<true, KPT>([&](int j) { return key[j]; }, valid, K, row_min, row_max, sm, T,
+                                keq);
+  const int cnt = max(0, min(KPT, n - i0));
+  emit_selection<KPT>([&](int j) { return make_uint2(key[j], (uint32_t)(i0 + j)); }, cnt, T, keq,
+                      out, K, sm.red);
 }
 
 template <int KPT>
