@@ -136,7 +136,9 @@ size_t csa_topk_workspace_bytes(const csa_shape_t* shape);
 csa_status_t csa_topk(const csa_shape_t* shape, const float* scores, const int32_t* start_pos,
                       int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes csa_sparse_attn_decode needs for this shape (split partials). */
+/* Workspace bytes csa_sparse_attn_decode needs for this shape (split
+ * partials).  Its contents need no initialisation; calls that overlap in time
+ * must not share a workspace. */
 size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* shape);
 
 /* Two-stream sparse attention of every query token, merged, RoPE undone, packed.

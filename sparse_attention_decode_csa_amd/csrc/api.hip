@@ -112,8 +112,7 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
       !aligned16(v_cmp) || !aligned16(topk_idx) || !aligned16(start_pos) || !aligned16(out) ||
       !aligned16(ws) || (rope_cos && !aligned16(rope_cos)) || (rope_sin && !aligned16(rope_sin)))
     return CSA_ERR_ALIGNMENT;
-  float* wsf = static_cast<float*>(ws);
-  const size_t o_floats = (pl.ws_o_floats * 4 + 255) / 256 * 256 / 4;
+  char* wsb = static_cast<char*>(ws);
   csa::AttnArgs a{};
   a.q = q;
   a.k_win = k_win;
@@ -125,8 +124,8 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
   a.out = out;
-  a.ws_o = wsf;
-  a.ws_ml = wsf + o_floats;
+  a.ws_o = reinterpret_cast<float*>(wsb);
+  a.ws_ml = reinterpret_cast<float*>(wsb + pl.ws_o_bytes);
   a.batch = sh->batch;
   a.q_per_req = sh->q_per_req;
   a.n_cap = sh->n_cap;
@@ -140,7 +139,7 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   a.max_len = sh->max_len;
   a.dtype = sh->dtype;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.waves_per_split = pl.waves_per_split;
+  a.tiles_per_wave = pl.tiles_per_wave;
   a.n_split_win = pl.n_split_win;
   a.n_split_cmp = pl.n_split_cmp;
   (void)hipGetLastError();

@@ -41,16 +41,17 @@ struct AttnArgs {
   int batch, q_per_req, n_cap, topk, win, w_cap, heads, head_dim, rope_dim, out_groups,
       max_len, dtype;
   float scale_log2;         // softmax_scale * log2(e)
-  int waves_per_split, n_split_win, n_split_cmp;
+  int tiles_per_wave, n_split_win, n_split_cmp;
 };
 
 // Split plan of the attention kernel; a function of the shape only, so the
 // workspace query and the launch always agree.
 struct AttnPlan {
-  int waves_per_split;  // waves per workgroup, one 32-row tile each
-  int rows_per_split;   // 32 * waves_per_split
+  int tiles_per_wave;   // 32-row tiles per wave (4 waves per workgroup)
+  int rows_per_split;   // 128 * tiles_per_wave
   int n_split_win, n_split_cmp;
-  size_t ws_o_floats, ws_ml_floats, ws_bytes;
+  size_t ws_o_floats, ws_ml_floats;
+  size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 
 AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk);
