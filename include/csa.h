@@ -169,7 +169,9 @@ size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* shape);
  *   rope_cos, rope_sin [rope_rows][Dr/2] float32, rope_rows >= max_len
  *   out      [G][B*S][(H/G)*D]   dtype output
  *   ws       at least csa_sparse_attn_workspace_bytes(shape) bytes
- * Requires w_cap >= win + S - 1.
+ * Requires w_cap >= win + S - 1.  One request's slice of a K or V cache
+ * (n_cap or w_cap rows) must stay below 2^31 - 4096 bytes, else
+ * CSA_ERR_UNSUPPORTED.
  */
 csa_status_t csa_sparse_attn_decode(const csa_shape_t* shape, const void* q, const void* k_win,
                                     const void* v_win, const void* k_cmp, const void* v_cmp,

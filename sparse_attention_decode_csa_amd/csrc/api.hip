@@ -83,7 +83,7 @@ csa_status_t csa_topk(const csa_shape_t* sh, const float* scores, const int32_t*
 size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* sh) {
   bool empty = false;
   if (check_common(sh, &empty) != CSA_OK || empty) return 0;
-  return csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk).ws_bytes;
+  return csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk, sh->dtype).ws_bytes;
 }
 
 csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const void* k_win,
@@ -105,8 +105,13 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   if (sh->heads > 16) return CSA_ERR_UNSUPPORTED;
   if ((int64_t)sh->w_cap < (int64_t)sh->win + sh->q_per_req - 1) return CSA_ERR_CAPACITY;
   if (sh->rope_dim > 0 && rope_rows < sh->max_len) return CSA_ERR_CAPACITY;
+  {  // one request's cache slice is addressed with 32-bit byte offsets
+    const int64_t row = (int64_t)sh->head_dim * (sh->dtype == CSA_DTYPE_BF16 ? 2 : 4);
+    if ((int64_t)sh->n_cap * row > csa::kMaxSliceBytes || (int64_t)sh->w_cap * row > csa::kMaxSliceBytes)
+      return CSA_ERR_UNSUPPORTED;
+  }
   const csa::AttnPlan pl =
-      csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk);
+      csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk, sh->dtype);
   if (!ws || ws_bytes < pl.ws_bytes) return CSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_win) || !aligned16(v_win) || !aligned16(k_cmp) ||
       !aligned16(v_cmp) || !aligned16(topk_idx) || !aligned16(start_pos) || !aligned16(out) ||
@@ -139,7 +144,7 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   a.max_len = sh->max_len;
   a.dtype = sh->dtype;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  a.tiles_per_wave = pl.tiles_per_wave;
+  a.chunks_per_wave = pl.chunks_per_wave;
   a.n_split_win = pl.n_split_win;
   a.n_split_cmp = pl.n_split_cmp;
   (void)hipGetLastError();

@@ -55,6 +55,30 @@ __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x16 bf16: lane l supplies 4 elements of A row (l % 16) and of B
+// column (l % 16), k-slots 4g .. 4g+3.
+__device__ __forceinline__ f32x4_t mfma_bf16_k16(bf16x4_t a, bf16x4_t b, f32x4_t c) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                    c, 0, 0, 0);
+}
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format,
+// no swizzle).  Loads through such a resource whose offset falls outside its
+// byte range return zero and do not access memory.
+constexpr int kBufferConfig = 0x00020000;
+
+// Buffer resource over [base, base + bytes).  base and bytes must be the same
+// in every lane; they are moved to scalar registers explicitly, since a
+// resource the compiler cannot prove uniform turns each load into a loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* up = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufferConfig);
+}
+
 __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

@@ -41,20 +41,24 @@ struct AttnArgs {
   int batch, q_per_req, n_cap, topk, win, w_cap, heads, head_dim, rope_dim, out_groups,
       max_len, dtype;
   float scale_log2;         // softmax_scale * log2(e)
-  int tiles_per_wave, n_split_win, n_split_cmp;
+  int chunks_per_wave, n_split_win, n_split_cmp;
 };
 
 // Split plan of the attention kernel; a function of the shape only, so the
 // workspace query and the launch always agree.
 struct AttnPlan {
-  int tiles_per_wave;   // 32-row tiles per wave (4 waves per workgroup)
-  int rows_per_split;   // 128 * tiles_per_wave
+  int chunks_per_wave;  // 16-row chunks per wave (4 waves per workgroup)
+  int rows_per_split;   // 64 * chunks_per_wave
   int n_split_win, n_split_cmp;
   size_t ws_o_floats, ws_ml_floats;
   size_t ws_o_bytes, ws_ml_bytes, ws_bytes;
 };
 
-AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk);
+AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk, int dtype);
+
+// Largest per-request K or V cache slice (bytes) the attention kernel
+// addresses: offsets are 32-bit and out-of-range rows use offsets >= 2^31.
+constexpr int64_t kMaxSliceBytes = 0x7FFFF000LL;
 
 hipError_t launch_indexer_score(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);

@@ -14,17 +14,23 @@
 // fixes to DSpark", description, last item).
 //
 // Design on gfx950:
-//   attn_split_kernel:
-//   A workgroup of 4 waves owns one (token, split): up to 128 * TPW rows of
-//   ONE stream.  Each wave takes TPW 32-row tiles (the 4 waves cover 128
-//   consecutive rows per step) and keeps an online softmax across them.
-//   - K rows go straight from HBM into the MFMA A operand (16-byte contiguous
-//     loads per lane); logits^T = K q^T puts heads on the lane axis, so the
-//     softmax statistics of a head live in the 4 lanes sharing its column.
-//   - V needs tile rows on the k axis of the PV MFMA, so each wave stages its
-//     32 x D V tile in LDS transposed (4 rows x 8 dims per lane, 64-bit LDS
-//     writes, 16-byte chunks XOR-swizzled by d / 8) and reads it back as
-//     16-byte operand fragments.
+//   attn_split_kernel: a workgroup of 4 waves owns one (token, split), i.e.
+//   up to 4 * 16 * CPW consecutive entries of ONE stream; each wave owns a
+//   contiguous run of 16 * CPW of them and walks it in 16-row chunks.
+//   - Latency first: the wave fetches the row numbers of its whole run with a
+//     single load (one Top-K entry, or one ring slot, per lane) and hands them
+//     to the lanes that need them with cross-lane moves, so no chunk waits on
+//     an index load; the next chunk's K/V loads are issued before the current
+//     chunk is computed (one chunk of prefetch, all in registers).
+//   - K and V are read with buffer loads against a per-request range; a row
+//     that is padding or past the end gets an out-of-range offset, which the
+//     hardware answers with zeros without touching memory.
+//   - logits^T = K q^T (16x16x32 bf16 MFMA, or 16x16x4 fp32) leaves lane
+//     (head n, group g) with rows 4g..4g+3 of the chunk, which is exactly the
+//     B operand of the 16x16x16 PV product O^T += V^T P^T.  Its A operand
+//     takes V straight from registers: lane (m, g) loads rows 4g..4g+3 at
+//     dims [m*D/16, (m+1)*D/16) and output row m of d-tile t stands for dim
+//     m*D/16 + t.  No LDS round trip and no transpose for V.
 //   - The 4 waves' (max, sum, O) are merged through LDS in fixed wave order
 //     into one split partial in the workspace.
 //   attn_finish_kernel: one thread per (token, head, dim pair) merges the
@@ -40,39 +46,117 @@
 namespace csa {
 namespace {
 
-constexpr int kTileRows = 32;
+constexpr int kChunk = 16;  // rows per MFMA chunk
 constexpr int kWaves = 4;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any valid range
 
 template <typename T, int D>
-struct AttnLayout {
+struct AttnGeo {
   static constexpr int ES = sizeof(T);
-  static constexpr int CH = D * ES / 64;   // 64-byte chunks per row (K fragments)
-  static constexpr int NP = D * ES / 16;   // 16-byte pieces per row
-  static constexpr int EP = 16 / ES;       // elements per piece
-  static constexpr int DT = D / 16;        // output d tiles
-  static constexpr int UPL = NP / 8;       // V staging units (4 rows x 1 piece) per lane
-  static constexpr int RS = 32 * ES;       // LDS bytes per transposed V d-row (32 tile rows)
-  static constexpr int NCH = RS / 16;      // 16-byte chunks per d-row
-  static constexpr int VT_BYTES = D * RS;
-  static constexpr int MO_STRIDE = D + 1;  // floats per (wave, head) row in the merge area
-  static constexpr int MERGE_BYTES = kWaves * 16 * MO_STRIDE * 4;
-  static constexpr int SMEM = (kWaves * VT_BYTES > MERGE_BYTES) ? kWaves * VT_BYTES : MERGE_BYTES;
-  static_assert(UPL >= 1 && NP % 8 == 0, "head_dim too small for the V staging layout");
+  static constexpr int ROW = D * ES;            // bytes per K or V row
+  static constexpr int CH = ROW / 64;           // K: 16-byte loads per lane per chunk
+  static constexpr int VB = ROW / 16;           // V: bytes per lane per row (D/16 elements)
+  static constexpr int VW = VB / 4;             // V: dwords per lane per row
+  static constexpr int DT = D / 16;             // output d tiles
+  static constexpr int MO_STRIDE = D + 4;       // floats per (wave, head) row of the merge area
+  static_assert(CH >= 1 && VW >= 2, "unsupported head_dim");
 };
 
-// Position of tile row r (0..31) inside a transposed V d-row.  Rows are
-// permuted so that the 8 rows a lane needs for one PV operand, rows
-// {4g..4g+3, 16+4g..16+4g+3}, sit contiguously at 8g .. 8g+7.
-__device__ __forceinline__ int vt_pos_of_quad(int quad) { return 8 * (quad & 3) + 4 * (quad >> 2); }
+// One chunk in flight: K as the A operand of logits^T, V as the A operand of
+// O^T, and which of the lane's four V rows (4g + i) carry a row.
+template <typename T, int D>
+struct Chunk {
+  using G = AttnGeo<T, D>;
+  u32x4_t kf[G::CH];
+  uint32_t vr[4][G::VW];
+  uint32_t valid;  // bit i: row 4g + i exists
+};
 
-// Byte address of position `pos` of d-row `d` in a wave's transposed V tile.
-// The 16-byte chunk index is XOR-swizzled by d / 8, so the staging writes of
-// lanes that differ in d by multiples of 8 fall in different banks; a lane's
-// operand read stays one contiguous 16-byte chunk.
-template <int RS, int NCH, int ES>
-__device__ __forceinline__ int vt_off(int d, int pos) {
-  const int byte = pos * ES;
-  return d * RS + (((byte >> 4) ^ ((d >> 3) & (NCH - 1))) << 4) + (byte & 15);
+__device__ __forceinline__ uint32_t row_offset_from(uint32_t rowoff, int src_lane) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)rowoff);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_chunk(Chunk<T, D>& ch, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                           uint32_t rowoff, int c, int n16, int g) {
+  using G = AttnGeo<T, D>;
+  const uint32_t ko = row_offset_from(rowoff, kChunk * c + n16);
+#pragma unroll
+  for (int cc = 0; cc < G::CH; ++cc)
+    ch.kf[cc] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(ko + 64 * cc + 16 * g), 0, 0);
+  ch.valid = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t vo = row_offset_from(rowoff, kChunk * c + 4 * g + i);
+    ch.valid |= (vo < kOutOfRange ? 1u : 0u) << i;
+    const int off = (int)(vo + G::VB * n16);
+    if constexpr (G::VW == 2) {
+      const u32x2_t x = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, 0);
+      ch.vr[i][0] = x[0];
+      ch.vr[i][1] = x[1];
+    } else {
+#pragma unroll
+      for (int w4 = 0; w4 < G::VW / 4; ++w4) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16 * w4, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ch.vr[i][4 * w4 + e] = x[e];
+      }
+    }
+  }
+}
+
+// One chunk of the online softmax: logits, rescale of the running state and
+// O^T += V^T P^T.
+template <typename T, int D>
+__device__ __forceinline__ void compute_chunk(const Chunk<T, D>& ch, const u32x4_t (&qf)[AttnGeo<T, D>::CH],
+                                              f32x4_t (&acc)[AttnGeo<T, D>::DT], float& m_run, float& l_run,
+                                              float scale_log2) {
+  using G = AttnGeo<T, D>;
+  f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int cc = 0; cc < G::CH; ++cc) sc = mma_chunk<T>(ch.kf[cc], qf[cc], sc);
+  float lg[4];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lg[i] = (ch.valid >> i) & 1u ? sc[i] * scale_log2 : -INFINITY;
+    cmax = fmaxf(cmax, lg[i]);
+  }
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+  const float m_new = fmaxf(m_run, cmax);
+  if (m_new == -INFINITY) return;  // wave-uniform: no row seen yet
+  const float alpha = exp2f(m_run - m_new);  // 0 while nothing was seen
+  float pr[4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pr[i] = lg[i] == -INFINITY ? 0.0f : exp2f(lg[i] - m_new);
+    psum += pr[i];
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int t = 0; t < G::DT; ++t) acc[t] *= alpha;
+  if constexpr (G::ES == 2) {
+    const u32x2_t pw = {float_to_bf16_bits(pr[0]) | (float_to_bf16_bits(pr[1]) << 16),
+                        float_to_bf16_bits(pr[2]) | (float_to_bf16_bits(pr[3]) << 16)};
+    const bf16x4_t pb = __builtin_bit_cast(bf16x4_t, pw);
+#pragma unroll
+    for (int t = 0; t < G::DT; ++t) {
+      const int w = t >> 1;
+      // element t of rows 4g..4g+3: low or high half of dword w
+      const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2_t av = {__builtin_amdgcn_perm(ch.vr[1][w], ch.vr[0][w], sel),
+                          __builtin_amdgcn_perm(ch.vr[3][w], ch.vr[2][w], sel)};
+      acc[t] = mfma_bf16_k16(__builtin_bit_cast(bf16x4_t, av), pb, acc[t]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < G::DT; ++t) acc[t] = mfma_f32(u32_as_float(ch.vr[i][t]), pr[i], acc[t]);
+  }
 }
 
 // Split partials of one stream, merged in ascending split order.  Loads of
@@ -155,12 +239,15 @@ __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int p, i
 
 constexpr int kFinishThreads = 256;
 
-template <typename T, int D, int TPW>
-__global__ __launch_bounds__(kWaves * 64, 4) void attn_split_kernel(AttnArgs a) {
-  using L = AttnLayout<T, D>;
-  __shared__ __attribute__((aligned(16))) char smem[L::SMEM];
-  __shared__ float wml[kWaves][16][2];   // per-wave (max, sum) per head
-  __shared__ float wfac[kWaves][16];     // per-wave rescale factor per head
+template <typename T, int D, int CPW>
+__global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) {
+  using G = AttnGeo<T, D>;
+  constexpr int RPW = kChunk * CPW;  // rows per wave
+  constexpr int RPS = kWaves * RPW;  // rows per split
+  static_assert(RPW <= 64, "one row number per lane");
+  __shared__ __attribute__((aligned(16))) float mo[kWaves * 16 * G::MO_STRIDE];  // [wave][head][d]
+  __shared__ float wml[kWaves][16][2];  // per-wave (max, sum) per head
+  __shared__ float wfac[kWaves][16];    // per-wave rescale factor per head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, g = lane >> 4;
@@ -174,244 +261,113 @@ __global__ __launch_bounds__(kWaves * 64, 4) void attn_split_kernel(AttnArgs a) 
   const int split = (logical / S) % NS;
   const int b = logical / (S * NS);
   const int tok = b * S + s;
-  const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
-  constexpr int RPS = kWaves * kTileRows * TPW;
-
   const bool win = split < NSW;
-  int e_begin, e_end, first_pos = 0;
-  if (win) {
-    const int nrows = min(a.win, p + 1);
-    first_pos = p - nrows + 1;
-    e_begin = split * RPS;
-    e_end = min(nrows, e_begin + RPS);
-  } else {
-    e_begin = (split - NSW) * RPS;
-    e_end = min(a.topk, e_begin + RPS);
-  }
   float* ml_out = a.ws_ml + ((size_t)tok * NS + split) * H * 2;
   float* o_out = a.ws_o + ((size_t)tok * NS + split) * H * D;
 
-  if (e_begin < e_end) {  // block-uniform: this split has rows
-    const char* kbase = static_cast<const char*>(win ? a.k_win : a.k_cmp);
-    const char* vbase = static_cast<const char*>(win ? a.v_win : a.v_cmp);
-    const int32_t* list = a.topk_idx + (size_t)tok * a.topk;
-    const size_t rbase = win ? (size_t)b * a.w_cap : (size_t)b * a.n_cap;
-    const size_t row_bytes = (size_t)D * L::ES;
-    // Row of list entry e: its byte offset and whether it carries a row.
-    auto lookup = [&](int e, bool& valid) -> size_t {
-      if (e >= e_end) {
-        valid = false;
-        return rbase * row_bytes;
-      }
-      if (win) {
-        valid = true;
-        return (rbase + (size_t)((first_pos + e) % a.w_cap)) * row_bytes;
-      }
-      const int j = list[e];
-      valid = (j >= 0) & (j < a.n_cap);
-      return (rbase + (size_t)(valid ? j : 0)) * row_bytes;
-    };
-
-    // B operand of logits^T: q^T, column = head n16 (zero for padded heads).
-    u32x4_t qf[L::CH];
-    {
-      const char* qp = static_cast<const char*>(a.q) + ((size_t)tok * H + min(n16, H - 1)) * row_bytes + g * 16;
+  // B operand of logits^T: q^T, column = head n16 (zero for padded heads);
+  // issued first, it does not depend on the position.
+  u32x4_t qf[G::CH];
+  {
+    const char* qp = static_cast<const char*>(a.q) + ((size_t)tok * H + min(n16, H - 1)) * G::ROW + g * 16;
 #pragma unroll
-      for (int c = 0; c < L::CH; ++c) {
-        const u32x4_t v = ld16(qp + c * 64);
-        qf[c] = n16 < H ? v : u32x4_t{0, 0, 0, 0};
-      }
+    for (int c = 0; c < G::CH; ++c) {
+      const u32x4_t v = ld16(qp + c * 64);
+      qf[c] = n16 < H ? v : u32x4_t{0, 0, 0, 0};
     }
+  }
 
-    f32x4_t acc[L::DT];
-#pragma unroll
-    for (int dt = 0; dt < L::DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-    char* vt = smem + wave * L::VT_BYTES;
+  // This wave's entries [e_lo, e_hi) of the stream, and the byte offset of the
+  // row behind entry e_lo + lane (kOutOfRange for padding or past the end).
+  int e_lo, e_hi;
+  uint32_t rowoff;
+  if (win) {
+    const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
+    const int nrows = min(a.win, p + 1);
+    const int first_pos = p - nrows + 1;
+    e_lo = split * RPS + wave * RPW;
+    e_hi = min(nrows, e_lo + RPW);
+    const int e = e_lo + lane;
+    rowoff = (lane < RPW && e < e_hi) ? (uint32_t)((first_pos + e) % a.w_cap) * G::ROW : kOutOfRange;
+  } else {
+    e_lo = (split - NSW) * RPS + wave * RPW;
+    e_hi = min(a.topk, e_lo + RPW);
+    const int e = e_lo + lane;
+    const int j = (lane < RPW && e < e_hi) ? a.topk_idx[(size_t)tok * a.topk + e] : -1;
+    rowoff = (j >= 0 && j < a.n_cap) ? (uint32_t)j * G::ROW : kOutOfRange;
+  }
+  const int nrows_wave = e_hi - e_lo;  // may be <= 0
 
-    // Tiles run one after the other: a scheduling barrier at the end of each
-    // tile keeps the next tile's loads out of the current tile's registers,
-    // which holds occupancy at 4 workgroups per CU, so every split of a large
-    // batch can be resident at once.
-#pragma unroll
-    for (int it = 0; it < TPW; ++it) {
-      const int e0 = e_begin + (it * kWaves + wave) * kTileRows;
-      if (e0 >= e_end) break;  // wave-uniform
+  const size_t rows_req = win ? (size_t)a.w_cap : (size_t)a.n_cap;
+  const char* kreq = static_cast<const char*>(win ? a.k_win : a.k_cmp) + (size_t)b * rows_req * G::ROW;
+  const char* vreq = static_cast<const char*>(win ? a.v_win : a.v_cmp) + (size_t)b * rows_req * G::ROW;
+  const int range = (int)(rows_req * G::ROW);  // the host keeps this below 2^31
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kreq, range);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vreq, range);
 
-      // K rows e0 + 16t + n16 as the A operand (16 bytes of each 64-byte chunk)
-      u32x4_t kf[2][L::CH];
-      bool kval[2];
+  f32x4_t acc[G::DT];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const char* rp = kbase + lookup(e0 + 16 * t + n16, kval[t]) + g * 16;
+  for (int t = 0; t < G::DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  // Chunks, one ahead: chunk c + 1 is in flight while chunk c is computed.
+  // The loads are issued unconditionally (rows past the end cost no memory
+  // traffic), so the compiler can count them exactly and wait for chunk c
+  // alone; a load under a runtime branch would make it wait for everything.
+  // A scheduling barrier after each chunk keeps later loads from being
+  // hoisted above it, which would only raise register pressure.
+  Chunk<T, D> buf[2];
+  load_chunk<T, D>(buf[0], krs, vrs, rowoff, 0, n16, g);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < L::CH; ++c) kf[t][c] = ld16(rp + c * 64);
+  for (int c = 0; c < CPW; ++c) {
+    if (c + 1 < CPW) load_chunk<T, D>(buf[(c + 1) & 1], krs, vrs, rowoff, c + 1, n16, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kChunk * c < nrows_wave)  // wave-uniform
+      compute_chunk<T, D>(buf[c & 1], qf, acc, m_run, l_run, a.scale_log2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // per-head sum over the 4 lanes that share a head column
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+
+  // ---- the 4 waves' partials, merged in fixed wave order.  Lane (n16, g)
+  // holds O[head n16][d] for d = g*D/4 + (D/16)*i + t in acc[t][i].
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < G::DT; ++t)
+      mo[(wave * 16 + n16) * G::MO_STRIDE + g * (D / 4) + (D / 16) * i + t] = acc[t][i];
+  if (g == 0) {
+    wml[wave][n16][0] = m_run;
+    wml[wave][n16][1] = l_tot;
+  }
+  __syncthreads();
+  if (tid < kWaves * 16) {  // rescale factor of wave w for head h
+    const int w = tid >> 4, h = tid & 15;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, wml[v][h][0]);
+    wfac[w][h] = wml[w][h][1] > 0.0f ? exp2f(wml[w][h][0] - M) : 0.0f;
+    if (w == 0 && h < H) {
+      float Lsum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        const float f = wml[v][h][1] > 0.0f ? exp2f(wml[v][h][0] - M) : 0.0f;
+        Lsum += f * wml[v][h][1];
       }
-      // V: unit u = (quad q of 4 rows, 16-byte piece pc); masked rows read as zero
-      u32x4_t vpc[L::UPL][4];
-#pragma unroll
-      for (int k = 0; k < L::UPL; ++k) {
-        const int u = lane + kWave * k, q = u & 7, pc = u >> 3;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          bool v;
-          const size_t off = lookup(e0 + 4 * q + jj, v);
-          const u32x4_t x = ld16(vbase + off + pc * 16);
-          vpc[k][jj] = v ? x : u32x4_t{0, 0, 0, 0};
-        }
-      }
-
-      // logits^T tile: lane (head n16, g) holds rows 16t + 4g + i
-      f32x4_t sc[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < L::CH; ++c) sc[t] = mma_chunk<T>(kf[t][c], qf[c], sc[t]);
-      }
-
-      // stage V transposed: d-row d holds the 32 tile rows at permuted positions
-      wave_lds_fence();  // the previous tile's operand reads precede these writes
-#pragma unroll
-      for (int k = 0; k < L::UPL; ++k) {
-        const int u = lane + kWave * k, q = u & 7, pc = u >> 3;
-        const int pos = vt_pos_of_quad(q);
-#pragma unroll
-        for (int x = 0; x < L::EP; ++x) {
-          const int d = pc * L::EP + x;
-          char* dst = vt + vt_off<L::RS, L::NCH, L::ES>(d, pos);
-          if constexpr (L::ES == 2) {
-            const int w = x >> 1;
-            uint32_t lo, hi;
-            if (x & 1) {
-              lo = (vpc[k][0][w] >> 16) | (vpc[k][1][w] & 0xFFFF0000u);
-              hi = (vpc[k][2][w] >> 16) | (vpc[k][3][w] & 0xFFFF0000u);
-            } else {
-              lo = (vpc[k][0][w] & 0xFFFFu) | (vpc[k][1][w] << 16);
-              hi = (vpc[k][2][w] & 0xFFFFu) | (vpc[k][3][w] << 16);
-            }
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{lo, hi};
-          } else {
-            *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{vpc[k][0][x], vpc[k][1][x], vpc[k][2][x], vpc[k][3][x]};
-          }
-        }
-      }
-      wave_lds_fence();
-
-      // base-2 logits; rows past the stream or without a row are masked
-      const uint32_t vm0 = (uint32_t)__ballot(kval[0]) & 0xFFFFu;  // lanes 0..15: rows 0..15
-      const uint32_t vm1 = (uint32_t)__ballot(kval[1]) & 0xFFFFu;  // rows 16..31
-      float lg[2][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = ((t ? vm1 : vm0) >> (4 * g + i)) & 1u;
-          lg[t][i] = ok ? sc[t][i] * a.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, lg[t][i]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      if (m_new != -INFINITY) {  // wave-uniform: masks are per row
-        const float alpha = exp2f(m_run - m_new);  // 0 while nothing was seen
-        float pr[2][4];
-        float psum = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pr[t][i] = lg[t][i] == -INFINITY ? 0.0f : exp2f(lg[t][i] - m_new);
-            psum += pr[t][i];
-          }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < L::DT; ++dt) acc[dt] *= alpha;
-
-        // O^T += V^T P^T: A = V^T (row d, tile rows on k), B = P^T (column = head)
-        if constexpr (L::ES == 2) {
-          u32x4_t pw;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int t = w >> 1, i0 = 2 * (w & 1);
-            pw[w] = float_to_bf16_bits(pr[t][i0]) | (float_to_bf16_bits(pr[t][i0 + 1]) << 16);
-          }
-          const bf16x8_t pf = as_bf16x8(pw);
-#pragma unroll
-          for (int dt = 0; dt < L::DT; ++dt) {
-            const u32x4_t vf =
-                *reinterpret_cast<const u32x4_t*>(vt + vt_off<L::RS, L::NCH, L::ES>(16 * dt + n16, 8 * g));
-            acc[dt] = mfma_bf16(as_bf16x8(vf), pf, acc[dt]);
-          }
-        } else {
-#pragma unroll
-          for (int dt = 0; dt < L::DT; ++dt) {
-            const int d = 16 * dt + n16;
-            const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(vt + vt_off<L::RS, L::NCH, L::ES>(d, 8 * g));
-            const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(vt + vt_off<L::RS, L::NCH, L::ES>(d, 8 * g + 4));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              acc[dt] = mfma_f32(u32_as_float(v0[j]), pr[0][j], acc[dt]);
-              acc[dt] = mfma_f32(u32_as_float(v1[j]), pr[1][j], acc[dt]);
-            }
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      ml_out[2 * h] = M;
+      ml_out[2 * h + 1] = Lsum;
     }
-
-    // per-head sum over the 4 lanes that share a head column
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-
-    // ---- the 4 waves' partials, merged in fixed wave order
-    __syncthreads();  // every wave is done with its V tile; reuse LDS
-    float* mo = reinterpret_cast<float*>(smem);  // [wave][head][MO_STRIDE]
+  }
+  __syncthreads();
+  for (int item = tid; item < H * D; item += kWaves * 64) {
+    const int h = item / D, d = item - h * D;
+    float o = 0.0f;
 #pragma unroll
-    for (int dt = 0; dt < L::DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mo[(wave * 16 + n16) * L::MO_STRIDE + 16 * dt + 4 * g + i] = acc[dt][i];
-    if (g == 0) {
-      wml[wave][n16][0] = m_run;
-      wml[wave][n16][1] = l_tot;
-    }
-    __syncthreads();
-    if (tid < kWaves * 16) {  // rescale factor of wave w for head h
-      const int w = tid >> 4, h = tid & 15;
-      float M = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, wml[v][h][0]);
-      wfac[w][h] = wml[w][h][1] > 0.0f ? exp2f(wml[w][h][0] - M) : 0.0f;
-      if (w == 0 && h < H) {
-        float Lsum = 0.0f;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-          const float f = wml[v][h][1] > 0.0f ? exp2f(wml[v][h][0] - M) : 0.0f;
-          Lsum += f * wml[v][h][1];
-        }
-        ml_out[2 * h] = M;
-        ml_out[2 * h + 1] = Lsum;
-      }
-    }
-    __syncthreads();
-    for (int item = tid; item < H * D; item += kWaves * 64) {
-      const int h = item / D, d = item - h * D;
-      float part[kWaves], f[kWaves];
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        part[w] = mo[(w * 16 + h) * L::MO_STRIDE + d];
-        f[w] = wfac[w][h];
-      }
-      float o = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) o += f[w] * part[w];
-      o_out[(size_t)h * D + d] = o;
-    }
-  } else if (tid < H) {  // nothing in this split (short window)
-    ml_out[2 * tid] = -INFINITY;
-    ml_out[2 * tid + 1] = 0.0f;
+    for (int w = 0; w < kWaves; ++w) o += wfac[w][h] * mo[(w * 16 + h) * G::MO_STRIDE + d];
+    o_out[(size_t)h * D + d] = o;
   }
 }
 
@@ -432,9 +388,17 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   const int tokens = a.batch * a.q_per_req;
   const int NS = a.n_split_win + a.n_split_cmp;
   const dim3 grid(tokens * NS);
-  switch (a.tiles_per_wave) {
+  constexpr bool kWideRows = sizeof(T) == 4 && D == 128;  // one chunk per wave only
+  switch (a.chunks_per_wave) {
     case 1: hipLaunchKernelGGL((attn_split_kernel<T, D, 1>), grid, dim3(kWaves * 64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_split_kernel<T, D, 2>), grid, dim3(kWaves * 64), 0, st, a); break;
+    case 2:
+      if constexpr (kWideRows) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((attn_split_kernel<T, D, 2>), grid, dim3(kWaves * 64), 0, st, a);
+      break;
+    case 4:
+      if constexpr (kWideRows) return hipErrorInvalidValue;
+      else hipLaunchKernelGGL((attn_split_kernel<T, D, 4>), grid, dim3(kWaves * 64), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -446,21 +410,32 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk) {
+AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, int topk, int dtype) {
   AttnPlan pl{};
-  // Two tiles per wave (256 rows per split) once there are enough rows for
-  // every split workgroup to stay resident in one round; one tile (128 rows)
-  // below that, so small batches still spread over many CUs.
-#ifndef CSA_ATTN_TPW2_ROWS
-#define CSA_ATTN_TPW2_ROWS 65536
+  // The most rows per wave (4, 2 or 1 chunks of 16) that still gives at least
+  // CSA_ATTN_MIN_SPLITS workgroups, so that a small batch spreads over many
+  // CUs while a large one keeps its partials few.  fp32 rows of 128 dims take
+  // one chunk per wave: two in flight would not fit the register budget.
+#ifndef CSA_ATTN_MIN_SPLITS
+#define CSA_ATTN_MIN_SPLITS 512
 #endif
-  const long long rows = (long long)batch * q_per_req * (win + topk);
-  pl.tiles_per_wave = rows >= CSA_ATTN_TPW2_ROWS ? 2 : 1;
-  pl.rows_per_split = kWaves * kTileRows * pl.tiles_per_wave;
+  const long long tokens = (long long)batch * q_per_req;
+  const bool wide_rows = dtype != 1 && head_dim == 128;
+  int cpw = 1;
+  for (int c : {4, 2}) {
+    if (wide_rows) break;
+    const int rps = kWaves * kChunk * c;
+    const long long n = tokens * ((win + rps - 1) / rps + (topk + rps - 1) / rps);
+    if (n >= CSA_ATTN_MIN_SPLITS) {
+      cpw = c;
+      break;
+    }
+  }
+  pl.chunks_per_wave = cpw;
+  pl.rows_per_split = kWaves * kChunk * cpw;
   pl.n_split_win = (win + pl.rows_per_split - 1) / pl.rows_per_split;
   pl.n_split_cmp = (topk + pl.rows_per_split - 1) / pl.rows_per_split;
-  const size_t tokens = (size_t)batch * q_per_req;
-  const size_t parts = tokens * (pl.n_split_win + pl.n_split_cmp) * heads;
+  const size_t parts = (size_t)tokens * (pl.n_split_win + pl.n_split_cmp) * heads;
   pl.ws_o_floats = parts * head_dim;
   pl.ws_ml_floats = parts * 2;
   pl.ws_o_bytes = (pl.ws_o_floats * 4 + 255) / 256 * 256;
