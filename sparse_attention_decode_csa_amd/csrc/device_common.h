@@ -68,6 +68,9 @@ __device__ __forceinline__ f32x4_t mfma_bf16_k16(bf16x4_t a, bf16x4_t b, f32x4_t
 // byte range return zero and do not access memory.
 constexpr int kBufferConfig = 0x00020000;
 
+// Cache-policy operand of the LDS DMA builtin: non-temporal (streamed data).
+constexpr int kNonTemporal = 2;
+
 // Buffer resource over [base, base + bytes).  base and bytes must be the same
 // in every lane; they are moved to scalar registers explicitly, since a
 // resource the compiler cannot prove uniform turns each load into a loop.

@@ -9,9 +9,9 @@
 // Design: the step streams k_idx once per request (every token of a request
 // shares it), so it is HBM-bound; the contraction runs on MFMA with the
 // request's S*Hi query rows as the M dimension (zero-padded to 16) and 16 keys
-// as N.  Each lane loads 16 contiguous bytes of one key row per 64-byte chunk
-// straight into the MFMA B operand, so a wave reads whole 256-byte rows with
-// no LDS staging and no reuse to exploit.  The per-head relu and weighted sum
+// as N.  Key tiles stream HBM -> LDS by DMA in whole rows, several tiles in
+// flight per wave, and each lane reads its 16-byte MFMA operand pieces back
+// from LDS.  The per-head relu and weighted sum
 // runs in registers when the head count is 4, 8 or 16 (each lane's four
 // result rows are heads of one token), else through a small per-wave LDS
 // tile; either way in a fixed head order.
@@ -24,14 +24,39 @@ namespace {
 #ifndef CSA_SCORE_TILES_PER_WAVE
 #define CSA_SCORE_TILES_PER_WAVE 8
 #endif
-#ifndef CSA_SCORE_UNROLL
-#define CSA_SCORE_UNROLL 4
+#ifndef CSA_SCORE_TILE_BUFFERS
+#define CSA_SCORE_TILE_BUFFERS 4
 #endif
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTilesPerWave = CSA_SCORE_TILES_PER_WAVE;               // 16-key tiles
-constexpr int kScoreUnroll = CSA_SCORE_UNROLL;                             // tiles per load group
-constexpr int kScoreGroups = kScoreTilesPerWave / kScoreUnroll;
+constexpr int kScoreBufs = CSA_SCORE_TILE_BUFFERS;                         // tiles in flight per wave
 constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 512
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
+// Key rows travel HBM -> LDS by DMA (global_load_lds_dwordx4): one instruction
+// moves 1 KiB, i.e. whole rows, so every 128-byte line is consumed by a single
+// request and the non-temporal hint can keep the stream from displacing the
+// rest of the cache.  In LDS the 16-byte piece p of tile row r sits at slot
+// p ^ (r % pieces-per-row); the MFMA operand reads (16 rows, one piece each)
+// then spread over the banks.  The DMA fixes the LDS slot of each lane, so the
+// swizzle is applied on the global side: the lane that fills slot s fetches
+// piece s ^ (r % pieces-per-row).
+template <int ROW>
+struct ScoreTile {
+  static constexpr int NPR = ROW / 16;      // 16-byte pieces per row
+  static constexpr int RPI = 1024 / ROW;    // rows per DMA instruction
+  static constexpr int NPT = 16 * ROW / 1024;  // DMA instructions per 16-row tile
+  static constexpr int BYTES = 16 * ROW;
+  static_assert(NPR >= 4 && RPI >= 1 && NPT >= 1, "unsupported row size");
+};
 
 // HI > 0: the indexer head count, a power of two in 4 .. 16, so that the four
 // result rows a lane holds (4g .. 4g+3 of a 16-row tile) belong to one token
@@ -40,11 +65,14 @@ constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 51
 template <typename T, int DI, int MT, int HI>
 __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   constexpr int ES = sizeof(T);
-  constexpr int CH = DI * ES / 64;   // 64-byte chunks per row; a lane holds 16 B of each
-  static_assert(CH >= 1 && DI * ES % 64 == 0, "row must be a whole number of 64-byte chunks");
+  constexpr int ROW = DI * ES;
+  constexpr int CH = ROW / 64;       // 64-byte k-chunks per row; a lane holds 16 B of each
+  static_assert(CH >= 1 && ROW % 64 == 0, "row must be a whole number of 64-byte chunks");
+  using TL = ScoreTile<ROW>;
   constexpr int ROWS = MT * 16;      // padded query rows
   constexpr int RP = 17;             // padded LDS row length (floats)
 
+  __shared__ __attribute__((aligned(1024))) char tiles[kScoreWaves][kScoreBufs][TL::BYTES];
   __shared__ float red[HI ? 1 : kScoreWaves][HI ? 1 : ROWS][RP];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -67,11 +95,11 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   // padded rows load a real row and are zeroed, so the loads stay unconditional.
   u32x4_t qa[MT][CH];
   float wv[MT][4];
-  const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * DI * ES;
+  const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * ROW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int qr = mt * 16 + n16;
-    const char* qp = qbase + (size_t)min(qr, SH - 1) * DI * ES + g * 16;
+    const char* qp = qbase + (size_t)min(qr, SH - 1) * ROW + g * 16;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const u32x4_t v = ld16(qp + c * 64);
@@ -84,7 +112,6 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
       wv[mt][i] = row < SH ? wr : 0.0f;
     }
   }
-
   // Fast path: the token of tile mt's rows 4g..4g+3 and its visible count.
   int tok_of[MT], nv_of[MT];
 #pragma unroll
@@ -93,81 +120,98 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
     tok_of[mt] = s;
     nv_of[mt] = s < S ? min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap) : 0;
   }
-
-  const char* kbase = static_cast<const char*>(a.k_idx) + (size_t)b * a.n_cap * DI * ES;
-  float* srow = a.scores + (size_t)b * S * a.n_cap;
-
+  const char* kbase = static_cast<const char*>(a.k_idx) + (size_t)b * a.n_cap * ROW;
   // Tiles are interleaved over the 4 waves so that at each step the block
-  // reads 4 consecutive 16-row tiles (16 KiB contiguous for Di = 128 bf16).
+  // reads 4 consecutive 16-row tiles.
   auto tile_key0 = [&](int t) { return key0 + (t * kScoreWaves + wave) * 16; };
-  auto load_group = [&](int grp, u32x4_t (&dst)[kScoreUnroll][CH]) {
+  auto issue_tile = [&](int t) {
+    const int k0 = tile_key0(t);
+    char* dst = tiles[wave][t % kScoreBufs];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int j = min(tile_key0(grp * kScoreUnroll + u) + n16, nmax - 1);  // clamp: a real row
-      const char* rp = kbase + (size_t)j * DI * ES + g * 16;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-#if CSA_SCORE_STREAMING_LOADS
-        dst[u][c] = ld16_stream(rp + c * 64);
-#else
-        dst[u][c] = ld16(rp + c * 64);  // plain loads measured faster than the non-temporal hint
-#endif
-      }
+    for (int k = 0; k < TL::NPT; ++k) {
+      const int r = k * TL::RPI + lane / TL::NPR;            // tile row this lane fetches
+      const int piece = (lane % TL::NPR) ^ (r % TL::NPR);
+      const int j = min(k0 + r, nmax - 1);                   // clamp: a real row
+      __builtin_amdgcn_global_load_lds(kbase + (size_t)j * ROW + 16 * piece,
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0,
+                                       kNonTemporal);
     }
   };
+  // the query loads above are older than every tile DMA, so waiting for them
+  // does not wait for the tiles
+#pragma unroll
+  for (int t = 0; t < kScoreBufs && t < kScoreTilesPerWave; ++t) issue_tile(t);
 
-  u32x4_t kb[2][kScoreUnroll][CH];
-  load_group(0, kb[0]);
+  float* srow = a.scores + (size_t)b * S * a.n_cap;
+
 #pragma unroll
-  for (int grp = 0; grp < kScoreGroups; ++grp) {
-    if (grp + 1 < kScoreGroups) load_group(grp + 1, kb[(grp + 1) & 1]);  // prefetch
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    // Tile t has landed once at most the DMA instructions of the younger tiles
+    // in flight are outstanding (other memory operations only make this wait
+    // longer, never shorter).
+    constexpr int kAhead = kScoreBufs - 1;
+    const int younger = (t + kAhead < kScoreTilesPerWave ? kAhead : kScoreTilesPerWave - 1 - t);
+    switch (younger) {  // t is a compile-time constant after unrolling
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1 * TL::NPT>(); break;
+      case 2: wait_vmcnt<2 * TL::NPT>(); break;
+      default: wait_vmcnt<3 * TL::NPT>(); break;
+    }
+    const char* src = tiles[wave][t % kScoreBufs];
+    u32x4_t kb[CH];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; ++u) {
-      const int tkey0 = tile_key0(grp * kScoreUnroll + u);
-      f32x4_t acc[MT];
+    for (int c = 0; c < CH; ++c) {
+      const int slot = (4 * c + g) ^ (n16 % TL::NPR);
+      kb[c] = *reinterpret_cast<const u32x4_t*>(src + n16 * ROW + 16 * slot);
+    }
+    if (t + kScoreBufs < kScoreTilesPerWave) {
+      wait_lgkmcnt0();  // the operand reads of this buffer are done: refill it
+      issue_tile(t + kScoreBufs);
+    }
+    const int tkey0 = tile_key0(t);
+    f32x4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < CH; ++c) acc[mt] = mma_chunk<T>(qa[mt][c], kb[c], acc[mt]);
+    }
+    // lane holds dot(query row mt*16+4g+i, key tkey0+n16)
+    if constexpr (HI > 0) {
+      // heads in ascending order: the lane's four, then pairs of lanes
+      const int j = tkey0 + n16;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float sum = 0.0f;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) acc[mt] = mma_chunk<T>(qa[mt][c], kb[grp & 1][u][c], acc[mt]);
-      }
-      // lane holds dot(query row mt*16+4g+i, key tkey0+n16)
-      if constexpr (HI > 0) {
-        // heads in ascending order: the lane's four, then pairs of lanes
-        const int j = tkey0 + n16;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          float sum = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float d = acc[mt][i];
-            sum += wv[mt][i] * (d > 0.0f ? d : 0.0f);
-          }
-          if constexpr (HI >= 8) sum += __shfl_xor(sum, 16);
-          if constexpr (HI >= 16) sum += __shfl_xor(sum, 32);
-          const bool writer = (g & (HI / 4 - 1)) == 0;
-          if (writer && tok_of[mt] < S && nv_of[mt] > a.topk && j < nv_of[mt])
-            srow[(size_t)tok_of[mt] * a.n_cap + j] = sum;
+        for (int i = 0; i < 4; ++i) {
+          const float d = acc[mt][i];
+          sum += wv[mt][i] * (d > 0.0f ? d : 0.0f);
         }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float d = acc[mt][i];
-            red[wave][mt * 16 + 4 * g + i][n16] = wv[mt][i] * (d > 0.0f ? d : 0.0f);
-          }
-        wave_lds_fence();
-        for (int e = lane; e < S * 16; e += kWave) {
-          const int s = e >> 4, n = e & 15;
-          const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
-          float sum = 0.0f;
-          for (int h = 0; h < Hi; ++h) sum += red[wave][s * Hi + h][n];
-          const int j = tkey0 + n;
-          if (nv > a.topk && j < nv) srow[(size_t)s * a.n_cap + j] = sum;
-        }
-        wave_lds_fence();
+        if constexpr (HI >= 8) sum += __shfl_xor(sum, 16);
+        if constexpr (HI >= 16) sum += __shfl_xor(sum, 32);
+        const bool writer = (g & (HI / 4 - 1)) == 0;
+        if (writer && tok_of[mt] < S && nv_of[mt] > a.topk && j < nv_of[mt])
+          srow[(size_t)tok_of[mt] * a.n_cap + j] = sum;
       }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float d = acc[mt][i];
+          red[wave][mt * 16 + 4 * g + i][n16] = wv[mt][i] * (d > 0.0f ? d : 0.0f);
+        }
+      wave_lds_fence();
+      for (int e = lane; e < S * 16; e += kWave) {
+        const int s = e >> 4, n = e & 15;
+        const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
+        float sum = 0.0f;
+        for (int h = 0; h < Hi; ++h) sum += red[wave][s * Hi + h][n];
+        const int j = tkey0 + n;
+        if (nv > a.topk && j < nv) srow[(size_t)s * a.n_cap + j] = sum;
+      }
+      wave_lds_fence();
     }
   }
 }
