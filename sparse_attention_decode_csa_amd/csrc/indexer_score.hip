@@ -22,7 +22,7 @@ namespace csa {
 namespace {
 
 #ifndef CSA_SCORE_TILES_PER_WAVE
-#define CSA_SCORE_TILES_PER_WAVE 8
+#define CSA_SCORE_TILES_PER_WAVE 16
 #endif
 #ifndef CSA_SCORE_TILE_BUFFERS
 #define CSA_SCORE_TILE_BUFFERS 4
@@ -30,7 +30,7 @@ namespace {
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTilesPerWave = CSA_SCORE_TILES_PER_WAVE;               // 16-key tiles
 constexpr int kScoreBufs = CSA_SCORE_TILE_BUFFERS;                         // tiles in flight per wave
-constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 512
+constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 1024
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
