@@ -204,6 +204,46 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total)
   return before + inc - v;
 }
 
+// Maximum over the 64 lanes of a wave with DPP moves (row_shr within each
+// 16-lane row, then readlane of the four row maxima).
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// block_exclusive_scan that also reduces a maximum over the block through
+// the same barriers.  `red` holds two ints per wave.
+__device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int* red, int& total,
+                                                        uint32_t& block_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  const uint32_t wm = wave_max(mx);
+  if (lane == kWave - 1) {
+    red[2 * wave] = inc;
+    red[2 * wave + 1] = (int)wm;
+  }
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  block_max = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int t = red[2 * w];
+    before += w < wave ? t : 0;
+    total += t;
+    block_max = max(block_max, (uint32_t)red[2 * w + 1]);
+  }
+  __syncthreads();
+  return before + inc - v;
+}
+
 // Histograms of the block-wide selections, double buffered by pass parity so
 // that zeroing the next pass's histogram needs no barrier of its own.
 constexpr int kHistStride = 257;   // per-wave copies sit off the bank period
@@ -397,53 +437,53 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     for (int j = 0; j < KPT; ++j) key[j] = order_key(row[min(i0 + j, n - 1)]);
   }
   auto valid = [&](int j) { return i0 + j < n; };
-  uint32_t kmin = key[0], kmax = key[0];
+  uint32_t kmax = key[0];  // slots past n copy a valid key, so they never raise it
 #pragma unroll
-  for (int j = 1; j < KPT; ++j) {
-    kmin = min(kmin, key[j]);
-    kmax = max(kmax, key[j]);
-  }
-  uint32_t row_min, row_max;
-  block_min_max(kmin, kmax, sm.red, row_min, row_max);
+  for (int j = 1; j < KPT; ++j) kmax = max(kmax, key[j]);
 
   if (n > kCandCap) {
-    // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT.
-    // Two 8-bit passes are enough: the threshold is the lower edge of the
-    // 16-bit bin holding the sample rank, which only keeps a few more rows.
+    // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT,
+    // which exists for the first m threads (closed form, no scan).
+    // Two 8-bit passes over the full key range fix the top 16 key bits: the
+    // threshold is the lower edge of the 16-bit bin holding the sample rank,
+    // which only keeps a few more rows.
     const int js = tid % KPT;
     uint32_t sk = 0u;  // key[js] without a dynamic register index
 #pragma unroll
     for (int j = 0; j < KPT; ++j) sk = j == js ? key[j] : sk;
     const bool sval = valid(js);
-    int m;
-    (void)block_exclusive_scan(sval ? 1 : 0, sm.red, m);
+    const int q = n / KPT, rr = n % KPT;
+    const int m = min(q, kTopkThreads) + ((q < kTopkThreads && q % KPT < rr) ? 1 : 0);
     // sample rank expected at row rank K, plus three standard deviations, so
     // that the threshold keeps at least K rows
     const int ks0 = (int)(((long long)K * m + n - 1) / n);
     const int ks = min(m, ks0 + 3 * (int)sqrtf((float)ks0) + 4);
     uint32_t tau;
     int unused;
-    block_radix_select<false, 1>([&](int) { return sk; }, [&](int) { return sval; }, ks, row_min,
-                                 row_max, sm, tau, unused, 2);
-    // ---- rows at or above the threshold, compacted in row order
+    block_radix_select<false, 1>([&](int) { return sk; }, [&](int) { return sval; }, ks, 0u,
+                                 0xFFFFFFFFu, sm, tau, unused, 2);
+    // ---- rows at or above the threshold, compacted in row order; the same
+    // barriers give the row maximum
     int mine = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) mine += (valid(j) && key[j] >= tau) ? 1 : 0;
     int c;
-    int pos = block_exclusive_scan(mine, sm.red, c);
+    uint32_t row_max;
+    int pos = block_exclusive_scan_max(mine, kmax, sm.red, c, row_max);
     if (c >= K && c <= kCandCap) {  // block-uniform
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if (valid(j) && key[j] >= tau && pos < kCandCap) {
+        if (valid(j) && key[j] >= tau) {
           cand_key[pos] = key[j];
           cand_idx[pos] = (uint32_t)(i0 + j);
           ++pos;
         }
       __syncthreads();
-      // every candidate lies in [tau, row max]
+      // every candidate lies in [tau, row max]; few keys per thread, so one
+      // shared histogram
       uint32_t T;
       int keq;
-      block_radix_select<true, kCandPerThread>(
+      block_radix_select<false, kCandPerThread>(
           [&](int r) { return cand_key[min(r * kTopkThreads + tid, c - 1)]; },
           [&](int r) { return r * kTopkThreads + tid < c; }, K, tau, row_max, sm, T, keq);
       // emission over the candidates only: thread t takes a contiguous run
@@ -456,6 +496,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     }
   }
   // ---- whole-row selection and emission
+  uint32_t kmin = key[0];
+#pragma unroll
+  for (int j = 1; j < KPT; ++j) kmin = min(kmin, key[j]);
+  uint32_t row_min, row_max;
+  block_min_max(kmin, kmax, sm.red, row_min, row_max);
   uint32_t T;
   int keq;
   block_radix_select<true, KPT>([&](int j) { return key[j]; }, valid, K, row_min, row_max, sm, T,
