@@ -138,12 +138,15 @@ def test_topk_exact_on_oracle_scores(cid, config_inputs):
 @pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero", "spiked16", "spiked32"])
 @pytest.mark.parametrize("n_cap,topk", [(300, 64), (4096, 256), (4096, 257), (9000, 1024),
                                         (16384, 512), (32768, 1024), (32768, 4096), (40000, 2048),
-                                        (1000, 999), (20000, 4000)])
+                                        (1000, 999), (20000, 4000), (4100, 1024), (12292, 2048)])
 def test_topk_exact_synthetic(kind, n_cap, topk):
     # "spiked" rows put their largest values exactly where the selection's
     # strided sample looks, so the sampled threshold keeps too few rows and
     # the full-row selection must take over; "coarse" rows tie heavily.
-    # rows of several visible lengths, including n_vis == K and K + 1
+    # rows of several visible lengths, including n_vis == K and K + 1.
+    # 4100 and 12292 are multiples of 4 but not of the per-thread slice length
+    # (8 and 16), so a thread's slice would straddle n_cap: the selection must
+    # take its per-element load path there.
     B, S = 3, 2
     sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=16, heads=1,
                  head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1,
