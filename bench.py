@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--query-sets", type=int, default=4,
+                    help="query sets cycled over the steps (queries rolled along the batch), so "
+                         "consecutive steps select different compressed rows")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -147,7 +150,19 @@ def main():
     print(f"# config {args.config} ({cfg.name}) inputs drawn in {t_gen:.1f}s, uploaded", file=sys.stderr,
           flush=True)
 
-    def run_step(ev=None):
+    # query sets: q, q_idx and w rolled along the batch, so each request meets
+    # other queries and selects other rows; caches, positions and the window
+    # stay the same, as in consecutive decode steps
+    R = max(1, args.query_sets)
+    qsets = []
+    for r in range(R):
+        qs = dict(dev)
+        for name in ("q", "q_idx", "w"):
+            qs[name] = torch.roll(dev[name], shifts=r, dims=0).contiguous()
+        qsets.append(qs)
+
+    def run_step(ev=None, r=0):
+        dev = qsets[r % R]
         if not cfg.supplied_topk:
             if ev: ev[0].record(stream)
             C.indexer_score(sh, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
@@ -164,8 +179,8 @@ def main():
                              bufs["out"], bufs["attn_ws"], stream)
         if ev: ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        run_step()
+    for k in range(args.warmup):
+        run_step(r=k)
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, events per stage on the launch stream
@@ -173,7 +188,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        run_step(evs[k])
+        run_step(evs[k], r=k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1000.0 / args.steps
@@ -183,10 +198,18 @@ def main():
     t_event_step = float(np.mean([e[0].elapsed_time(e[3]) for e in evs])) * 1e-3
 
     sp = inp["start_pos"]
-    ti = (bufs["topk_idx"] if not cfg.supplied_topk else dev["topk_idx"]).cpu().numpy()
     sb, sf = score_bytes(sh, sp), score_flops(sh, sp)
     tb = topk_bytes(sh, sp)
-    ab, rows_att = attn_bytes(sh, sp, ti)
+    # attention bytes depend on the selection: mean over the query sets
+    abs_, rows_ = [], []
+    for r in range(R):
+        run_step(r=r)
+        torch.cuda.synchronize()
+        ti = (bufs["topk_idx"] if not cfg.supplied_topk else dev["topk_idx"]).cpu().numpy()
+        a_, r_ = attn_bytes(sh, sp, ti)
+        abs_.append(a_)
+        rows_.append(r_)
+    ab, rows_att = float(np.mean(abs_)), int(np.mean(rows_))
     T = sh.batch * sh.q_per_req
 
     def stage(bytes_, t):
@@ -250,7 +273,7 @@ def main():
                                f"WIN={sh.win} H={sh.heads} D={sh.head_dim} Dr={sh.rope_dim} "
                                f"Hi={sh.idx_heads} Di={sh.idx_dim} G={sh.out_groups}",
                    "batch": sh.batch, "q_per_req": sh.q_per_req, "topk": sh.topk,
-                   "max_len": sh.max_len, "parallelism": "single GPU"},
+                   "max_len": sh.max_len, "query_sets": R, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
