@@ -159,41 +159,49 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D>& ch, const u32x4
   }
 }
 
-// Split partials of one stream, merged in ascending split order.  Loads of
-// up to kMergeBatch splits are issued before any of them is used.
+// Split partials of a token, merged in ascending split order into the state
+// of their stream (window splits first, then compressed).  Loads of up to
+// kMergeBatch splits are issued before any of them is used, so a token with
+// at most that many splits costs one round trip.
 constexpr int kMergeBatch = 8;
 
 struct StreamState {
   float m, l, o0, o1;
 };
 
-__device__ __forceinline__ StreamState merge_splits(const AttnArgs& a, int tok, int NS, int h, int d,
-                                                    int D, int lo, int hi) {
-  StreamState st{-INFINITY, 0.0f, 0.0f, 0.0f};
-  for (int b0 = lo; b0 < hi; b0 += kMergeBatch) {
+__device__ __forceinline__ void merge_into(StreamState& st, float m, float l, float2 o) {
+  if (!(l > 0.0f)) return;  // empty split: its partial sum was never written
+  const float mn = fmaxf(st.m, m);
+  const float fo = exp2f(st.m - mn), fn = exp2f(m - mn);
+  st.l = st.l * fo + l * fn;
+  st.o0 = st.o0 * fo + o.x * fn;
+  st.o1 = st.o1 * fo + o.y * fn;
+  st.m = mn;
+}
+
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int tok, int h, int d, int D, StreamState& w,
+                                             StreamState& c) {
+  const int NSW = a.n_split_win, NS = a.n_split_win + a.n_split_cmp;
+  w = StreamState{-INFINITY, 0.0f, 0.0f, 0.0f};
+  c = w;
+  for (int b0 = 0; b0 < NS; b0 += kMergeBatch) {
     float m[kMergeBatch], l[kMergeBatch];
     float2 ov[kMergeBatch];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      const int sp = min(b0 + k, hi - 1);
+      const int sp = min(b0 + k, NS - 1);
       const size_t r = ((size_t)tok * NS + sp) * a.heads + h;
       const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * r);
       m[k] = ml.x;
-      l[k] = b0 + k < hi ? ml.y : 0.0f;
+      l[k] = b0 + k < NS ? ml.y : 0.0f;
       ov[k] = *reinterpret_cast<const float2*>(a.ws_o + r * D + d);
     }
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
-      if (!(l[k] > 0.0f)) continue;  // empty split: its partial sum was never written
-      const float mn = fmaxf(st.m, m[k]);
-      const float fo = exp2f(st.m - mn), fn = exp2f(m[k] - mn);
-      st.l = st.l * fo + l[k] * fn;
-      st.o0 = st.o0 * fo + ov[k].x * fn;
-      st.o1 = st.o1 * fo + ov[k].y * fn;
-      st.m = mn;
+      if (b0 + k < NSW) merge_into(w, m[k], l[k], ov[k]);
+      else merge_into(c, m[k], l[k], ov[k]);
     }
   }
-  return st;
 }
 
 // Final output of one (token, head, dim pair) from all of the token's split
@@ -202,7 +210,6 @@ __device__ __forceinline__ StreamState merge_splits(const AttnArgs& a, int tok, 
 template <typename T, int D>
 __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int p, int item) {
   const int H = a.heads, G = a.out_groups, Hg = H / G;
-  const int NSW = a.n_split_win, NS = a.n_split_win + a.n_split_cmp;
   const int T_ = a.batch * a.q_per_req;
   const int r0 = D - a.rope_dim;
   const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
@@ -212,8 +219,8 @@ __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int p, i
     cs = a.rope_cos[(size_t)p * (a.rope_dim >> 1) + i];
     sn = a.rope_sin[(size_t)p * (a.rope_dim >> 1) + i];
   }
-  const StreamState w = merge_splits(a, tok, NS, h, d, D, 0, NSW);
-  const StreamState c = merge_splits(a, tok, NS, h, d, D, NSW, NS);
+  StreamState w, c;
+  merge_splits(a, tok, h, d, D, w, c);
   // stream merge: an empty stream (sum 0) carries no weight
   const float M = fmaxf(w.m, c.m);
   const float fw = w.l > 0.0f ? exp2f(w.m - M) : 0.0f;
