@@ -247,7 +247,7 @@ __device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int*
 // Histograms of the block-wide selections, double buffered by pass parity so
 // that zeroing the next pass's histogram needs no barrier of its own.
 constexpr int kHistStride = 257;   // per-wave copies sit off the bank period
-struct SelectSmem {
+struct alignas(16) SelectSmem {  // 16-byte aligned: the bin scan reads uint4
   uint32_t hist[2][kTopkWaves * kHistStride];
   uint32_t cnt[2][256];
   int res[2][2];   // per pass parity: (bin, keys above the bin)
@@ -289,12 +289,14 @@ __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red
 // PER_WAVE selects one histogram per wave (many keys) or one shared
 // histogram (few keys).  With max_passes < 4 the select stops early and T is
 // the lower edge of the bin holding the k-th key (at least k keys are >= T).
-// No floating point anywhere.
+// (12-bit digits were measured too: the single-wave scan of 4096 bins cost
+// more than the pass they save.)  No floating point anywhere.
 template <bool PER_WAVE, int NK, typename Key, typename Valid>
 __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uint32_t hi,
                                    SelectSmem& sm, uint32_t& T, int& keq, int max_passes = 4) {
+  constexpr int DB = 8, kBins = 1 << DB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kWords = PER_WAVE ? kTopkWaves * kHistStride : 256;
+  constexpr int kWords = PER_WAVE ? kTopkWaves * kHistStride : kBins;
   const int nb = lo == hi ? 0 : 32 - __clz(lo ^ hi);   // bits still to decide
   uint32_t pmask = nb == 32 ? 0u : ~((1u << nb) - 1u);
   uint32_t prefix = lo & pmask;
@@ -302,8 +304,8 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
   for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[0][i] = 0u;
   __syncthreads();
   int pass = 0;
-  for (int top = nb; top > 0; top -= 8, ++pass) {
-    const int shift = top > 8 ? top - 8 : 0;
+  for (int top = nb; top > 0; top -= DB, ++pass) {
+    const int shift = top > DB ? top - DB : 0;
     const uint32_t dmask = (1u << (top - shift)) - 1u;
     const int par = pass & 1;
     uint32_t* h = sm.hist[par];
@@ -328,19 +330,21 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
       c = sm.cnt[par];
     }
     if (wave == 0) {
-      // lane owns bins 255-4*lane down to 252-4*lane, so a prefix scan over
-      // lanes counts the keys in all higher bins
-      const int b0 = 255 - 4 * lane;
-      const int cs[4] = {(int)c[b0], (int)c[b0 - 1], (int)c[b0 - 2], (int)c[b0 - 3]};
-      const int local = cs[0] + cs[1] + cs[2] + cs[3];
+      // lane owns bins 4*lane .. 4*lane+3 (one 16-byte read), the higher lanes
+      // the higher bins, so an exclusive prefix over lanes in reverse order
+      // counts the keys in all higher bins
+      const uint4 v = *reinterpret_cast<const uint4*>(c + kBins - 4 * (lane + 1));
+      const int e[4] = {(int)v.w, (int)v.z, (int)v.y, (int)v.x};  // bins downward
+      const int local = e[0] + e[1] + e[2] + e[3];
       int run = wave_inclusive_scan(local) - local;
+      const int b0 = kBins - 1 - 4 * lane;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        if (run < krem && krem <= run + cs[d]) {
+        if (run < krem && krem <= run + e[d]) {
           sm.res[par][0] = b0 - d;
           sm.res[par][1] = run;
         }
-        run += cs[d];
+        run += e[d];
       }
     }
     __syncthreads();
@@ -357,6 +361,8 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
 // (key, row index) pairs in ascending row order.
 constexpr int kCandCap = 8192;
 constexpr int kCandPerThread = kCandCap / kTopkThreads;
+constexpr int kCandSlots = kCandCap + kWave;  // + one spare slot per lane
+
 
 // Ascending-index emission of the selection {key > T} plus the keq
 // lowest-indexed keys equal to T, over items that thread t holds as a
@@ -396,8 +402,7 @@ __device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, i
 template <int KPT, bool VEC4>
 __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
   __shared__ SelectSmem sm;
-  __shared__ uint32_t cand_key[kCandCap];
-  __shared__ uint32_t cand_idx[kCandCap];
+  __shared__ uint2 cand[kCandSlots];  // (key, row index)
 
   const int tid = threadIdx.x;
   const int tok = blockIdx.x;
@@ -471,27 +476,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     uint32_t row_max;
     int pos = block_exclusive_scan_max(mine, kmax, sm.red, c, row_max);
     if (c >= K && c <= kCandCap) {  // block-uniform
+      // branch-free: every slot is written, a non-candidate into this lane's
+      // spare slot past the buffer
+      const int spare = kCandCap + (tid & (kWave - 1));
 #pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (valid(j) && key[j] >= tau) {
-          cand_key[pos] = key[j];
-          cand_idx[pos] = (uint32_t)(i0 + j);
-          ++pos;
-        }
+      for (int j = 0; j < KPT; ++j) {
+        const bool hit = valid(j) && key[j] >= tau;
+        cand[hit ? pos : spare] = make_uint2(key[j], (uint32_t)(i0 + j));
+        pos += hit ? 1 : 0;
+      }
       __syncthreads();
       // every candidate lies in [tau, row max]; few keys per thread, so one
       // shared histogram
       uint32_t T;
       int keq;
       block_radix_select<false, kCandPerThread>(
-          [&](int r) { return cand_key[min(r * kTopkThreads + tid, c - 1)]; },
+          [&](int r) { return cand[min(r * kTopkThreads + tid, c - 1)].x; },
           [&](int r) { return r * kTopkThreads + tid < c; }, K, tau, row_max, sm, T, keq);
       // emission over the candidates only: thread t takes a contiguous run
       const int cpt = (c + kTopkThreads - 1) / kTopkThreads;
       const int c0 = min(c, tid * cpt), cnt = min(c, c0 + cpt) - c0;
-      emit_selection<kCandPerThread>(
-          [&](int j) { return make_uint2(cand_key[c0 + j], cand_idx[c0 + j]); }, cnt, T, keq, out, K,
-          sm.red);
+      emit_selection<kCandPerThread>([&](int j) { return cand[c0 + j]; }, cnt, T, keq, out, K, sm.red);
       return;
     }
   }
