@@ -204,6 +204,29 @@ def test_end_to_end(cid, config_inputs):
     U.compare_outputs(sh, got["out"], ref["out"], tokens=keep)
 
 
+@pytest.mark.parametrize("n_cap,topk,S,Hi", [(3000, 256, 2, 8), (12000, 1024, 2, 8), (9000, 512, 1, 4)])
+def test_end_to_end_exact_grid(n_cap, topk, S, Hi):
+    # On the dyadic grid every score is exact on both sides, so GPU scoring
+    # plus GPU Top-K must give the oracle's lists with no exemption at all,
+    # although the grid makes ties plentiful (lower index wins).
+    cfg = small_cfg(q_per_req=S, idx_heads=Hi, n_cap=n_cap, topk=topk, max_len=4 * n_cap,
+                    win=64, w_cap=64 + S)
+    inp = I.make_inputs(cfg, start_pos=np.array([4 * n_cap - S, 4 * n_cap - 2 * S - 77,
+                                                 4 * topk - 1, 4 * topk + 3], np.int32))
+    g = np.random.default_rng(n_cap + topk)
+    inp["q_idx"] = I.f32_to_bf16_bits((g.integers(-8, 9, inp["q_idx"].shape) / 4.0).astype(np.float32))
+    kg = I.f32_to_bf16_bits((g.integers(-8, 9, inp["k_idx"].shape) / 4.0).astype(np.float32))
+    inp["k_idx"] = np.where(inp["k_idx"] == I.f32_to_bf16_bits(np.float32([I.POISON]))[0],
+                            inp["k_idx"], kg)
+    inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    sh = cfg.shape
+    ref = oracle_step(sh, inp)
+    got = gpu_step(sh, inp)
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+    U.compare_outputs(sh, got["out"], ref["out"])
+
+
 def test_determinism(config_inputs):
     cid = 3
     sh, inp = I.CONFIGS[cid].shape, config_inputs(cid)
