@@ -4,5 +4,5 @@ Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
 may import this package.  The product path never does: it runs the HIP
 library or fails.
 """
-from .csa_oracle import (JOB_ATTN, JOB_SCORE, JOB_TOPK, build, n_vis, round_bf16,  # noqa: F401
+from .csa_oracle import (JOB_ATTN, JOB_SCORE, JOB_TOPK, build, e4m3_value, n_vis, round_bf16,  # noqa: F401
                          run, select_row)

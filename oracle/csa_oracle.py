@@ -54,8 +54,11 @@ def _get():
         lib.oracle_round_bf16.restype = ctypes.c_float
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_run.restype = ctypes.c_int32
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_int32]
         lib.oracle_run.argtypes = ([ctypes.POINTER(_OShape)] + [ctypes.c_int32] * 4
                                    + [ctypes.c_void_p] * 13 + [ctypes.c_int32, ctypes.c_float,
+                                                               ctypes.c_void_p, ctypes.c_void_p,
                                                                ctypes.c_void_p])
         _lib = lib
     return _lib
@@ -67,6 +70,11 @@ def n_vis(p: int, ratio: int) -> int:
 
 def round_bf16(x: float) -> float:
     return float(_get().oracle_round_bf16(float(x)))
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP FP8 E4M3 code, as the oracle decodes it."""
+    return float(_get().oracle_e4m3_value(int(code)))
 
 
 def select_row(scores: np.ndarray, k: int, n: Optional[int] = None) -> np.ndarray:
@@ -90,7 +98,9 @@ def run(shape, inp: dict, jobs: int = JOB_SCORE | JOB_TOPK | JOB_ATTN, scale: Op
 
     `inp` is the dict from the seeded input generator.  `scores` / `topk_idx`
     may be given to start from a later step; otherwise they are allocated
-    (scores filled with NaN, so untouched entries stay recognisable).
+    (scores filled with NaN, so untouched entries stay recognisable).  When
+    `inp` holds "k_idx8" and "k_scale" (an FP8 indexer key cache), the keys
+    come from those and "k_idx" is not read.
     Returns dict(scores, topk_idx, out) with out as float32 [G, B*S, (H/G)*D].
     """
     sh = _OShape(*[int(getattr(shape, f)) for f in _FIELDS])
@@ -118,7 +128,7 @@ def run(shape, inp: dict, jobs: int = JOB_SCORE | JOB_TOPK | JOB_ATTN, scale: Op
         _ptr(a.get("q")), _ptr(a.get("k_win")), _ptr(a.get("v_win")), _ptr(a.get("k_cmp")),
         _ptr(a.get("v_cmp")), _ptr(a.get("rope_cos")), _ptr(a.get("rope_sin")),
         int(a["rope_cos"].shape[0]) if a.get("rope_cos") is not None else 0,
-        float(scale), out.ctypes.data)
+        float(scale), out.ctypes.data, _ptr(a.get("k_idx8")), _ptr(a.get("k_scale")))
     if rc:
         raise RuntimeError(f"oracle_run failed with code {rc}")
     return dict(scores=scores, topk_idx=topk_idx, out=out)

@@ -56,6 +56,31 @@ static float round_bf16(double x) {
   return (float)ldexp(r, e - 8);
 }
 
+/* Value of an OCP FP8 E4M3 code (the "e4m3fn" encoding): sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m/8 * 2^-6; S.1111.111 is NaN and there are no infinities, so
+ * the largest finite value is 1.75 * 2^8 = 448.  Written from that definition,
+ * in float64, where every such value is exact. */
+static double e4m3_val(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* Element c of indexer key row j of request b.  With an FP8 key cache
+ * (k_idx8 non-NULL) the row is stored as E4M3 codes plus one fp32 scale per
+ * row, and its value is scale * decode(code) (the pages pass an indexer key
+ * cache together with its scale, "Fix: complete DeepSeek V4 TP CSA decode",
+ * description; the encoding and the per-row granularity are this build's
+ * reading).  Otherwise the row is read in the input dtype. */
+static double key_val(const oracle_shape_t *sh, const void *k_idx, const uint8_t *k_idx8,
+                      const float *k_scale, int32_t b, int32_t j, int32_t c) {
+  const size_t row = (size_t)b * sh->n_cap + (size_t)j;
+  if (k_idx8) return (double)k_scale[row] * e4m3_val(k_idx8[row * (size_t)sh->idx_dim + c]);
+  return in_val(k_idx, row * (size_t)sh->idx_dim + c, sh->dtype);
+}
+
 /* Causal visibility: compressed row j summarises raw tokens R*j .. R*j+R-1
  * and is visible to a query at position p once the whole block is at or before
  * p.  Hence the count of visible rows is floor((p+1)/R).  (The pages name only
@@ -117,6 +142,7 @@ int32_t oracle_select_row(const float *scores, int32_t n, int32_t k,
  * fp32.  Tokens that bypass (n_vis <= K) are not scored at all. */
 static void score_token(const oracle_shape_t *sh, int32_t b, int32_t s,
                         const void *q_idx, const float *w, const void *k_idx,
+                        const uint8_t *k_idx8, const float *k_scale,
                         const int32_t *start_pos, float *scores) {
   const int32_t S = sh->q_per_req, Hi = sh->idx_heads, Di = sh->idx_dim;
   const int32_t p = start_pos[b] + s;
@@ -129,9 +155,8 @@ static void score_token(const oracle_shape_t *sh, int32_t b, int32_t s,
     for (int32_t h = 0; h < Hi; ++h) {
       double dot = 0.0;
       const size_t qo = (tok * Hi + h) * (size_t)Di;
-      const size_t ko = ((size_t)b * sh->n_cap + j) * (size_t)Di;
       for (int32_t c = 0; c < Di; ++c)
-        dot += in_val(q_idx, qo + c, sh->dtype) * in_val(k_idx, ko + c, sh->dtype);
+        dot += in_val(q_idx, qo + c, sh->dtype) * key_val(sh, k_idx, k_idx8, k_scale, b, j, c);
       double r = dot > 0.0 ? dot : 0.0;
       acc += (double)w[tok * Hi + h] * r;
     }
@@ -258,6 +283,8 @@ typedef struct {
   const oracle_shape_t *sh;
   int jobs;
   const void *q_idx, *k_idx, *q, *k_win, *v_win, *k_cmp, *v_cmp;
+  const uint8_t *k_idx8;
+  const float *k_scale;
   const float *w, *rope_cos, *rope_sin;
   const int32_t *start_pos;
   float *scores;
@@ -283,7 +310,8 @@ static void *run_job(void *arg) {
     for (int32_t t = jb->tok_begin + jb->tid; t < jb->tok_end; t += jb->nthreads) {
       int32_t b = t / S, s = t % S;
       if (jb->jobs & JOB_SCORE)
-        score_token(sh, b, s, jb->q_idx, jb->w, jb->k_idx, jb->start_pos, jb->scores);
+        score_token(sh, b, s, jb->q_idx, jb->w, jb->k_idx, jb->k_idx8, jb->k_scale,
+                    jb->start_pos, jb->scores);
       if (jb->jobs & JOB_TOPK)
         topk_token(sh, b, s, jb->scores, jb->start_pos, jb->topk_idx);
       if (jb->jobs & JOB_ATTN)
@@ -318,7 +346,9 @@ static int check_shape(const oracle_shape_t *sh, const int32_t *start_pos,
 }
 
 /* Run any subset of the three steps over tokens [tok_begin, tok_end) with
- * nthreads threads.  Returns 0 on success. */
+ * nthreads threads.  With k_idx8 and k_scale non-NULL the indexer keys come
+ * from the FP8 cache (key_val above) and k_idx is not read.  Returns 0 on
+ * success. */
 int32_t oracle_run(const oracle_shape_t *sh, int32_t jobs, int32_t tok_begin,
                    int32_t tok_end, int32_t nthreads, const void *q_idx,
                    const float *w, const void *k_idx, const int32_t *start_pos,
@@ -326,7 +356,8 @@ int32_t oracle_run(const oracle_shape_t *sh, int32_t jobs, int32_t tok_begin,
                    const void *k_win, const void *v_win, const void *k_cmp,
                    const void *v_cmp, const float *rope_cos,
                    const float *rope_sin, int32_t rope_rows,
-                   float softmax_scale, float *out) {
+                   float softmax_scale, float *out, const uint8_t *k_idx8,
+                   const float *k_scale) {
   int st = check_shape(sh, start_pos, (jobs & (JOB_SCORE | JOB_TOPK)) != 0);
   if (st) return st;
   if ((jobs & JOB_ATTN) && rope_rows < sh->max_len) return 14;
@@ -340,6 +371,7 @@ int32_t oracle_run(const oracle_shape_t *sh, int32_t jobs, int32_t tok_begin,
   }
   for (int32_t i = 0; i < nthreads; ++i) {
     jb[i] = (job_t){.sh = sh, .jobs = jobs, .q_idx = q_idx, .k_idx = k_idx,
+                    .k_idx8 = k_idx8, .k_scale = k_scale,
                     .q = q, .k_win = k_win, .v_win = v_win, .k_cmp = k_cmp,
                     .v_cmp = v_cmp, .w = w, .rope_cos = rope_cos,
                     .rope_sin = rope_sin, .start_pos = start_pos,
@@ -366,3 +398,6 @@ int32_t oracle_run(const oracle_shape_t *sh, int32_t jobs, int32_t tok_begin,
 
 /* Helper for tests: round a double to bf16 exactly as the output step does. */
 float oracle_round_bf16(double x) { return round_bf16(x); }
+
+/* Helper for tests: the value of one E4M3 code. */
+double oracle_e4m3_value(int32_t code) { return e4m3_val((uint8_t)code); }

@@ -129,6 +129,46 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint16)
 
 
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Encode values as OCP FP8 E4M3 codes (uint8): round to nearest, ties to
+    even; magnitudes past the largest finite value (448) saturate to it.
+
+    Data formatting of the FP8 indexer key cache the inputs carry; the kernels
+    and the oracle only decode.  NaN inputs are not expected.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    # binade exponent of a, floored at the smallest normal binade (2^-6)
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))   # a = m * 2^ex, m in [0.5, 1)
+    e = np.clip(ex - 1, -6, 8)
+    q = np.rint(a / np.exp2(e - 3))              # 3 fraction bits: q in [0, 16]
+    up = q >= 16                                 # rounded into the next binade
+    e = np.where(up, e + 1, e)
+    q = np.where(up, 8, q)
+    over = (e > 8) | ((e == 8) & (q > 14))       # past 1.75 * 2^8: saturate
+    e = np.where(over, 8, e)
+    q = np.where(over, 14, q)
+    normal = q >= 8                              # else a subnormal (e == -6)
+    field = np.where(normal, e + 7, 0).astype(np.uint8)
+    man = np.where(normal, q - 8, q).astype(np.uint8)
+    sign = np.signbit(x).astype(np.uint8) << np.uint8(7)
+    return (sign | (field << np.uint8(3)) | man).astype(np.uint8)
+
+
+def quantize_rows_e4m3(k: np.ndarray):
+    """Per-row FP8 E4M3 quantisation of float32 rows [..., Di]: scale = amax / 448
+    (1 for an all-zero row), codes = E4M3(k / scale).  Returns (codes uint8,
+    scales float32)."""
+    k = np.asarray(k, dtype=np.float32)
+    amax = np.abs(k).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    codes = f32_to_e4m3_bits(k / scale[..., None])
+    return codes, scale
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
@@ -204,7 +244,7 @@ def visible_rows(p: np.ndarray, ratio: int) -> np.ndarray:
 
 def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
                 shape: Optional[Shape] = None, start_pos: Optional[np.ndarray] = None,
-                structure: Optional[str] = None) -> Dict[str, np.ndarray]:
+                structure: Optional[str] = None, key_format: str = "bf16") -> Dict[str, np.ndarray]:
     """Draw every input of one decode step.
 
     Returns a dict of contiguous numpy arrays:
@@ -214,6 +254,10 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
       for configurations whose harness supplies the selection,
       topk_idx [B,S,K] int32.
     Storage is uint16 (bf16 bits) or float32 according to shape.dtype.
+    With key_format="fp8" the indexer keys come instead as an FP8 cache:
+    k_idx8 [B,N_cap,Di] uint8 E4M3 codes and k_scale [B,N_cap] float32, each
+    row quantised from the keys drawn above (so planted rows, duplicated
+    rows and poison keep their meaning); k_idx is then left out.
     """
     cfg = CONFIGS[cfg_id_or_cfg] if isinstance(cfg_id_or_cfg, int) else cfg_id_or_cfg
     sh = shape or cfg.shape
@@ -293,6 +337,15 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
         out = {k: f.result() for k, f in futs.items()}
     del raw
     out.update(start_pos=sp, w=np.ascontiguousarray(w, np.float32), rope_cos=cos, rope_sin=sin)
+    if key_format == "fp8":
+        kf = out.pop("k_idx")
+        codes = np.empty(kf.shape, dtype=np.uint8)
+        scales = np.empty(kf.shape[:2], dtype=np.float32)
+        for b in range(B):   # one request at a time keeps the float64 temporaries small
+            codes[b], scales[b] = quantize_rows_e4m3(as_float(kf[b], dt))
+        out.update(k_idx8=codes, k_scale=scales)
+    elif key_format != "bf16":
+        raise ValueError(key_format)
     if cfg.supplied_topk:
         # The HCA-shaped case attends every compressed row it is given.
         K = sh.topk

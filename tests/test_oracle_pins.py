@@ -194,6 +194,107 @@ def test_scores_exact_grid():
 
 
 # --------------------------------------------------------------------------
+# FP8 (OCP E4M3) indexer key cache with one fp32 scale per row
+# --------------------------------------------------------------------------
+
+def torch_e4m3(codes):
+    """Library decode of E4M3 codes (torch's float8_e4m3fn), as float64."""
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_decode_vs_library():
+    dec = np.array([oracle.e4m3_value(c) for c in range(256)])
+    lib = torch_e4m3(np.arange(256))
+    assert np.array_equal(np.isnan(dec), np.isnan(lib))
+    fin = ~np.isnan(lib)
+    assert np.array_equal(dec[fin], lib[fin])
+    # landmarks of the format: 1.0, the largest finite value 448, the smallest
+    # normal 2^-6 and subnormal 2^-9, the two NaN codes, negative zero
+    assert dec[0x38] == 1.0 and dec[0x7E] == 448.0
+    assert dec[0x08] == 2.0 ** -6 and dec[0x01] == 2.0 ** -9
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    assert dec[0x80] == 0.0 and math.copysign(1.0, dec[0x80]) == -1.0
+    # finite positive codes increase strictly; negative codes mirror them
+    assert np.all(np.diff(dec[:0x7F]) > 0)
+    assert np.array_equal(dec[0x80:0xFF], -dec[:0x7F])
+
+
+def test_e4m3_encoder_vs_library():
+    # the input generator's nearest-even encoding agrees with torch's in range
+    g = np.random.default_rng(3)
+    x = (g.standard_normal(50000) * np.exp2(g.integers(-12, 10, 50000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(I.f32_to_e4m3_bits(x), lib)
+    assert I.f32_to_e4m3_bits(np.float32([1000.0, -500.0])).tolist() == [0x7E, 0xFE]  # saturates
+
+
+def fp8_case(sh, seed, pow2_scales):
+    """Inputs with random finite E4M3 key codes and per-row scales, plus the
+    same keys dequantised by the library decoder as float64."""
+    inp = small_inputs(sh, seed=seed)
+    g = np.random.default_rng(seed + 1)
+    codes = g.integers(0, 256, size=inp["k_idx"].shape).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    if pow2_scales:
+        scales = np.exp2(g.integers(-3, 4, size=codes.shape[:2])).astype(np.float32)
+    else:
+        scales = g.uniform(0.01, 3.0, size=codes.shape[:2]).astype(np.float32)
+    deq = torch_e4m3(codes) * scales.astype(np.float64)[..., None]
+    inp8 = dict(inp)
+    del inp8["k_idx"]
+    inp8.update(k_idx8=codes, k_scale=scales)
+    return inp, inp8, deq
+
+
+def test_fp8_keys_equal_dequantised_bf16_keys():
+    # With power-of-two scales every dequantised key is a bf16 value, so the
+    # FP8 path must give the bf16 path's scores bit for bit.
+    sh = small_shape(dtype=I.BF16, topk=4)
+    inp, inp8, deq = fp8_case(sh, 11, pow2_scales=True)
+    inp["k_idx"] = I.f32_to_bf16_bits(deq.astype(np.float32))
+    assert np.array_equal(I.as_float(inp["k_idx"], I.BF16), deq)   # exact in bf16
+    r16 = oracle.run(sh, inp, jobs=oracle.JOB_SCORE)
+    r8 = oracle.run(sh, inp8, jobs=oracle.JOB_SCORE)
+    assert np.array_equal(r8["scores"], r16["scores"], equal_nan=True)
+    assert np.isfinite(r8["scores"]).any()
+
+
+def test_fp8_scores_vs_einsum():
+    sh = small_shape(dtype=I.BF16, topk=4)
+    _, inp8, deq = fp8_case(sh, 12, pow2_scales=False)
+    r = oracle.run(sh, inp8, jobs=oracle.JOB_SCORE)
+    q = fvals(inp8["q_idx"], I.BF16)
+    d = np.einsum("bshc,bjc->bshj", q, deq)
+    ref = np.einsum("bsh,bshj->bsj", inp8["w"].astype(np.float64), np.maximum(d, 0.0))
+    for b in range(sh.batch):
+        for s in range(sh.q_per_req):
+            n = oracle.n_vis(int(inp8["start_pos"][b]) + s, sh.ratio)
+            if n > sh.topk:
+                np.testing.assert_allclose(r["scores"][b, s, :n], ref[b, s, :n], rtol=2e-7, atol=1e-6)
+
+
+def test_fp8_scale_is_per_row():
+    # doubling one row's scale doubles exactly that row's scores (relu is
+    # positively homogeneous) and changes nothing else
+    sh = small_shape(dtype=I.BF16, topk=4)
+    _, inp8, _ = fp8_case(sh, 13, pow2_scales=True)
+    r1 = oracle.run(sh, inp8, jobs=oracle.JOB_SCORE)["scores"]
+    b0 = 1
+    j0 = 3
+    inp2 = dict(inp8)
+    inp2["k_scale"] = inp8["k_scale"].copy()
+    inp2["k_scale"][b0, j0] *= 2
+    r2 = oracle.run(sh, inp2, jobs=oracle.JOB_SCORE)["scores"]
+    changed = np.zeros(r1.shape, dtype=bool)
+    changed[b0, :, j0] = True
+    assert np.array_equal(r2[~changed], r1[~changed], equal_nan=True)
+    col1, col2 = r1[b0, :, j0], r2[b0, :, j0]
+    ok = ~np.isnan(col1)
+    assert ok.any() and np.array_equal(col2[ok], 2 * col1[ok])
+
+
+# --------------------------------------------------------------------------
 # attention: library attention on the concatenated rows, closed forms
 # --------------------------------------------------------------------------
 
