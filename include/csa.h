@@ -5,6 +5,7 @@
  * order on one HIP stream:
  *
  *   csa_indexer_score      score every causally visible compressed row
+ *                          (csa_indexer_score_fp8: from an FP8 key cache)
  *   csa_topk               pick the Top-K rows per query token (or bypass)
  *   csa_sparse_attn_decode attend the raw window plus the picked rows, merge
  *                          the two softmax streams, undo RoPE, pack heads
@@ -111,6 +112,29 @@ typedef struct {
 csa_status_t csa_indexer_score(const csa_shape_t* shape, const void* q_idx, const float* w,
                                const void* k_idx, const int32_t* start_pos, float* scores,
                                void* stream);
+
+/* Indexer scores from an FP8 indexer key cache.
+ *
+ * Same result contract as csa_indexer_score, with key row j of request b
+ * given as OCP FP8 E4M3 codes ("e4m3fn": bias 7, largest finite 448, code
+ * S.1111.111 is NaN) and one fp32 scale:
+ *   k_idx[b][j][c] = k_scale[b][j] * e4m3(k_idx8[b][j][c])
+ * The pages pass the indexer key cache together with its scale ("Fix:
+ * complete DeepSeek V4 TP CSA decode", description); the encoding and the
+ * per-row granularity are this library's reading.  The codes are widened to
+ * bf16 exactly, so products stay exact and sums are float32 as in
+ * csa_indexer_score; the scale multiplies each row's head sum.
+ *
+ *   q_idx   [B][S][Hi][Di]  bf16 (shape->dtype must be CSA_DTYPE_BF16, else
+ *                           CSA_ERR_BAD_DTYPE)
+ *   w       [B][S][Hi]      float32
+ *   k_idx8  [B][n_cap][Di]  uint8 E4M3 codes (NaN codes are outside the contract)
+ *   k_scale [B][n_cap]      float32, >= 0 and finite
+ *   start_pos, scores       as csa_indexer_score
+ */
+csa_status_t csa_indexer_score_fp8(const csa_shape_t* shape, const void* q_idx, const float* w,
+                                   const uint8_t* k_idx8, const float* k_scale,
+                                   const int32_t* start_pos, float* scores, void* stream);
 
 /* Workspace bytes csa_topk needs for this shape (0 means none). */
 size_t csa_topk_workspace_bytes(const csa_shape_t* shape);

@@ -5,9 +5,9 @@ device pointers and sizes through the C ABI declared in include/csa.h and
 raises if the library returns an error.  There is no CPU path: a missing
 library, a CPU tensor or a non-contiguous tensor is an error.
 
-Names match the C ABI: indexer_score, topk, sparse_attn_decode, plus the
-workspace queries and step(), which issues the three calls in order on one
-stream.
+Names match the C ABI: indexer_score, indexer_score_fp8, topk,
+sparse_attn_decode, plus the workspace queries and step(), which issues the
+three calls in order on one stream.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL_PTR", 2: "CSA_ERR_BAD_SHAPE", 3: "CSA_ER
           4: "CSA_ERR_CAPACITY", 5: "CSA_ERR_ALIGNMENT", 6: "CSA_ERR_WORKSPACE",
           7: "CSA_ERR_LAUNCH", 8: "CSA_ERR_UNSUPPORTED"}
 
-EXPORTS = ("csa_indexer_score", "csa_topk_workspace_bytes", "csa_topk",
+EXPORTS = ("csa_indexer_score", "csa_indexer_score_fp8", "csa_topk_workspace_bytes", "csa_topk",
            "csa_sparse_attn_workspace_bytes", "csa_sparse_attn_decode", "csa_status_string",
            "csa_abi_version")
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         sp = ctypes.POINTER(CShape)
         L.csa_indexer_score.restype = i32
         L.csa_indexer_score.argtypes = [sp, vp, vp, vp, vp, vp, vp]
+        L.csa_indexer_score_fp8.restype = i32
+        L.csa_indexer_score_fp8.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk_workspace_bytes.argtypes = [sp]
         L.csa_topk.restype = i32
@@ -129,6 +131,14 @@ def indexer_score(shape, q_idx, w, k_idx, start_pos, scores, stream=None) -> Non
         _dev(start_pos, "start_pos"), _dev(scores, "scores"), _stream(stream)))
 
 
+def indexer_score_fp8(shape, q_idx, w, k_idx8, k_scale, start_pos, scores, stream=None) -> None:
+    cs = CShape.of(shape)
+    _check("csa_indexer_score_fp8", lib().csa_indexer_score_fp8(
+        ctypes.byref(cs), _dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx8, "k_idx8"),
+        _dev(k_scale, "k_scale"), _dev(start_pos, "start_pos"), _dev(scores, "scores"),
+        _stream(stream)))
+
+
 def topk(shape, scores, start_pos, topk_idx, ws=None, stream=None) -> None:
     cs = CShape.of(shape)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -189,8 +199,12 @@ def step(shape, dev: dict, bufs: dict, softmax_scale: float, stream=None,
     if supplied_topk:
         ti = dev["topk_idx"]
     else:
-        indexer_score(shape, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
-                      bufs["scores"], stream)
+        if "k_idx8" in dev:   # FP8 indexer key cache
+            indexer_score_fp8(shape, dev["q_idx"], dev["w"], dev["k_idx8"], dev["k_scale"],
+                              dev["start_pos"], bufs["scores"], stream)
+        else:
+            indexer_score(shape, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
+                          bufs["scores"], stream)
         topk(shape, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
         ti = bufs["topk_idx"]
     sparse_attn_decode(shape, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],

@@ -54,7 +54,27 @@ csa_status_t csa_indexer_score(const csa_shape_t* sh, const void* q_idx, const f
       !aligned16(scores))
     return CSA_ERR_ALIGNMENT;
   csa::ScoreArgs a{q_idx, w, k_idx, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
-                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype};
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, nullptr};
+  (void)hipGetLastError();  // report only what these launches cause
+  return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status_t csa_indexer_score_fp8(const csa_shape_t* sh, const void* q_idx, const float* w,
+                                   const uint8_t* k_idx8, const float* k_scale,
+                                   const int32_t* start_pos, float* scores, void* stream) {
+  bool empty = false;
+  csa_status_t st = check_common(sh, &empty);
+  if (st != CSA_OK || empty) return st;
+  if (!q_idx || !w || !k_idx8 || !k_scale || !start_pos || !scores) return CSA_ERR_NULL_PTR;
+  if (sh->dtype != CSA_DTYPE_BF16) return CSA_ERR_BAD_DTYPE;  // bf16 queries only
+  if (sh->idx_dim != 64 && sh->idx_dim != 128) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)sh->q_per_req * sh->idx_heads > 64) return CSA_ERR_UNSUPPORTED;
+  if ((st = check_selection(sh)) != CSA_OK) return st;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx8) || !aligned16(k_scale) ||
+      !aligned16(start_pos) || !aligned16(scores))
+    return CSA_ERR_ALIGNMENT;
+  csa::ScoreArgs a{q_idx, w, k_idx8, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, k_scale};
   (void)hipGetLastError();  // report only what these launches cause
   return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
 }

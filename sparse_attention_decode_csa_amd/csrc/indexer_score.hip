@@ -58,16 +58,40 @@ struct ScoreTile {
   static_assert(NPR >= 4 && RPI >= 1 && NPT >= 1, "unsupported row size");
 };
 
+// Eight OCP E4M3 codes (two dwords, lowest byte first) as eight bf16 values
+// in the MFMA operand order.  Every E4M3 value has at most 4 significant bits,
+// so the high half of its fp32 decoding is the exact bf16 value.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(w0, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(w0, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(w1, false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(w1, true);
+  auto pk = [](float lo, float hi) {  // high halves of two fp32 values
+    return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                                 0x07060302u);
+  };
+  return u32x4_t{pk(a.x, a.y), pk(b.x, b.y), pk(c.x, c.y), pk(d.x, d.y)};
+}
+
 // HI > 0: the indexer head count, a power of two in 4 .. 16, so that the four
 // result rows a lane holds (4g .. 4g+3 of a 16-row tile) belong to one token
 // and the head sum finishes with at most two cross-lane adds.  HI == 0: any
 // head count, summed through a small per-wave LDS tile.
-template <typename T, int DI, int MT, int HI>
+// KF8: the keys are an FP8 cache (E4M3 codes plus one fp32 scale per row,
+// the indexer key cache and its scale of "Fix: complete DeepSeek V4 TP CSA
+// decode", description).  Rows are half as long, the codes are widened to
+// bf16 exactly in registers, the bf16 query is unchanged, and the row's scale
+// multiplies its head sum (relu is positively homogeneous, so
+// scale * sum_h w_h relu(q_h . c) = sum_h w_h relu(q_h . (scale * c))).
+template <typename T, int DI, int MT, int HI, bool KF8>
 __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   constexpr int ES = sizeof(T);
-  constexpr int ROW = DI * ES;
-  constexpr int CH = ROW / 64;       // 64-byte k-chunks per row; a lane holds 16 B of each
-  static_assert(CH >= 1 && ROW % 64 == 0, "row must be a whole number of 64-byte chunks");
+  constexpr int QROW = DI * ES;              // bytes per query row
+  constexpr int ROW = KF8 ? DI : DI * ES;    // bytes per key row
+  constexpr int CH = QROW / 64;              // 32-dim MFMA k-steps per row; 16 B of each per lane
+  static_assert(CH >= 1 && QROW % 64 == 0, "row must be a whole number of 64-byte chunks");
+  static_assert(!KF8 || (ES == 2 && CH % 2 == 0), "FP8 keys pair with bf16 queries");
   using TL = ScoreTile<ROW>;
   constexpr int ROWS = MT * 16;      // padded query rows
   constexpr int RP = 17;             // padded LDS row length (floats)
@@ -91,25 +115,39 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   const int key0 = blockIdx.x * kScoreKeysPerBlock;
   if (key0 >= nmax) return;  // whole workgroup: nothing visible in this chunk
 
-  // A operand: query row qr = mt*16 + n16 (token qr / Hi, head qr % Hi);
-  // padded rows load a real row and are zeroed, so the loads stay unconditional.
+  // per-row scales of this lane's key in each tile (FP8 keys), loaded first:
+  // every load issued before the tile DMAs is older than them, so the tile
+  // waits below can count DMA instructions only
+  float ks[KF8 ? kScoreTilesPerWave : 1];
+  if constexpr (KF8) {
+#pragma unroll
+    for (int t = 0; t < kScoreTilesPerWave; ++t)
+      ks[t] = a.k_scale[(size_t)b * a.n_cap + min(key0 + (t * kScoreWaves + wave) * 16 + n16, nmax - 1)];
+  }
+
+  // A operand: query row qr = mt*16 + n16 (token qr / Hi, head qr % Hi).
+  // Rows past S*Hi (padding to 16) load a copy of the last real row and are
+  // never used: on the register path they belong to token indices >= S, whose
+  // sums are not stored; on the LDS path the head sum reads real rows only.
+  // Nothing consumes these loads before the MFMAs, so no wait delays the DMAs.
   u32x4_t qa[MT][CH];
   float wv[MT][4];
-  const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * ROW;
+  const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * QROW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int qr = mt * 16 + n16;
-    const char* qp = qbase + (size_t)min(qr, SH - 1) * ROW + g * 16;
+    const char* qp = qbase + (size_t)min(qr, SH - 1) * QROW;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const u32x4_t v = ld16(qp + c * 64);
-      qa[mt][c] = qr < SH ? v : u32x4_t{0, 0, 0, 0};
+      // k-step c, group g: dims [32c + 8g, +8); with FP8 keys, whose lane reads
+      // 16 contiguous codes per two steps, dims [64(c/2) + 16g + 8(c%2), +8)
+      const int qoff = KF8 ? 128 * (c >> 1) + 32 * g + 16 * (c & 1) : 64 * c + 16 * g;
+      qa[mt][c] = ld16(qp + qoff);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = mt * 16 + 4 * g + i;   // result rows this lane holds
-      const float wr = a.w[(size_t)b * SH + min(row, SH - 1)];
-      wv[mt][i] = row < SH ? wr : 0.0f;
+      wv[mt][i] = a.w[(size_t)b * SH + min(row, SH - 1)];
     }
   }
   // Fast path: the token of tile mt's rows 4g..4g+3 and its visible count.
@@ -159,10 +197,20 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
     }
     const char* src = tiles[wave][t % kScoreBufs];
     u32x4_t kb[CH];
+    if constexpr (KF8) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int slot = (4 * c + g) ^ (n16 % TL::NPR);
-      kb[c] = *reinterpret_cast<const u32x4_t*>(src + n16 * ROW + 16 * slot);
+      for (int c2 = 0; c2 < CH / 2; ++c2) {
+        const int slot = (4 * c2 + g) ^ (n16 % TL::NPR);
+        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(src + n16 * ROW + 16 * slot);
+        kb[2 * c2] = e4m3x8_to_bf16(raw[0], raw[1]);
+        kb[2 * c2 + 1] = e4m3x8_to_bf16(raw[2], raw[3]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int slot = (4 * c + g) ^ (n16 % TL::NPR);
+        kb[c] = *reinterpret_cast<const u32x4_t*>(src + n16 * ROW + 16 * slot);
+      }
     }
     if (t + kScoreBufs < kScoreTilesPerWave) {
       wait_lgkmcnt0();  // the operand reads of this buffer are done: refill it
@@ -190,6 +238,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         }
         if constexpr (HI >= 8) sum += __shfl_xor(sum, 16);
         if constexpr (HI >= 16) sum += __shfl_xor(sum, 32);
+        if constexpr (KF8) sum *= ks[t];
         const bool writer = (g & (HI / 4 - 1)) == 0;
         if (writer && tok_of[mt] < S && nv_of[mt] > a.topk && j < nv_of[mt])
           srow[(size_t)tok_of[mt] * a.n_cap + j] = sum;
@@ -208,6 +257,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
         float sum = 0.0f;
         for (int h = 0; h < Hi; ++h) sum += red[wave][s * Hi + h][n];
+        if constexpr (KF8) sum *= ks[t];  // n == n16: this lane's key
         const int j = tkey0 + n;
         if (nv > a.topk && j < nv) srow[(size_t)s * a.n_cap + j] = sum;
       }
@@ -216,26 +266,26 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   }
 }
 
-template <typename T, int DI, int HI>
+template <typename T, int DI, int HI, bool KF8>
 hipError_t launch_mt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   const int mt = (a.q_per_req * a.idx_heads + 15) / 16;
   switch (mt) {
-    case 1: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 1, HI>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 2, HI>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 3, HI>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 4, HI>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 1, HI, KF8>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 2, HI, KF8>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 3, HI, KF8>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 4, HI, KF8>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T, int DI>
+template <typename T, int DI, bool KF8 = false>
 hipError_t launch_hi(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   switch (a.idx_heads) {
-    case 4: return launch_mt<T, DI, 4>(a, grid, st);
-    case 8: return launch_mt<T, DI, 8>(a, grid, st);
-    case 16: return launch_mt<T, DI, 16>(a, grid, st);
-    default: return launch_mt<T, DI, 0>(a, grid, st);
+    case 4: return launch_mt<T, DI, 4, KF8>(a, grid, st);
+    case 8: return launch_mt<T, DI, 8, KF8>(a, grid, st);
+    case 16: return launch_mt<T, DI, 16, KF8>(a, grid, st);
+    default: return launch_mt<T, DI, 0, KF8>(a, grid, st);
   }
 }
 
@@ -245,6 +295,9 @@ hipError_t launch_indexer_score(const ScoreArgs& a, hipStream_t st) {
   const int n_bound = std::min(a.n_cap, a.max_len / a.ratio);
   if (n_bound <= a.topk) return hipSuccess;  // every token fits Top-K: nothing to score
   dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch);
+  if (a.k_scale) {  // FP8 key cache, bf16 queries (checked by the caller)
+    return a.idx_dim == 128 ? launch_hi<__bf16, 128, true>(a, grid, st) : launch_hi<__bf16, 64, true>(a, grid, st);
+  }
   if (a.dtype == 1) {
     return a.idx_dim == 128 ? launch_hi<__bf16, 128>(a, grid, st) : launch_hi<__bf16, 64>(a, grid, st);
   }

@@ -12,10 +12,11 @@ namespace csa {
 struct ScoreArgs {
   const void* q_idx;        // [B][S][Hi][Di]
   const float* w;           // [B][S][Hi]
-  const void* k_idx;        // [B][n_cap][Di]
+  const void* k_idx;        // [B][n_cap][Di] in dtype, or E4M3 codes when k_scale is set
   const int32_t* start_pos; // [B]
   float* scores;            // [B][S][n_cap]
   int batch, q_per_req, idx_heads, idx_dim, n_cap, topk, ratio, max_len, dtype;
+  const float* k_scale;     // [B][n_cap] per-row scale of an FP8 key cache, else null
 };
 
 struct TopkArgs {

@@ -23,16 +23,36 @@ def score_error_bound(shape, inp, tok_rows):
     or rounded fp32 products; then relu, one product with w and Hi-1 additions
     in fp32, plus the oracle's own final rounding.  With u = 2^-24 the error of
     any summation order is at most (Di + Hi + 3) u sum_h w_h sum_c |q_hc k_jc|.
+    With an FP8 key cache (inp holds k_idx8 / k_scale) the keys are the
+    dequantised values, and the per-row scale applied to the head sum is one
+    more rounding: (Di + Hi + 4).
     """
     dt = shape.dtype
     q = np.abs(I.as_float(inp["q_idx"], dt).astype(np.float64))
-    k = np.abs(I.as_float(inp["k_idx"], dt).astype(np.float64))
     w = inp["w"].astype(np.float64)
+    fp8 = "k_idx8" in inp
+    terms = shape.idx_dim + shape.idx_heads + (4 if fp8 else 3)
     bound = {}
     for (b, s, n) in tok_rows:
-        mag = np.einsum("h,hc,jc->j", w[b, s], q[b, s], k[b, :n])
-        bound[(b, s)] = (shape.idx_dim + shape.idx_heads + 3) * U32 * mag
+        if fp8:
+            k = np.abs(e4m3_values(inp["k_idx8"][b, :n])) * inp["k_scale"][b, :n, None].astype(np.float64)
+        else:
+            k = np.abs(I.as_float(inp["k_idx"][b, :n], dt).astype(np.float64))
+        mag = np.einsum("h,hc,jc->j", w[b, s], q[b, s], k)
+        bound[(b, s)] = terms * U32 * mag
     return bound
+
+
+_E4M3 = None
+
+
+def e4m3_values(codes):
+    """E4M3 code -> value through the oracle's (pinned) decoder."""
+    global _E4M3
+    if _E4M3 is None:
+        import oracle
+        _E4M3 = np.array([oracle.e4m3_value(c) for c in range(256)])
+    return _E4M3[np.asarray(codes, np.uint8)]
 
 
 def token_rows(shape, start_pos):

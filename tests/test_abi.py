@@ -86,6 +86,32 @@ def test_indexer_score_null_and_alignment():
     assert call_score(shape(), [FAKE, FAKE, MISALIGNED, FAKE, FAKE]) == 5
 
 
+def call_score_fp8(sh, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return C.lib().csa_indexer_score_fp8(None if sh is None else ctypes.byref(C.CShape.of(sh)),
+                                         *p, None)
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(dtype=I.F32), 3),          # bf16 queries only
+    (dict(dtype=5), 3),
+    (dict(idx_dim=96), 8),
+    (dict(q_per_req=8, idx_heads=16), 8),
+    (dict(n_cap=200), 4),
+    (dict(batch=-1), 2),
+])
+def test_indexer_score_fp8_refusals(case, code):
+    assert call_score_fp8(shape(**case)) == code
+
+
+def test_indexer_score_fp8_null_and_alignment():
+    assert call_score_fp8(None) == 1
+    assert call_score_fp8(shape(), [FAKE, FAKE, FAKE, None, FAKE, FAKE]) == 1   # k_scale
+    assert call_score_fp8(shape(), [FAKE, FAKE, None, FAKE, FAKE, FAKE]) == 1   # codes
+    assert call_score_fp8(shape(), [FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE]) == 5
+    assert call_score_fp8(shape(batch=0), [None] * 6) == 0  # empty problem
+
+
 @pytest.mark.parametrize("case,code", [
     (dict(n_cap=255), 4),
     (dict(win=0), 2),

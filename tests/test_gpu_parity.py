@@ -48,7 +48,11 @@ def gpu_step(shape, inp, supplied=False, topk_idx=None, scores=None, jobs=("scor
     if scores is not None:
         bufs["scores"].copy_(torch.from_numpy(scores))
     if "score" in jobs:
-        C.indexer_score(shape, d["q_idx"], d["w"], d["k_idx"], d["start_pos"], bufs["scores"])
+        if "k_idx8" in d:   # FP8 indexer key cache
+            C.indexer_score_fp8(shape, d["q_idx"], d["w"], d["k_idx8"], d["k_scale"], d["start_pos"],
+                                bufs["scores"])
+        else:
+            C.indexer_score(shape, d["q_idx"], d["w"], d["k_idx"], d["start_pos"], bufs["scores"])
     if "topk" in jobs:
         C.topk(shape, bufs["scores"], d["start_pos"], bufs["topk_idx"], bufs["topk_ws"])
     ti = bufs["topk_idx"]
@@ -88,6 +92,18 @@ def test_attention_matches_oracle(cid, config_inputs):
 # indexer scores
 # --------------------------------------------------------------------------
 
+def check_scores(sh, inp, got, ref):
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, inp, rows)
+    assert rows, "configuration scores nothing"
+    scored = np.zeros(got["scores"].shape, dtype=bool)
+    for (b, s, n) in rows:
+        err = np.abs(got["scores"][b, s, :n].astype(np.float64) - ref["scores"][b, s, :n])
+        assert np.all(err <= bound[(b, s)]), f"token {(b, s)}: score error above bound"
+        scored[b, s, :n] = True
+    assert np.isnan(got["scores"][~scored]).all(), "entries outside the scored set were written"
+
+
 @pytest.mark.parametrize("cid", [0, 3])
 def test_scores_match_oracle(cid, config_inputs):
     cfg = I.CONFIGS[cid]
@@ -120,6 +136,58 @@ def test_scores_exact_grid(S, Hi, Di):
     ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE)
     got = gpu_step(sh, inp, jobs=("score",))
     assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+
+
+# --------------------------------------------------------------------------
+# FP8 indexer key cache (E4M3 codes + per-row scale)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_scores_fp8_match_oracle(cid):
+    sh = I.CONFIGS[cid].shape
+    inp = I.make_inputs(cid, key_format="fp8")
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE)
+    got = gpu_step(sh, inp, jobs=("score",))
+    check_scores(sh, inp, got, ref)
+
+
+@pytest.mark.parametrize("S,Hi,Di", [(1, 4, 128), (2, 8, 128), (4, 8, 64), (8, 8, 128), (3, 5, 64),
+                                     (2, 16, 128)])
+def test_scores_fp8_exact_grid(S, Hi, Di):
+    # Keys on the dyadic grid are exact E4M3 codes; with power-of-two scales
+    # every partial sum is exact on both sides: bitwise equality.
+    cfg = small_cfg(q_per_req=S, idx_heads=Hi, idx_dim=Di, n_cap=600, topk=32, max_len=2400)
+    inp = I.make_inputs(cfg, key_format="fp8")
+    g = np.random.default_rng(S * 1000 + Hi * 10 + Di)
+    inp["q_idx"] = I.f32_to_bf16_bits((g.integers(-8, 9, inp["q_idx"].shape) / 4.0).astype(np.float32))
+    inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    live = inp["k_scale"] < 1.0   # rows quantised from N(0,1) keys; poisoned rows keep theirs
+    codes = I.f32_to_e4m3_bits((g.integers(-8, 9, inp["k_idx8"].shape) / 4.0).astype(np.float32))
+    inp["k_idx8"] = np.where(live[..., None], codes, inp["k_idx8"])
+    pow2 = np.exp2(g.integers(-1, 2, inp["k_scale"].shape)).astype(np.float32)
+    inp["k_scale"] = np.where(live, pow2, inp["k_scale"]).astype(np.float32)
+    sh = cfg.shape
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE)
+    got = gpu_step(sh, inp, jobs=("score",))
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+
+
+def test_end_to_end_fp8_keys():
+    # FP8 scoring, GPU Top-K and attention on the wide Top-K configuration
+    cid = 4
+    sh = I.CONFIGS[cid].shape
+    inp = I.make_inputs(cid, key_format="fp8")
+    ref = oracle_step(sh, inp)
+    got = gpu_step(sh, inp)
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, inp, rows)
+    exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
+                               inp["start_pos"])
+    print(f"fp8 config {cid}: {len(exempt)} boundary exemptions {exempt}")
+    assert len(exempt) <= max(1, sh.batch * sh.q_per_req // 32)
+    ex = {b * sh.q_per_req + s for (b, s, _) in exempt}
+    keep = [t for t in range(sh.batch * sh.q_per_req) if t not in ex]
+    U.compare_outputs(sh, got["out"], ref["out"], tokens=keep)
 
 
 # --------------------------------------------------------------------------
