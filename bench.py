@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--key-format", choices=("bf16", "fp8"), default="bf16",
+                    help="indexer key cache: bf16 rows, or FP8 E4M3 codes with a per-row scale")
     ap.add_argument("--query-sets", type=int, default=4,
                     help="query sets cycled over the steps (queries rolled along the batch), so "
                          "consecutive steps select different compressed rows")
@@ -62,16 +64,17 @@ def n_vis(p, ratio, n_cap):
     return min((p + 1) // ratio, n_cap)
 
 
-def score_bytes(sh, sp):
+def score_bytes(sh, sp, key_format="bf16"):
     """k_idx rows read once per request + scores written + q_idx + w."""
     es = 2 if sh.dtype == 1 else 4
+    key_row = sh.idx_dim + 4 if key_format == "fp8" else sh.idx_dim * es   # codes + scale
     total = 0
     for b in range(sh.batch):
         nv = [n_vis(int(sp[b]) + s, sh.ratio, sh.n_cap) for s in range(sh.q_per_req)]
         scored = [n for n in nv if n > sh.topk]
         if not scored:
             continue
-        total += max(scored) * sh.idx_dim * es          # keys, shared by the request's tokens
+        total += max(scored) * key_row                  # keys, shared by the request's tokens
         total += sum(scored) * 4                        # fp32 scores
         total += sh.q_per_req * sh.idx_heads * (sh.idx_dim * es + 4)
     return total
@@ -141,7 +144,8 @@ def main():
     cfg = I.CONFIGS[args.config]
     sh = cfg.shape
     t0 = time.time()
-    inp = I.make_inputs(args.config)
+    fp8 = args.key_format == "fp8"
+    inp = I.make_inputs(args.config, key_format=args.key_format)
     t_gen = time.time() - t0
     dev = C.to_device(inp, sh)
     bufs = C.alloc_outputs(sh)
@@ -171,8 +175,12 @@ def main():
         rec_attn = ev is not None and (mode == "all" or dominant == "sparse_attn")
         if not cfg.supplied_topk:
             if rec_score: ev[0].record(stream)
-            C.indexer_score(sh, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
-                            bufs["scores"], stream)
+            if fp8:
+                C.indexer_score_fp8(sh, dev["q_idx"], dev["w"], dev["k_idx8"], dev["k_scale"],
+                                    dev["start_pos"], bufs["scores"], stream)
+            else:
+                C.indexer_score(sh, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
+                                bufs["scores"], stream)
             if rec_score: ev[1].record(stream)
             C.topk(sh, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
             ti = bufs["topk_idx"]
@@ -189,7 +197,7 @@ def main():
     # of the first query set decide it; scoring moves far more on the long
     # configurations)
     sp = inp["start_pos"]
-    sb, sf = score_bytes(sh, sp), score_flops(sh, sp)
+    sb, sf = score_bytes(sh, sp, args.key_format), score_flops(sh, sp)
     run_step(r=0)
     torch.cuda.synchronize()
     ti0 = (bufs["topk_idx"] if not cfg.supplied_topk else dev["topk_idx"]).cpu().numpy()
@@ -251,7 +259,8 @@ def main():
     dom_bytes = sb if dominant == "indexer_score" else ab
     achieved = dom_bytes / t_dom / 1e9
     traffic = None
-    tfile = os.path.join(PROFILES, f"traffic_{dominant}_config{args.config}.json")
+    kf = "_fp8" if fp8 and dominant == "indexer_score" else ""
+    tfile = os.path.join(PROFILES, f"traffic_{dominant}{kf}_config{args.config}.json")
     if os.path.exists(tfile):
         tj = json.load(open(tfile))
         src = "indexer_score.hip" if dominant == "indexer_score" else "sparse_attn.hip"
@@ -298,7 +307,8 @@ def main():
                                f"WIN={sh.win} H={sh.heads} D={sh.head_dim} Dr={sh.rope_dim} "
                                f"Hi={sh.idx_heads} Di={sh.idx_dim} G={sh.out_groups}",
                    "batch": sh.batch, "q_per_req": sh.q_per_req, "topk": sh.topk,
-                   "max_len": sh.max_len, "query_sets": R, "parallelism": "single GPU"},
+                   "max_len": sh.max_len, "query_sets": R, "indexer_keys": args.key_format,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
