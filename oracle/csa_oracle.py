@@ -54,6 +54,10 @@ def _get():
         lib.oracle_round_bf16.restype = ctypes.c_float
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_run.restype = ctypes.c_int32
+        lib.oracle_swa_writeback.restype = None
+        lib.oracle_swa_writeback.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_value.argtypes = [ctypes.c_int32]
         lib.oracle_run.argtypes = ([ctypes.POINTER(_OShape)] + [ctypes.c_int32] * 4
@@ -75,6 +79,22 @@ def round_bf16(x: float) -> float:
 def e4m3_value(code: int) -> float:
     """Value of one OCP FP8 E4M3 code, as the oracle decodes it."""
     return float(_get().oracle_e4m3_value(int(code)))
+
+
+def swa_writeback(k_new: np.ndarray, v_new: np.ndarray, slot_mapping: np.ndarray,
+                  k_cache: np.ndarray, v_cache: np.ndarray) -> tuple:
+    """Copies of the caches after the writeback of rows k_new/v_new [T, D] to
+    rows slot_mapping[t] of the caches [n_slots, D] (slots outside the cache
+    are padding)."""
+    kn, vn = np.ascontiguousarray(k_new), np.ascontiguousarray(v_new)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    kc, vc = np.ascontiguousarray(k_cache).copy(), np.ascontiguousarray(v_cache).copy()
+    assert kn.shape == vn.shape and kc.shape == vc.shape and kn.shape[1] == kc.shape[1]
+    assert kn.dtype == kc.dtype and sm.shape == (kn.shape[0],)
+    _get().oracle_swa_writeback(kn.shape[0], kn.shape[1], kn.dtype.itemsize, kn.ctypes.data,
+                                vn.ctypes.data, sm.ctypes.data, kc.ctypes.data, vc.ctypes.data,
+                                kc.shape[0])
+    return kc, vc
 
 
 def select_row(scores: np.ndarray, k: int, n: Optional[int] = None) -> np.ndarray:

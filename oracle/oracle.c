@@ -396,6 +396,27 @@ int32_t oracle_run(const oracle_shape_t *sh, int32_t jobs, int32_t tok_begin,
   return rc;
 }
 
+/* ------------------------------------------------ window-cache writeback -- */
+
+/* Writeback of the step's new window entries: the K and V rows of each new
+ * token t (rows of k_new / v_new, elem_bytes per element, D elements) are
+ * copied to row slot[t] of k_cache / v_cache.  Every entry of the slot mapping
+ * is committed whatever the token count ("Perf: parallelize the DSpark TP-4
+ * SWA decode hot tasks", description, writeback item, and the review on the
+ * same page: a partial last tile must not be dropped).  A slot outside
+ * [0, n_slots) marks padding and is skipped.  Rows are copied bit for bit. */
+void oracle_swa_writeback(int32_t n_tokens, int32_t D, int32_t elem_bytes, const void *k_new,
+                          const void *v_new, const int32_t *slot, void *k_cache,
+                          void *v_cache, int64_t n_slots) {
+  const size_t row = (size_t)D * (size_t)elem_bytes;
+  for (int32_t t = 0; t < n_tokens; ++t) {
+    const int64_t dst = slot[t];
+    if (dst < 0 || dst >= n_slots) continue;
+    memcpy((char *)k_cache + (size_t)dst * row, (const char *)k_new + (size_t)t * row, row);
+    memcpy((char *)v_cache + (size_t)dst * row, (const char *)v_new + (size_t)t * row, row);
+  }
+}
+
 /* Helper for tests: round a double to bf16 exactly as the output step does. */
 float oracle_round_bf16(double x) { return round_bf16(x); }
 

@@ -356,6 +356,15 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
     return out
 
 
+def ring_slot_mapping(shape: Shape, start_pos: np.ndarray) -> np.ndarray:
+    """Slot mapping of the step's new tokens into the per-request window rings
+    viewed as one flat cache [B*w_cap][D]: token (b, s) at position
+    p = start_pos[b] + s goes to row b*w_cap + p mod w_cap.  Shape [B*S] int32."""
+    B, S, Wc = shape.batch, shape.q_per_req, shape.w_cap
+    p = np.asarray(start_pos, np.int64)[:, None] + np.arange(S)[None, :]
+    return (np.arange(B)[:, None] * Wc + p % Wc).reshape(-1).astype(np.int32)
+
+
 def softmax_scale(shape: Shape) -> float:
     """fp32(1/sqrt(D)), the scale every configuration uses."""
     return float(np.float32(1.0 / np.sqrt(shape.head_dim)))

@@ -295,6 +295,56 @@ def test_fp8_scale_is_per_row():
 
 
 # --------------------------------------------------------------------------
+# window-cache writeback by slot mapping
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 31, 33, 100, 257])
+@pytest.mark.parametrize("dtype", [np.uint16, np.float32])
+def test_writeback_vs_fancy_index(T, dtype):
+    # every entry is committed, whatever the token count (no tile multiple),
+    # and padding slots (negative or past the cache) are skipped
+    g = np.random.default_rng(T)
+    n_slots, D = 300, 64
+    cache = g.integers(0, 2 ** 15, size=(2, n_slots, D)).astype(dtype)
+    new = g.integers(0, 2 ** 15, size=(2, T, D)).astype(dtype)
+    slots = g.permutation(n_slots)[:T].astype(np.int32)
+    pad = g.random(T) < 0.2
+    slots[pad] = np.where(g.random(int(pad.sum())) < 0.5, -1, n_slots + 5)
+    kc, vc = oracle.swa_writeback(new[0], new[1], slots, cache[0], cache[1])
+    ref_k, ref_v = cache[0].copy(), cache[1].copy()
+    ok = ~pad
+    ref_k[slots[ok]] = new[0][ok]
+    ref_v[slots[ok]] = new[1][ok]
+    assert np.array_equal(kc, ref_k) and np.array_equal(vc, ref_v)
+
+
+def test_writeback_feeds_the_window_stream():
+    # Poison the ring slots of the step's new tokens, write the tokens back
+    # through the ring mapping: attention must equal attention on the
+    # original window bit for bit (writeback precedes attention).
+    sh = small_shape(dtype=I.BF16)
+    inp = small_inputs(sh)
+    ref = oracle.run(sh, inp)
+    B, S, Wc, D = sh.batch, sh.q_per_req, sh.w_cap, sh.head_dim
+    slots = I.ring_slot_mapping(sh, inp["start_pos"])
+    kflat = inp["k_win"].reshape(B * Wc, D)
+    vflat = inp["v_win"].reshape(B * Wc, D)
+    k_new, v_new = kflat[slots].copy(), vflat[slots].copy()
+    poisoned = dict(inp)
+    kp, vp = kflat.copy(), vflat.copy()
+    kp[slots] = I.f32_to_bf16_bits(np.float32([I.POISON]))[0]
+    vp[slots] = kp[slots]
+    kc, vc = oracle.swa_writeback(k_new, v_new, slots, kp, vp)
+    poisoned["k_win"], poisoned["v_win"] = kc.reshape(B, Wc, D), vc.reshape(B, Wc, D)
+    got = oracle.run(sh, poisoned, topk_idx=ref["topk_idx"], jobs=oracle.JOB_ATTN)
+    assert np.array_equal(got["out"], ref["out"])
+    # and without the writeback the poison is read
+    bad = oracle.run(sh, dict(poisoned, k_win=kp.reshape(B, Wc, D), v_win=vp.reshape(B, Wc, D)),
+                     topk_idx=ref["topk_idx"], jobs=oracle.JOB_ATTN)
+    assert not np.array_equal(bad["out"], ref["out"])
+
+
+# --------------------------------------------------------------------------
 # attention: library attention on the concatenated rows, closed forms
 # --------------------------------------------------------------------------
 
