@@ -10,6 +10,9 @@
  *   csa_sparse_attn_decode attend the raw window plus the picked rows, merge
  *                          the two softmax streams, undo RoPE, pack heads
  *
+ * and, before them, csa_swa_writeback, which commits the step's new window
+ * entries to the window cache.
+ *
  * The step is the one described on the pages "Perf: skip redundant CSA
  * scoring and fuse gather unpack" (description and changes table: scoring and
  * sorting skipped when the ratio-4 cache fits IDX_TOPK, causal visibility
@@ -203,6 +206,29 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* shape, const void* q, con
                                     const float* rope_cos, const float* rope_sin,
                                     int32_t rope_rows, float softmax_scale, void* out, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/* Window-cache writeback of the step's new tokens, by slot mapping.
+ *
+ * Copies the K and V rows of every new token t = b*S + s to row
+ * slot_mapping[t] of the caches, bit for bit; every entry is committed for any
+ * token count (the writeback of "Perf: parallelize the DSpark TP-4 SWA decode
+ * hot tasks", description, and its review: the tail of a partial tile must not
+ * be dropped).  A slot outside [0, n_slots) is padding and writes nothing.
+ * Two entries naming the same slot leave that row with either one.
+ * With the per-request rings of csa_sparse_attn_decode seen as one flat cache
+ * [B*w_cap][D], token (b, s) at position p belongs in row b*w_cap + p mod w_cap;
+ * writing it there before the attention call makes it part of its own window.
+ * Uses shape->batch, q_per_req, head_dim and dtype only.
+ *
+ *   k_new, v_new     [B*S][D]     dtype
+ *   slot_mapping     [B*S]        int32
+ *   k_cache, v_cache [n_slots][D] dtype, updated in place
+ * Requires D * element size to be a multiple of 16 bytes (else
+ * CSA_ERR_UNSUPPORTED).
+ */
+csa_status_t csa_swa_writeback(const csa_shape_t* shape, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                               int64_t n_slots, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* csa_status_string(csa_status_t status);

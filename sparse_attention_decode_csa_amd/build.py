@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip"]
+SOURCES = ["api.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip", "swa_writeback.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -6,8 +6,8 @@ raises if the library returns an error.  There is no CPU path: a missing
 library, a CPU tensor or a non-contiguous tensor is an error.
 
 Names match the C ABI: indexer_score, indexer_score_fp8, topk,
-sparse_attn_decode, plus the workspace queries and step(), which issues the
-three calls in order on one stream.
+sparse_attn_decode, swa_writeback, plus the workspace queries and step(),
+which issues the three calls in order on one stream.
 """
 from __future__ import annotations
 
@@ -31,8 +31,8 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL_PTR", 2: "CSA_ERR_BAD_SHAPE", 3: "CSA_ER
           7: "CSA_ERR_LAUNCH", 8: "CSA_ERR_UNSUPPORTED"}
 
 EXPORTS = ("csa_indexer_score", "csa_indexer_score_fp8", "csa_topk_workspace_bytes", "csa_topk",
-           "csa_sparse_attn_workspace_bytes", "csa_sparse_attn_decode", "csa_status_string",
-           "csa_abi_version")
+           "csa_sparse_attn_workspace_bytes", "csa_sparse_attn_decode", "csa_swa_writeback",
+           "csa_status_string", "csa_abi_version")
 
 
 class CShape(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.csa_sparse_attn_decode.restype = i32
         L.csa_sparse_attn_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
                                              vp, sz, vp]
+        L.csa_swa_writeback.restype = i32
+        L.csa_swa_writeback.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         L.csa_status_string.restype = ctypes.c_char_p
         L.csa_status_string.argtypes = [i32]
         L.csa_abi_version.restype = i32
@@ -158,6 +160,19 @@ def sparse_attn_decode(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos
         _dev(start_pos, "start_pos"), _dev(rope_cos, "rope_cos"), _dev(rope_sin, "rope_sin"),
         rope_rows, float(softmax_scale), _dev(out, "out"), _dev(ws, "ws"), nbytes,
         _stream(stream)))
+
+
+def swa_writeback(shape, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """k_new/v_new [B*S, D]; k_cache/v_cache [n_slots, D] (any leading shape
+    whose rows are D elements, e.g. the [B, w_cap, D] rings)."""
+    cs = CShape.of(shape)
+    if k_cache.numel() != v_cache.numel():
+        raise ValueError("k_cache and v_cache must hold the same number of rows")
+    n_slots = k_cache.numel() // shape.head_dim
+    _check("csa_swa_writeback", lib().csa_swa_writeback(
+        ctypes.byref(cs), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        n_slots, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

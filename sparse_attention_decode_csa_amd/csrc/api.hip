@@ -171,6 +171,25 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   return to_status(csa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
 
+csa_status_t csa_swa_writeback(const csa_shape_t* sh, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                               int64_t n_slots, void* stream) {
+  if (!sh) return CSA_ERR_NULL_PTR;
+  if (sh->dtype != CSA_DTYPE_F32 && sh->dtype != CSA_DTYPE_BF16) return CSA_ERR_BAD_DTYPE;
+  if (sh->batch < 0 || sh->q_per_req < 0 || sh->head_dim < 1 || n_slots < 0) return CSA_ERR_BAD_SHAPE;
+  if (sh->batch == 0 || sh->q_per_req == 0) return CSA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return CSA_ERR_NULL_PTR;
+  const int64_t row = (int64_t)sh->head_dim * (sh->dtype == CSA_DTYPE_BF16 ? 2 : 4);
+  const int64_t tokens = (int64_t)sh->batch * sh->q_per_req;
+  if (row % 16 != 0 || tokens * (row / 16) > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(slot_mapping) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return CSA_ERR_ALIGNMENT;
+  const csa::WritebackArgs a{k_new, v_new, slot_mapping, k_cache, v_cache, n_slots, (int)tokens, (int)row};
+  (void)hipGetLastError();
+  return to_status(csa::launch_swa_writeback(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* csa_status_string(csa_status_t s) {
   switch (s) {
     case CSA_OK: return "ok";

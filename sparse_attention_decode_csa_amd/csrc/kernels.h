@@ -45,6 +45,16 @@ struct AttnArgs {
   int chunks_per_wave, n_split_win, n_split_cmp;
 };
 
+struct WritebackArgs {
+  const void* k_new;           // [T][D] new rows (T = B*S)
+  const void* v_new;
+  const int32_t* slot_mapping; // [T] destination row, padding outside [0, n_slots)
+  void* k_cache;               // [n_slots][D]
+  void* v_cache;
+  int64_t n_slots;
+  int n_tokens, row_bytes;     // row_bytes: a multiple of 16
+};
+
 // Split plan of the attention kernel; a function of the shape only, so the
 // workspace query and the launch always agree.
 struct AttnPlan {
@@ -64,5 +74,6 @@ constexpr int64_t kMaxSliceBytes = 0x7FFFF000LL;
 hipError_t launch_indexer_score(const ScoreArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_swa_writeback(const WritebackArgs& a, hipStream_t stream);
 
 }  // namespace csa

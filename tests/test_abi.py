@@ -112,6 +112,32 @@ def test_indexer_score_fp8_null_and_alignment():
     assert call_score_fp8(shape(batch=0), [None] * 6) == 0  # empty problem
 
 
+def call_writeback(sh, ptrs=None, n_slots=100):
+    p = ptrs or [FAKE] * 5
+    return C.lib().csa_swa_writeback(None if sh is None else ctypes.byref(C.CShape.of(sh)),
+                                     *p, n_slots, None)
+
+
+@pytest.mark.parametrize("case,n_slots,code", [
+    (dict(dtype=5), 100, 3),
+    (dict(batch=-1), 100, 2),
+    (dict(head_dim=0), 100, 2),
+    (dict(), -1, 2),
+    (dict(head_dim=6), 100, 8),               # 12-byte bf16 rows: not whole 16-byte pieces
+    (dict(head_dim=6, dtype=I.F32), 100, 8),  # 24-byte rows
+])
+def test_writeback_refusals(case, n_slots, code):
+    assert call_writeback(shape(**case), n_slots=n_slots) == code
+
+
+def test_writeback_null_alignment_empty():
+    assert call_writeback(None) == 1
+    assert call_writeback(shape(), [FAKE, FAKE, None, FAKE, FAKE]) == 1
+    assert call_writeback(shape(), [FAKE, FAKE, FAKE, MISALIGNED, FAKE]) == 5
+    assert call_writeback(shape(q_per_req=0), [None] * 5) == 0
+    assert call_writeback(shape(head_dim=4, dtype=I.F32), [FAKE] * 4 + [MISALIGNED]) == 5
+
+
 @pytest.mark.parametrize("case,code", [
     (dict(n_cap=255), 4),
     (dict(win=0), 2),

@@ -191,6 +191,67 @@ def test_end_to_end_fp8_keys():
 
 
 # --------------------------------------------------------------------------
+# window-cache writeback
+# --------------------------------------------------------------------------
+
+def to_gpu(a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.cuda()
+
+
+@pytest.mark.parametrize("B,S,D,dt", [(1, 1, 128, I.BF16), (31, 1, 128, I.BF16), (11, 3, 64, I.BF16),
+                                      (257, 16, 128, I.BF16), (127, 1, 64, I.F32)])
+def test_writeback_matches_oracle(B, S, D, dt):
+    # token counts 1, 31, 33, 4112 and 127: no tile multiple; some slots padding
+    g = np.random.default_rng(B * 100 + S)
+    T, n_slots = B * S, B * S * 2 + 7
+    npdt = np.uint16 if dt == I.BF16 else np.float32
+    if dt == I.BF16:
+        cache = g.integers(0, 2 ** 16, size=(2, n_slots, D)).astype(np.uint16)
+        new = g.integers(0, 2 ** 16, size=(2, T, D)).astype(np.uint16)
+    else:
+        cache = g.standard_normal(size=(2, n_slots, D)).astype(npdt)
+        new = g.standard_normal(size=(2, T, D)).astype(npdt)
+    slots = g.permutation(n_slots)[:T].astype(np.int32)
+    pad = g.random(T) < 0.1
+    slots[pad] = np.where(g.random(int(pad.sum())) < 0.5, -3, n_slots)
+    ref_k, ref_v = oracle.swa_writeback(new[0], new[1], slots, cache[0], cache[1])
+    sh = small_cfg(batch=B, q_per_req=S, head_dim=D, dtype=dt).shape
+    kc, vc = to_gpu(cache[0]), to_gpu(cache[1])
+    C.swa_writeback(sh, to_gpu(new[0]), to_gpu(new[1]), to_gpu(slots), kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), ref_k) and np.array_equal(vc.cpu().numpy(), ref_v)
+
+
+def test_writeback_then_attention():
+    # the step's new window entries start poisoned in the rings; the GPU
+    # writeback through the ring mapping must restore the oracle's output
+    cfg = small_cfg(batch=4, q_per_req=3, win=48, w_cap=53, max_len=1024)
+    sh = cfg.shape
+    inp = I.make_inputs(cfg)
+    ref = oracle_step(sh, inp)
+    B, S, Wc, D = sh.batch, sh.q_per_req, sh.w_cap, sh.head_dim
+    slots = I.ring_slot_mapping(sh, inp["start_pos"])
+    kflat = inp["k_win"].reshape(B * Wc, D)
+    vflat = inp["v_win"].reshape(B * Wc, D)
+    k_new, v_new = kflat[slots].copy(), vflat[slots].copy()
+    poison = I.f32_to_bf16_bits(np.float32([I.POISON]))[0]
+    kp, vp = kflat.copy(), vflat.copy()
+    kp[slots] = poison
+    vp[slots] = poison
+    d = C.to_device(dict(inp, k_win=kp.reshape(B, Wc, D), v_win=vp.reshape(B, Wc, D)), sh)
+    bufs = C.alloc_outputs(sh)
+    C.swa_writeback(sh, C.to_device(dict(x=k_new), sh)["x"], C.to_device(dict(x=v_new), sh)["x"],
+                    to_gpu(slots), d["k_win"], d["v_win"])
+    ti = to_gpu(ref["topk_idx"])   # the oracle's lists: this checks the window alone
+    C.sparse_attn_decode(sh, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"], ti,
+                         d["start_pos"], d["rope_cos"], d["rope_sin"], I.softmax_scale(sh),
+                         bufs["out"], bufs["attn_ws"])
+    torch.cuda.synchronize()
+    U.compare_outputs(sh, bufs["out"].float().cpu().numpy(), ref["out"])
+
+
+# --------------------------------------------------------------------------
 # Top-K: bit-exact on the same scores
 # --------------------------------------------------------------------------
 
