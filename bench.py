@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--key-format", choices=("bf16", "fp8"), default="bf16",
                     help="indexer key cache: bf16 rows, or FP8 E4M3 codes with a per-row scale")
+    ap.add_argument("--writeback", action="store_true",
+                    help="start each step with the window-cache writeback of its new tokens")
     ap.add_argument("--query-sets", type=int, default=4,
                     help="query sets cycled over the steps (queries rolled along the batch), so "
                          "consecutive steps select different compressed rows")
@@ -165,11 +167,21 @@ def main():
             qs[name] = torch.roll(dev[name], shifts=r, dims=0).contiguous()
         qsets.append(qs)
 
+    # window writeback: the step's new rows (as the rings already hold them, so
+    # the write is idempotent) to their ring slots
+    if args.writeback:
+        B_, S_, Wc, D_ = sh.batch, sh.q_per_req, sh.w_cap, sh.head_dim
+        wb_slots = torch.from_numpy(I.ring_slot_mapping(sh, inp["start_pos"])).cuda()
+        k_new = dev["k_win"].reshape(B_ * Wc, D_)[wb_slots.long()].contiguous()
+        v_new = dev["v_win"].reshape(B_ * Wc, D_)[wb_slots.long()].contiguous()
+
     # ev: events recorded around the stages, on the launch stream.  "dom" records
     # only the two around the dominant kernel (the timed region keeps its
     # event packets to those); "all" records the four stage boundaries.
     def run_step(ev=None, r=0, mode="all"):
         dev = qsets[r % R]
+        if args.writeback:
+            C.swa_writeback(sh, k_new, v_new, wb_slots, dev["k_win"], dev["v_win"], stream)
         rec_all = ev is not None and mode == "all"
         rec_score = ev is not None and (mode == "all" or dominant == "indexer_score")
         rec_attn = ev is not None and (mode == "all" or dominant == "sparse_attn")
@@ -308,6 +320,7 @@ def main():
                                f"Hi={sh.idx_heads} Di={sh.idx_dim} G={sh.out_groups}",
                    "batch": sh.batch, "q_per_req": sh.q_per_req, "topk": sh.topk,
                    "max_len": sh.max_len, "query_sets": R, "indexer_keys": args.key_format,
+                   "window_writeback": bool(args.writeback),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
                      "achieved": round(achieved, 1),

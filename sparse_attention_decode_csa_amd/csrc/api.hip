@@ -48,13 +48,13 @@ csa_status_t csa_indexer_score(const csa_shape_t* sh, const void* q_idx, const f
   if (st != CSA_OK || empty) return st;
   if (!q_idx || !w || !k_idx || !start_pos || !scores) return CSA_ERR_NULL_PTR;
   if (sh->idx_dim != 64 && sh->idx_dim != 128) return CSA_ERR_UNSUPPORTED;
-  if ((int64_t)sh->q_per_req * sh->idx_heads > 64) return CSA_ERR_UNSUPPORTED;
+  if (sh->idx_heads > 64 || (sh->q_per_req + 63) / 64 > 65535) return CSA_ERR_UNSUPPORTED;
   if ((st = check_selection(sh)) != CSA_OK) return st;
   if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx) || !aligned16(start_pos) ||
       !aligned16(scores))
     return CSA_ERR_ALIGNMENT;
   csa::ScoreArgs a{q_idx, w, k_idx, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
-                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, nullptr};
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, nullptr, 0};
   (void)hipGetLastError();  // report only what these launches cause
   return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
 }
@@ -68,13 +68,13 @@ csa_status_t csa_indexer_score_fp8(const csa_shape_t* sh, const void* q_idx, con
   if (!q_idx || !w || !k_idx8 || !k_scale || !start_pos || !scores) return CSA_ERR_NULL_PTR;
   if (sh->dtype != CSA_DTYPE_BF16) return CSA_ERR_BAD_DTYPE;  // bf16 queries only
   if (sh->idx_dim != 64 && sh->idx_dim != 128) return CSA_ERR_UNSUPPORTED;
-  if ((int64_t)sh->q_per_req * sh->idx_heads > 64) return CSA_ERR_UNSUPPORTED;
+  if (sh->idx_heads > 64 || (sh->q_per_req + 63) / 64 > 65535) return CSA_ERR_UNSUPPORTED;
   if ((st = check_selection(sh)) != CSA_OK) return st;
   if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_idx8) || !aligned16(k_scale) ||
       !aligned16(start_pos) || !aligned16(scores))
     return CSA_ERR_ALIGNMENT;
   csa::ScoreArgs a{q_idx, w, k_idx8, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
-                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, k_scale};
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, k_scale, 0};
   (void)hipGetLastError();  // report only what these launches cause
   return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
 }

@@ -9,7 +9,10 @@
 // Design: the step streams k_idx once per request (every token of a request
 // shares it), so it is HBM-bound; the contraction runs on MFMA with the
 // request's S*Hi query rows as the M dimension (zero-padded to 16) and 16 keys
-// as N.  Key tiles stream HBM -> LDS by DMA in whole rows, several tiles in
+// as N.  A prefill chunk (many query tokens per request, the prefill indexer
+// of "Fix: port the DeepSeek-V4 MoE, hc_pre and prefill fixes to DSpark",
+// description) is cut into blocks of at most 64 query rows, a third grid
+// dimension; each block reads the keys its own tokens see, mostly from L2.  Key tiles stream HBM -> LDS by DMA in whole rows, several tiles in
 // flight per wave, and each lane reads its 16-byte MFMA operand pieces back
 // from LDS.  The per-head relu and weighted sum
 // runs in registers when the head count is 4, 8 or 16 (each lane's four
@@ -102,10 +105,14 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
-  const int S = a.q_per_req, Hi = a.idx_heads, SH = S * Hi;
-  const int sp = a.start_pos[b];
+  // This workgroup's tokens: s0 .. s0+S-1 of request b (one block of at most
+  // 64 query rows; a decode step is one block, a prefill chunk several).
+  const int s0 = blockIdx.z * a.tok_per_block;
+  const int S = min(a.q_per_req - s0, a.tok_per_block), Hi = a.idx_heads, SH = S * Hi;
+  const int sp = a.start_pos[b] + s0;      // position of the block's first token
+  const size_t tok0 = (size_t)b * a.q_per_req + s0;
 
-  // Rows scored for this request: the largest visible count among its tokens
+  // Rows scored for this block: the largest visible count among its tokens
   // that do not fit Top-K.
   int nmax = 0;
   for (int s = 0; s < S; ++s) {
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   // Nothing consumes these loads before the MFMAs, so no wait delays the DMAs.
   u32x4_t qa[MT][CH];
   float wv[MT][4];
-  const char* qbase = static_cast<const char*>(a.q_idx) + (size_t)b * SH * QROW;
+  const char* qbase = static_cast<const char*>(a.q_idx) + tok0 * Hi * QROW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int qr = mt * 16 + n16;
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = mt * 16 + 4 * g + i;   // result rows this lane holds
-      wv[mt][i] = a.w[(size_t)b * SH + min(row, SH - 1)];
+      wv[mt][i] = a.w[tok0 * Hi + min(row, SH - 1)];
     }
   }
   // Fast path: the token of tile mt's rows 4g..4g+3 and its visible count.
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
 #pragma unroll
   for (int t = 0; t < kScoreBufs && t < kScoreTilesPerWave; ++t) issue_tile(t);
 
-  float* srow = a.scores + (size_t)b * S * a.n_cap;
+  float* srow = a.scores + tok0 * a.n_cap;
 
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
 
 template <typename T, int DI, int HI, bool KF8>
 hipError_t launch_mt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
-  const int mt = (a.q_per_req * a.idx_heads + 15) / 16;
+  const int mt = (a.tok_per_block * a.idx_heads + 15) / 16;
   switch (mt) {
     case 1: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 1, HI, KF8>), grid, dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 2, HI, KF8>), grid, dim3(256), 0, st, a); break;
@@ -291,10 +298,16 @@ hipError_t launch_hi(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_indexer_score(const ScoreArgs& a, hipStream_t st) {
-  const int n_bound = std::min(a.n_cap, a.max_len / a.ratio);
-  if (n_bound <= a.topk) return hipSuccess;  // every token fits Top-K: nothing to score
-  dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch);
+hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
+  const int n_bound = std::min(in.n_cap, in.max_len / in.ratio);
+  if (n_bound <= in.topk) return hipSuccess;  // every token fits Top-K: nothing to score
+  // Query rows per workgroup: all of a request's when they fit in 64 (decode),
+  // else blocks of floor(64 / Hi) tokens (prefill chunks).
+  ScoreArgs a = in;
+  a.tok_per_block = a.q_per_req * a.idx_heads <= 64 ? a.q_per_req : 64 / a.idx_heads;
+  const int row_blocks = (a.q_per_req + a.tok_per_block - 1) / a.tok_per_block;
+  if (row_blocks > 65535) return hipErrorInvalidValue;
+  dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch, row_blocks);
   if (a.k_scale) {  // FP8 key cache, bf16 queries (checked by the caller)
     return a.idx_dim == 128 ? launch_hi<__bf16, 128, true>(a, grid, st) : launch_hi<__bf16, 64, true>(a, grid, st);
   }

@@ -17,6 +17,7 @@ struct ScoreArgs {
   float* scores;            // [B][S][n_cap]
   int batch, q_per_req, idx_heads, idx_dim, n_cap, topk, ratio, max_len, dtype;
   const float* k_scale;     // [B][n_cap] per-row scale of an FP8 key cache, else null
+  int tok_per_block;        // query tokens per workgroup (set by the launcher)
 };
 
 struct TopkArgs {

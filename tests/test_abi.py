@@ -72,7 +72,7 @@ def call_attn(sh, ptrs=None, rope_rows=1 << 20, ws_bytes=1 << 40, scale=0.1):
     (dict(topk=0), 2),
     (dict(topk=5000), 8),
     (dict(idx_dim=96), 8),
-    (dict(q_per_req=8, idx_heads=16), 8),
+    (dict(idx_heads=65), 8),
     (dict(n_cap=200), 4),            # floor(1024 / 4) = 256 rows needed
     (dict(max_len=0), 2),
 ])
@@ -96,7 +96,7 @@ def call_score_fp8(sh, ptrs=None):
     (dict(dtype=I.F32), 3),          # bf16 queries only
     (dict(dtype=5), 3),
     (dict(idx_dim=96), 8),
-    (dict(q_per_req=8, idx_heads=16), 8),
+    (dict(idx_heads=65), 8),
     (dict(n_cap=200), 4),
     (dict(batch=-1), 2),
 ])

@@ -191,6 +191,54 @@ def test_end_to_end_fp8_keys():
 
 
 # --------------------------------------------------------------------------
+# prefill indexer: many query tokens per request (q_per_req = chunk length)
+# --------------------------------------------------------------------------
+
+def prefill_cfg(T, K, Hi, start, B=2, grid=False):
+    max_len = start + T
+    cfg = small_cfg(name="prefill", batch=B, q_per_req=T, topk=K, idx_heads=Hi,
+                    n_cap=max(256, max_len // 4), win=64, w_cap=64 + T, heads=4,
+                    max_len=max_len)
+    inp = I.make_inputs(cfg, start_pos=np.full(B, start, np.int32))
+    if grid:   # dyadic grid: every partial sum exact on both sides
+        g = np.random.default_rng(T + K)
+        inp["q_idx"] = I.f32_to_bf16_bits((g.integers(-8, 9, inp["q_idx"].shape) / 4.0).astype(np.float32))
+        kg = I.f32_to_bf16_bits((g.integers(-8, 9, inp["k_idx"].shape) / 4.0).astype(np.float32))
+        inp["k_idx"] = np.where(inp["k_idx"] == I.f32_to_bf16_bits(np.float32([I.POISON]))[0],
+                                inp["k_idx"], kg)
+        inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    return cfg.shape, inp
+
+
+@pytest.mark.parametrize("T,K,Hi,start", [(512, 64, 8, 0), (1024, 256, 8, 3000), (300, 128, 5, 1000),
+                                          (2048, 1024, 4, 30000)])
+def test_prefill_indexer_topk(T, K, Hi, start):
+    # Each of the T tokens scores its own causally visible rows (widths well
+    # past 256) and selects its own Top-K; bypass tokens get bounded indices.
+    sh, inp = prefill_cfg(T, K, Hi, start)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    got = gpu_step(sh, inp, jobs=("score", "topk"))
+    check_scores(sh, inp, got, ref)
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, inp, rows)
+    exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
+                               inp["start_pos"])
+    print(f"prefill T={T}: {len(rows)} scored tokens, {len(exempt)} boundary exemptions")
+    assert len(exempt) <= max(1, len(rows) // 32)
+    # and the selection alone is bit-exact on the oracle's scores
+    got2 = gpu_step(sh, inp, scores=ref["scores"], jobs=("topk",))
+    assert np.array_equal(got2["topk_idx"], ref["topk_idx"])
+
+
+def test_prefill_indexer_exact_grid():
+    sh, inp = prefill_cfg(600, 256, 8, 1500, grid=True)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    got = gpu_step(sh, inp, jobs=("score", "topk"))
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+
+
+# --------------------------------------------------------------------------
 # window-cache writeback
 # --------------------------------------------------------------------------
 
