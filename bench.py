@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sparse_attention_decode_csa_amd", "csrc")
 
@@ -200,9 +201,10 @@ def main():
             if rec_all: ev[0].record(stream); ev[1].record(stream)
             ti = dev["topk_idx"]
         if rec_attn: ev[2].record(stream)
-        C.sparse_attn_decode(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
-                             ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], scale,
-                             bufs["out"], bufs["attn_ws"], stream)
+        if not cfg.indexer_only:
+            C.sparse_attn_decode(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
+                                 ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], scale,
+                                 bufs["out"], bufs["attn_ws"], stream)
         if rec_attn: ev[3].record(stream)
 
     # the dominant kernel: the larger algorithmic byte count (attention bytes
@@ -213,7 +215,8 @@ def main():
     run_step(r=0)
     torch.cuda.synchronize()
     ti0 = (bufs["topk_idx"] if not cfg.supplied_topk else dev["topk_idx"]).cpu().numpy()
-    dominant = "indexer_score" if sb >= attn_bytes(sh, sp, ti0)[0] else "sparse_attn"
+    dominant = ("indexer_score" if cfg.indexer_only or sb >= attn_bytes(sh, sp, ti0)[0]
+                else "sparse_attn")
 
     for k in range(args.warmup):
         run_step(r=k)
@@ -248,14 +251,14 @@ def main():
     tb = topk_bytes(sh, sp)
     # attention bytes depend on the selection: mean over the query sets
     abs_, rows_ = [], []
-    for r in range(R):
+    for r in (range(R) if not cfg.indexer_only else []):
         run_step(r=r)
         torch.cuda.synchronize()
         ti = (bufs["topk_idx"] if not cfg.supplied_topk else dev["topk_idx"]).cpu().numpy()
         a_, r_ = attn_bytes(sh, sp, ti)
         abs_.append(a_)
         rows_.append(r_)
-    ab, rows_att = float(np.mean(abs_)), int(np.mean(rows_))
+    ab, rows_att = (float(np.mean(abs_)), int(np.mean(rows_))) if abs_ else (0.0, 0)
     T = sh.batch * sh.q_per_req
 
     def stage(bytes_, t):
@@ -270,6 +273,13 @@ def main():
 
     dom_bytes = sb if dominant == "indexer_score" else ab
     achieved = dom_bytes / t_dom / 1e9
+    if cfg.indexer_only:
+        # a prefill chunk re-reads each request's few MB of keys from L2 for
+        # every block of query rows: the contraction, not HBM, bounds it
+        roofline = {"bound": "mfma", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
+                    "achieved": round(sf / t_dom / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(sf / t_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": None}
     traffic = None
     kf = "_fp8" if fp8 and dominant == "indexer_score" else ""
     tfile = os.path.join(PROFILES, f"traffic_{dominant}{kf}_config{args.config}.json")
@@ -284,17 +294,20 @@ def main():
     if not args.no_cpu_baseline:
         nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
         times = []
+        if cfg.indexer_only:   # scoring + Top-K of the chunk's first 1024 tokens
+            jobs, n_tok, what = oracle.JOB_SCORE | oracle.JOB_TOPK, min(T, 1024), "scoring + Top-K"
+        else:
+            jobs, n_tok, what = (oracle.JOB_ATTN if cfg.supplied_topk else 7), T, "the full step"
         for _ in range(max(1, args.cpu_reps)):
             t0 = time.perf_counter()
-            oracle.run(sh, inp, nthreads=nthreads,
-                       jobs=(oracle.JOB_ATTN if cfg.supplied_topk else 7))
+            oracle.run(sh, inp, nthreads=nthreads, jobs=jobs, tokens=(0, n_tok))
             times.append(time.perf_counter() - t0)
             if times[-1] > 60:
                 break
         tc = float(np.median(times))
-        cpu = {"value": round(T / tc, 2), "unit": "query-tokens/s", "cores": nthreads,
+        cpu = {"value": round(n_tok / tc, 2), "unit": "query-tokens/s", "cores": nthreads,
                "kind": "oracle",
-               "sample": f"the full step of this workload ({T} query tokens), median of "
+               "sample": f"{what} of {n_tok} of this workload's {T} query tokens, median of "
                          f"{len(times)} runs, {tc:.2f} s each, fp64 oracle"}
 
     if args.copy_calibration:
@@ -306,7 +319,9 @@ def main():
         torch.cuda.synchronize()
 
     line = {
-        "metric": "decode query-tokens/sec for CSA sparse attn step; achieved HBM GB/s vs peak",
+        "metric": ("prefill indexer query-tokens/sec (scoring + Top-K of a prefill chunk)"
+                   if cfg.indexer_only else
+                   "decode query-tokens/sec for CSA sparse attn step; achieved HBM GB/s vs peak"),
         "value": round(T / (ms_per_step * 1e-3), 1),
         "unit": "query-tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -322,7 +337,8 @@ def main():
                    "max_len": sh.max_len, "query_sets": R, "indexer_keys": args.key_format,
                    "window_writeback": bool(args.writeback),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
+        "roofline": roofline if cfg.indexer_only else
+                    {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -70,6 +70,7 @@ class Config:
     lengths: str          # how start_pos is drawn (documentation + dispatch key)
     structure: str        # extra structure planted into the indexer keys
     supplied_topk: bool   # True: the harness supplies topk_idx (attention only)
+    indexer_only: bool = False  # True: a prefill chunk measured for scoring + Top-K
 
 
 def _shape(**kw) -> Shape:
@@ -107,6 +108,14 @@ CONFIGS: Dict[int, Config] = {
                      heads=16, head_dim=128, rope_dim=64, idx_heads=8, idx_dim=128,
                      out_groups=1, max_len=131072, dtype=BF16),
         seed=4, lengths="fixed:131072", structure="dup:0.01", supplied_topk=False),
+    # A prefill chunk: the last 4096 tokens of a 32768-token context, each
+    # scoring its own causally visible compressed rows (7168 .. 8192).
+    5: Config(
+        name="prefill_chunk",
+        shape=_shape(batch=2, q_per_req=4096, ratio=4, n_cap=8192, topk=1024, win=128, w_cap=4224,
+                     heads=16, head_dim=128, rope_dim=64, idx_heads=8, idx_dim=128,
+                     out_groups=1, max_len=32768, dtype=BF16),
+        seed=5, lengths="fixed:32768", structure="none", supplied_topk=False, indexer_only=True),
 }
 
 
