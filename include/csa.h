@@ -97,6 +97,29 @@ typedef struct {
   int32_t dtype;      /* csa_dtype_t                                           */
 } csa_shape_t;
 
+/* Paged compressed caches.
+ *
+ * Instead of a dense [B][n_cap][...] buffer per request, a compressed cache
+ * may live in a pool of fixed-size blocks shared by all requests, located
+ * through a per-request block table (the cache pools with allocator slot
+ * mappings of "Fix: complete DeepSeek V4 TP CSA decode", description; the
+ * block-table form is this library's reading).  Logical row j of request b is
+ * pool row  block_table[b * blocks_per_req + j / block_size] * block_size
+ * + j % block_size.
+ *   block_table    [B][blocks_per_req] int32, device memory; entries that
+ *                  logical rows j < n_vis use must lie in [0, n_blocks)
+ *   blocks_per_req >= ceil(n_cap / block_size)
+ *   block_size     rows per block: a power of two, 16 .. 4096
+ *   n_blocks       blocks in the pool; a pool of K or V rows must stay below
+ *                  2^31 - 4096 bytes (CSA_ERR_UNSUPPORTED otherwise)
+ * The struct itself is host memory. */
+typedef struct {
+  const int32_t* block_table;
+  int32_t blocks_per_req;
+  int32_t block_size;
+  int64_t n_blocks;
+} csa_pages_t;
+
 /* Indexer scores of every visible compressed row.
  *
  * For each query token (b,s) that does not fit (n_vis(p) > K) and each
@@ -141,6 +164,22 @@ csa_status_t csa_indexer_score(const csa_shape_t* shape, const void* q_idx, cons
 csa_status_t csa_indexer_score_fp8(const csa_shape_t* shape, const void* q_idx, const float* w,
                                    const uint8_t* k_idx8, const float* k_scale,
                                    const int32_t* start_pos, float* scores, void* stream);
+
+/* csa_indexer_score / csa_indexer_score_fp8 over a paged indexer key cache.
+ *
+ *   k_pool   [n_blocks][block_size][Di]: keys in shape->dtype, or E4M3 codes
+ *            when k_scale is non-NULL
+ *   k_scale  NULL, or [n_blocks][block_size] float32 per-row scales (FP8 keys;
+ *            then shape->dtype must be CSA_DTYPE_BF16)
+ *   pages    the block table of the indexer key cache (see csa_pages_t)
+ * Every other argument, and the result, as csa_indexer_score.  Unmapped or
+ * out-of-range table entries for visible rows are outside the contract; the
+ * device clamps them into the pool so that no access leaves it.
+ */
+csa_status_t csa_indexer_score_paged(const csa_shape_t* shape, const void* q_idx, const float* w,
+                                     const void* k_pool, const float* k_scale,
+                                     const csa_pages_t* pages, const int32_t* start_pos,
+                                     float* scores, void* stream);
 
 /* Workspace bytes csa_topk needs for this shape (0 means none). */
 size_t csa_topk_workspace_bytes(const csa_shape_t* shape);
@@ -232,6 +271,25 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* shape, const void* q, con
 csa_status_t csa_swa_writeback(const csa_shape_t* shape, const void* k_new, const void* v_new,
                                const int32_t* slot_mapping, void* k_cache, void* v_cache,
                                int64_t n_slots, void* stream);
+
+/* csa_sparse_attn_decode with the compressed K and V caches paged.
+ *
+ *   k_pool, v_pool [n_blocks][block_size][D] dtype
+ *   pages          the block table of the compressed K/V cache (see
+ *                  csa_pages_t); entries reached by valid Top-K indices must
+ *                  lie in [0, n_blocks) (outside the contract otherwise; the
+ *                  device clamps them into the pool)
+ * The window cache stays a per-request ring (rows placed by
+ * csa_swa_writeback).  Every other argument, the workspace query and the
+ * result as csa_sparse_attn_decode.
+ */
+csa_status_t csa_sparse_attn_decode_paged(const csa_shape_t* shape, const void* q,
+                                          const void* k_win, const void* v_win, const void* k_pool,
+                                          const void* v_pool, const csa_pages_t* pages,
+                                          const int32_t* topk_idx, const int32_t* start_pos,
+                                          const float* rope_cos, const float* rope_sin,
+                                          int32_t rope_rows, float softmax_scale, void* out,
+                                          void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* csa_status_string(csa_status_t status);

@@ -5,4 +5,4 @@ may import this package.  The product path never does: it runs the HIP
 library or fails.
 """
 from .csa_oracle import (JOB_ATTN, JOB_SCORE, JOB_TOPK, build, e4m3_value, n_vis, round_bf16,  # noqa: F401
-                         run, select_row, swa_writeback)
+                         run, run_paged, select_row, swa_writeback, unpage)

@@ -107,6 +107,35 @@ def select_row(scores: np.ndarray, k: int, n: Optional[int] = None) -> np.ndarra
     return out
 
 
+def unpage(pool: np.ndarray, block_table: np.ndarray, block_size: int, n_cap: int) -> np.ndarray:
+    """Dense rows [B, n_cap, ...] of a paged cache: logical row j of request b
+    is pool row block_table[b, j // block_size] * block_size + j % block_size
+    (pool [n_blocks, block_size, ...])."""
+    table = np.asarray(block_table, dtype=np.int64)
+    j = np.arange(n_cap)
+    phys = table[:, j // block_size] * block_size + j % block_size      # [B, n_cap]
+    return pool.reshape(-1, *pool.shape[2:])[phys]
+
+
+def run_paged(shape, inp: dict, **kw) -> dict:
+    """The oracle on paged caches: the pools are first gathered to the dense
+    per-request layout through the block tables, then `run` computes as usual.
+    Paged names in `inp`: k_idx_pool (or k_idx8_pool + k_scale_pool) with
+    idx_table / idx_block_size, and k_cmp_pool + v_cmp_pool with cmp_table /
+    cmp_block_size."""
+    d = {k: v for k, v in inp.items() if not k.endswith(("_pool", "_table", "_block_size"))}
+    nc = shape.n_cap
+    if "k_idx_pool" in inp:
+        d["k_idx"] = unpage(inp["k_idx_pool"], inp["idx_table"], inp["idx_block_size"], nc)
+    if "k_idx8_pool" in inp:
+        d["k_idx8"] = unpage(inp["k_idx8_pool"], inp["idx_table"], inp["idx_block_size"], nc)
+        d["k_scale"] = unpage(inp["k_scale_pool"], inp["idx_table"], inp["idx_block_size"], nc)
+    if "k_cmp_pool" in inp:
+        d["k_cmp"] = unpage(inp["k_cmp_pool"], inp["cmp_table"], inp["cmp_block_size"], nc)
+        d["v_cmp"] = unpage(inp["v_cmp_pool"], inp["cmp_table"], inp["cmp_block_size"], nc)
+    return run(shape, d, **kw)
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data
 

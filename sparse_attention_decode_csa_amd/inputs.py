@@ -365,6 +365,36 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
     return out
 
 
+def page_cache(dense: np.ndarray, block_size: int, seed: int, spare_blocks: int = 3,
+               fill=None):
+    """Lay a dense per-request cache [B, n_cap, ...] out as a pool of blocks.
+
+    Returns (pool [n_blocks, block_size, ...], table [B, ceil(n_cap/block_size)]
+    int32): the blocks of all requests in a seeded random order, plus
+    `spare_blocks` blocks that no table entry names, filled with `fill` (the
+    poison value by default) so that a wrong mapping reads them.  Data layout
+    only: logical row j of request b is pool row
+    table[b, j // block_size] * block_size + j % block_size.
+    """
+    B, n_cap = dense.shape[:2]
+    bpr = -(-n_cap // block_size)
+    pad = bpr * block_size - n_cap
+    d = dense
+    if pad:
+        d = np.concatenate([dense, np.repeat(dense[:, -1:], pad, axis=1)], axis=1)
+    blocks = d.reshape(B * bpr, block_size, *dense.shape[2:])
+    n_blocks = B * bpr + spare_blocks
+    g = np.random.default_rng([seed, 555])
+    perm = g.permutation(n_blocks)
+    pool = np.empty((n_blocks, block_size) + dense.shape[2:], dtype=dense.dtype)
+    if fill is None:
+        fill = f32_to_bf16_bits(np.float32([POISON]))[0] if dense.dtype == np.uint16 else POISON
+    pool[perm[B * bpr:]] = fill
+    pool[perm[:B * bpr]] = blocks
+    table = perm[:B * bpr].reshape(B, bpr).astype(np.int32)
+    return pool, table
+
+
 def ring_slot_mapping(shape: Shape, start_pos: np.ndarray) -> np.ndarray:
     """Slot mapping of the step's new tokens into the per-request window rings
     viewed as one flat cache [B*w_cap][D]: token (b, s) at position

@@ -345,6 +345,40 @@ def test_writeback_feeds_the_window_stream():
 
 
 # --------------------------------------------------------------------------
+# paged compressed caches
+# --------------------------------------------------------------------------
+
+def test_unpage_hand_worked():
+    # block size 2, 4 rows per request, a table worked out by hand:
+    # request 0: rows 0,1 -> block 3 (pool rows 6,7); rows 2,3 -> block 0 (0,1)
+    # request 1: rows 0,1 -> block 1 (pool rows 2,3); rows 2,3 -> block 2 (4,5)
+    pool = np.arange(8 * 3, dtype=np.float32).reshape(4, 2, 3)   # pool row r holds 3r, 3r+1, 3r+2
+    flat = pool.reshape(8, 3)
+    table = np.array([[3, 0], [1, 2]], np.int32)
+    got = oracle.unpage(pool, table, 2, 4)
+    assert np.array_equal(got[0], flat[[6, 7, 0, 1]])
+    assert np.array_equal(got[1], flat[[2, 3, 4, 5]])
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_paged_oracle_equals_dense(bs):
+    # paging the caches with a random block order (plus poisoned spare blocks)
+    # changes no score, list or output of the step
+    sh = small_shape(dtype=I.BF16, topk=8, n_cap=64)
+    inp = small_inputs(sh)
+    ref = oracle.run(sh, inp)
+    paged = {k: v for k, v in inp.items() if k not in ("k_idx", "k_cmp", "v_cmp")}
+    paged["k_idx_pool"], paged["idx_table"] = I.page_cache(inp["k_idx"], bs, seed=1)
+    paged["idx_block_size"] = bs
+    paged["k_cmp_pool"], paged["cmp_table"] = I.page_cache(inp["k_cmp"], bs, seed=2)
+    paged["v_cmp_pool"], _ = I.page_cache(inp["v_cmp"], bs, seed=2)
+    paged["cmp_block_size"] = bs
+    got = oracle.run_paged(sh, paged)
+    for k in ("scores", "topk_idx", "out"):
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+
+
+# --------------------------------------------------------------------------
 # attention: library attention on the concatenated rows, closed forms
 # --------------------------------------------------------------------------
 
