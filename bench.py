@@ -44,6 +44,9 @@ def parse():
                     help="indexer key cache: bf16 rows, or FP8 E4M3 codes with a per-row scale")
     ap.add_argument("--writeback", action="store_true",
                     help="start each step with the window-cache writeback of its new tokens")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="lay the indexer key cache and the compressed K/V cache out as pools of "
+                         "BLOCK-row blocks in a seeded random order, read through block tables")
     ap.add_argument("--query-sets", type=int, default=4,
                     help="query sets cycled over the steps (queries rolled along the batch), so "
                          "consecutive steps select different compressed rows")
@@ -150,7 +153,8 @@ def main():
     fp8 = args.key_format == "fp8"
     inp = I.make_inputs(args.config, key_format=args.key_format)
     t_gen = time.time() - t0
-    dev = C.to_device(inp, sh)
+    paged = args.paged > 0
+    dev = C.to_device(I.page_inputs(inp, args.paged, seed=11) if paged else inp, sh)
     bufs = C.alloc_outputs(sh)
     scale = I.softmax_scale(sh)
     stream = torch.cuda.current_stream()
@@ -188,7 +192,12 @@ def main():
         rec_attn = ev is not None and (mode == "all" or dominant == "sparse_attn")
         if not cfg.supplied_topk:
             if rec_score: ev[0].record(stream)
-            if fp8:
+            if paged:
+                C.indexer_score_paged(sh, dev["q_idx"], dev["w"],
+                                      dev["k_idx8_pool"] if fp8 else dev["k_idx_pool"],
+                                      dev["k_scale_pool"] if fp8 else None, dev["idx_table"],
+                                      dev["start_pos"], bufs["scores"], stream)
+            elif fp8:
                 C.indexer_score_fp8(sh, dev["q_idx"], dev["w"], dev["k_idx8"], dev["k_scale"],
                                     dev["start_pos"], bufs["scores"], stream)
             else:
@@ -201,7 +210,12 @@ def main():
             if rec_all: ev[0].record(stream); ev[1].record(stream)
             ti = dev["topk_idx"]
         if rec_attn: ev[2].record(stream)
-        if not cfg.indexer_only:
+        if not cfg.indexer_only and paged:
+            C.sparse_attn_decode_paged(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp_pool"],
+                                       dev["v_cmp_pool"], dev["cmp_table"], ti, dev["start_pos"],
+                                       dev["rope_cos"], dev["rope_sin"], scale, bufs["out"],
+                                       bufs["attn_ws"], stream)
+        elif not cfg.indexer_only:
             C.sparse_attn_decode(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
                                  ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], scale,
                                  bufs["out"], bufs["attn_ws"], stream)
@@ -281,7 +295,7 @@ def main():
                     "unit": "TFLOP/s", "frac": round(sf / t_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                     "traffic": None}
     traffic = None
-    kf = "_fp8" if fp8 and dominant == "indexer_score" else ""
+    kf = ("_fp8" if fp8 and dominant == "indexer_score" else "") + ("_paged" if paged else "")
     tfile = os.path.join(PROFILES, f"traffic_{dominant}{kf}_config{args.config}.json")
     if os.path.exists(tfile):
         tj = json.load(open(tfile))
@@ -336,6 +350,7 @@ def main():
                    "batch": sh.batch, "q_per_req": sh.q_per_req, "topk": sh.topk,
                    "max_len": sh.max_len, "query_sets": R, "indexer_keys": args.key_format,
                    "window_writeback": bool(args.writeback),
+                   "paged_block_rows": args.paged or None,
                    "parallelism": "single GPU"},
         "roofline": roofline if cfg.indexer_only else
                     {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),

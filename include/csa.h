@@ -106,13 +106,17 @@ typedef struct {
  * block-table form is this library's reading).  Logical row j of request b is
  * pool row  block_table[b * blocks_per_req + j / block_size] * block_size
  * + j % block_size.
- *   block_table    [B][blocks_per_req] int32, device memory; entries that
- *                  logical rows j < n_vis use must lie in [0, n_blocks)
- *   blocks_per_req >= ceil(n_cap / block_size)
+ *   block_table    [B][blocks_per_req] int32, device memory, 16-byte aligned
+ *                  (CSA_ERR_ALIGNMENT otherwise); entries that logical rows
+ *                  j < n_vis use must lie in [0, n_blocks)
+ *   blocks_per_req >= ceil(n_cap / block_size) (CSA_ERR_CAPACITY otherwise)
  *   block_size     rows per block: a power of two, 16 .. 4096
- *   n_blocks       blocks in the pool; a pool of K or V rows must stay below
+ *                  (CSA_ERR_BAD_SHAPE otherwise)
+ *   n_blocks       blocks in the pool, >= 1; n_blocks * block_size must fit
+ *                  int32, and a pool of attention K or V rows must stay below
  *                  2^31 - 4096 bytes (CSA_ERR_UNSUPPORTED otherwise)
- * The struct itself is host memory. */
+ * The struct itself is host memory, read during the call only; a NULL
+ * struct or table is CSA_ERR_NULL_PTR. */
 typedef struct {
   const int32_t* block_table;
   int32_t blocks_per_req;

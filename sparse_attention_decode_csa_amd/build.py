@@ -50,6 +50,14 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A shared library links with undefined symbols; every symbol of the
+    # library's own namespace must be defined inside it (a missing kernel
+    # stub would otherwise surface only when the library is loaded).
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "_ZN3csa" in ln]
+    if r.returncode != 0 or missing:
+        os.remove(tmp)
+        raise RuntimeError(f"{out}: undefined library symbols {missing[:4]} ({len(missing)})")
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")

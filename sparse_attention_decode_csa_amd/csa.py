@@ -5,9 +5,10 @@ device pointers and sizes through the C ABI declared in include/csa.h and
 raises if the library returns an error.  There is no CPU path: a missing
 library, a CPU tensor or a non-contiguous tensor is an error.
 
-Names match the C ABI: indexer_score, indexer_score_fp8, topk,
-sparse_attn_decode, swa_writeback, plus the workspace queries and step(),
-which issues the three calls in order on one stream.
+Names match the C ABI: indexer_score, indexer_score_fp8,
+indexer_score_paged, topk, sparse_attn_decode, sparse_attn_decode_paged,
+swa_writeback, plus the workspace queries and step(), which issues the three
+calls in order on one stream.
 """
 from __future__ import annotations
 
@@ -30,8 +31,9 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL_PTR", 2: "CSA_ERR_BAD_SHAPE", 3: "CSA_ER
           4: "CSA_ERR_CAPACITY", 5: "CSA_ERR_ALIGNMENT", 6: "CSA_ERR_WORKSPACE",
           7: "CSA_ERR_LAUNCH", 8: "CSA_ERR_UNSUPPORTED"}
 
-EXPORTS = ("csa_indexer_score", "csa_indexer_score_fp8", "csa_topk_workspace_bytes", "csa_topk",
-           "csa_sparse_attn_workspace_bytes", "csa_sparse_attn_decode", "csa_swa_writeback",
+EXPORTS = ("csa_indexer_score", "csa_indexer_score_fp8", "csa_indexer_score_paged",
+           "csa_topk_workspace_bytes", "csa_topk", "csa_sparse_attn_workspace_bytes",
+           "csa_sparse_attn_decode", "csa_sparse_attn_decode_paged", "csa_swa_writeback",
            "csa_status_string", "csa_abi_version")
 
 
@@ -42,6 +44,12 @@ class CShape(ctypes.Structure):
     @classmethod
     def of(cls, shape) -> "CShape":
         return cls(*[int(getattr(shape, f)) for f in _FIELDS])
+
+
+class CPages(ctypes.Structure):
+    """Mirror of csa_pages_t."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("blocks_per_req", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("n_blocks", ctypes.c_int64)]
 
 
 class CsaError(RuntimeError):
@@ -67,6 +75,12 @@ def lib() -> ctypes.CDLL:
         L.csa_indexer_score.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.csa_indexer_score_fp8.restype = i32
         L.csa_indexer_score_fp8.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+        pp = ctypes.POINTER(CPages)
+        L.csa_indexer_score_paged.restype = i32
+        L.csa_indexer_score_paged.argtypes = [sp, vp, vp, vp, vp, pp, vp, vp, vp]
+        L.csa_sparse_attn_decode_paged.restype = i32
+        L.csa_sparse_attn_decode_paged.argtypes = [sp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, i32,
+                                                   f32, vp, vp, sz, vp]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk_workspace_bytes.argtypes = [sp]
         L.csa_topk.restype = i32
@@ -141,6 +155,26 @@ def indexer_score_fp8(shape, q_idx, w, k_idx8, k_scale, start_pos, scores, strea
         _stream(stream)))
 
 
+def _pages(pool, block_table, name: str) -> CPages:
+    """csa_pages_t of a pool [n_blocks, block_size, ...] and its table [B, blocks_per_req]."""
+    if pool.dim() < 2 or block_table.dim() != 2 or block_table.dtype != torch.int32:
+        raise ValueError(f"{name}: pool [n_blocks, block_size, ...] and int32 table [B, bpr] expected")
+    return CPages(_dev(block_table, name + " block_table"), int(block_table.shape[1]),
+                  int(pool.shape[1]), int(pool.shape[0]))
+
+
+def indexer_score_paged(shape, q_idx, w, k_pool, k_scale, block_table, start_pos, scores,
+                        stream=None) -> None:
+    """k_pool [n_blocks, block_size, Di] (shape.dtype keys, or uint8 E4M3 codes
+    with k_scale [n_blocks, block_size] float32); block_table [B, bpr] int32."""
+    cs = CShape.of(shape)
+    pg = _pages(k_pool, block_table, "k_pool")
+    _check("csa_indexer_score_paged", lib().csa_indexer_score_paged(
+        ctypes.byref(cs), _dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_pool, "k_pool"),
+        _dev(k_scale, "k_scale"), ctypes.byref(pg), _dev(start_pos, "start_pos"),
+        _dev(scores, "scores"), _stream(stream)))
+
+
 def topk(shape, scores, start_pos, topk_idx, ws=None, stream=None) -> None:
     cs = CShape.of(shape)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -162,6 +196,24 @@ def sparse_attn_decode(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos
         _stream(stream)))
 
 
+def sparse_attn_decode_paged(shape, q, k_win, v_win, k_pool, v_pool, block_table, topk_idx,
+                             start_pos, rope_cos, rope_sin, softmax_scale, out, ws,
+                             stream=None) -> None:
+    """k_pool/v_pool [n_blocks, block_size, D] sharing block_table [B, bpr] int32."""
+    cs = CShape.of(shape)
+    if k_pool.shape != v_pool.shape:
+        raise ValueError("k_pool and v_pool must have the same shape")
+    pg = _pages(k_pool, block_table, "k_pool")
+    rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa_sparse_attn_decode_paged", lib().csa_sparse_attn_decode_paged(
+        ctypes.byref(cs), _dev(q, "q"), _dev(k_win, "k_win"), _dev(v_win, "v_win"),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ctypes.byref(pg),
+        _dev(topk_idx, "topk_idx"), _dev(start_pos, "start_pos"), _dev(rope_cos, "rope_cos"),
+        _dev(rope_sin, "rope_sin"), rope_rows, float(softmax_scale), _dev(out, "out"),
+        _dev(ws, "ws"), nbytes, _stream(stream)))
+
+
 def swa_writeback(shape, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """k_new/v_new [B*S, D]; k_cache/v_cache [n_slots, D] (any leading shape
     whose rows are D elements, e.g. the [B, w_cap, D] rings)."""
@@ -180,9 +232,12 @@ def swa_writeback(shape, k_new, v_new, slot_mapping, k_cache, v_cache, stream=No
 # ----------------------------------------------------------------------------
 
 def to_device(inp: dict, shape, device="cuda") -> dict:
-    """Upload a seeded input dict: bf16 bit patterns become torch.bfloat16."""
+    """Upload a seeded input dict: bf16 bit patterns become torch.bfloat16;
+    plain numbers (block sizes) are left out."""
     out = {}
     for k, v in inp.items():
+        if not isinstance(v, np.ndarray):
+            continue
         if v.dtype == np.uint16:
             t = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16)
         else:
@@ -214,7 +269,13 @@ def step(shape, dev: dict, bufs: dict, softmax_scale: float, stream=None,
     if supplied_topk:
         ti = dev["topk_idx"]
     else:
-        if "k_idx8" in dev:   # FP8 indexer key cache
+        if "idx_table" in dev:   # paged indexer key cache (bf16/f32 keys or FP8 codes)
+            fp8 = "k_idx8_pool" in dev
+            indexer_score_paged(shape, dev["q_idx"], dev["w"],
+                                dev["k_idx8_pool"] if fp8 else dev["k_idx_pool"],
+                                dev["k_scale_pool"] if fp8 else None, dev["idx_table"],
+                                dev["start_pos"], bufs["scores"], stream)
+        elif "k_idx8" in dev:   # FP8 indexer key cache
             indexer_score_fp8(shape, dev["q_idx"], dev["w"], dev["k_idx8"], dev["k_scale"],
                               dev["start_pos"], bufs["scores"], stream)
         else:
@@ -222,6 +283,12 @@ def step(shape, dev: dict, bufs: dict, softmax_scale: float, stream=None,
                           bufs["scores"], stream)
         topk(shape, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
         ti = bufs["topk_idx"]
+    if "cmp_table" in dev:   # paged compressed K/V cache
+        sparse_attn_decode_paged(shape, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp_pool"],
+                                 dev["v_cmp_pool"], dev["cmp_table"], ti, dev["start_pos"],
+                                 dev["rope_cos"], dev["rope_sin"], softmax_scale, bufs["out"],
+                                 bufs["attn_ws"], stream)
+        return
     sparse_attn_decode(shape, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
                        ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], softmax_scale,
                        bufs["out"], bufs["attn_ws"], stream)

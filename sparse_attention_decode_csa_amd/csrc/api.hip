@@ -36,6 +36,24 @@ csa_status_t check_selection(const csa_shape_t* sh) {
 
 csa_status_t to_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH; }
 
+// A block table and its pool: block size a power of two in [16, 4096], enough
+// blocks per request for n_cap rows, a pool whose row count fits int32 and
+// whose rows of row_bytes stay below max_pool_bytes.
+csa_status_t check_pages(const csa_shape_t* sh, const csa_pages_t* pg, int64_t row_bytes,
+                         int64_t max_pool_bytes, int* shift) {
+  if (!pg || !pg->block_table) return CSA_ERR_NULL_PTR;
+  const int32_t bs = pg->block_size;
+  if (bs < 16 || bs > 4096 || (bs & (bs - 1))) return CSA_ERR_BAD_SHAPE;
+  if (pg->n_blocks < 1 || pg->blocks_per_req < 1) return CSA_ERR_BAD_SHAPE;
+  if ((int64_t)pg->blocks_per_req * bs < sh->n_cap) return CSA_ERR_CAPACITY;
+  if (pg->n_blocks * bs > INT32_MAX || pg->n_blocks * bs * row_bytes > max_pool_bytes)
+    return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)sh->batch * pg->blocks_per_req > INT32_MAX) return CSA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(pg->block_table) & 15u) != 0) return CSA_ERR_ALIGNMENT;
+  *shift = __builtin_ctz((unsigned)bs);
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,7 +72,8 @@ csa_status_t csa_indexer_score(const csa_shape_t* sh, const void* q_idx, const f
       !aligned16(scores))
     return CSA_ERR_ALIGNMENT;
   csa::ScoreArgs a{q_idx, w, k_idx, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
-                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, nullptr, 0};
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, nullptr, 0,
+                   nullptr, 0, 0, 0};
   (void)hipGetLastError();  // report only what these launches cause
   return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
 }
@@ -74,7 +93,8 @@ csa_status_t csa_indexer_score_fp8(const csa_shape_t* sh, const void* q_idx, con
       !aligned16(start_pos) || !aligned16(scores))
     return CSA_ERR_ALIGNMENT;
   csa::ScoreArgs a{q_idx, w, k_idx8, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
-                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, k_scale, 0};
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, k_scale, 0,
+                   nullptr, 0, 0, 0};
   (void)hipGetLastError();  // report only what these launches cause
   return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
 }
@@ -106,12 +126,12 @@ size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* sh) {
   return csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk, sh->dtype).ws_bytes;
 }
 
-csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const void* k_win,
-                                    const void* v_win, const void* k_cmp, const void* v_cmp,
-                                    const int32_t* topk_idx, const int32_t* start_pos,
-                                    const float* rope_cos, const float* rope_sin,
-                                    int32_t rope_rows, float softmax_scale, void* out, void* ws,
-                                    size_t ws_bytes, void* stream) {
+static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void* k_win,
+                                const void* v_win, const void* k_cmp, const void* v_cmp,
+                                const int32_t* topk_idx, const int32_t* start_pos,
+                                const float* rope_cos, const float* rope_sin, int32_t rope_rows,
+                                float softmax_scale, void* out, void* ws, size_t ws_bytes,
+                                void* stream, const csa_pages_t* pages, int block_shift) {
   bool empty = false;
   csa_status_t st = check_common(sh, &empty);
   if (st != CSA_OK || empty) return st;
@@ -167,8 +187,24 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   a.chunks_per_wave = pl.chunks_per_wave;
   a.n_split_win = pl.n_split_win;
   a.n_split_cmp = pl.n_split_cmp;
+  if (pages) {
+    a.block_table = pages->block_table;
+    a.blocks_per_req = pages->blocks_per_req;
+    a.block_shift = block_shift;
+    a.n_blocks = pages->n_blocks;
+  }
   (void)hipGetLastError();
   return to_status(csa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const void* k_win,
+                                    const void* v_win, const void* k_cmp, const void* v_cmp,
+                                    const int32_t* topk_idx, const int32_t* start_pos,
+                                    const float* rope_cos, const float* rope_sin,
+                                    int32_t rope_rows, float softmax_scale, void* out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  return attn_decode(sh, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos, rope_cos, rope_sin,
+                     rope_rows, softmax_scale, out, ws, ws_bytes, stream, nullptr, 0);
 }
 
 csa_status_t csa_swa_writeback(const csa_shape_t* sh, const void* k_new, const void* v_new,
@@ -188,6 +224,49 @@ csa_status_t csa_swa_writeback(const csa_shape_t* sh, const void* k_new, const v
   const csa::WritebackArgs a{k_new, v_new, slot_mapping, k_cache, v_cache, n_slots, (int)tokens, (int)row};
   (void)hipGetLastError();
   return to_status(csa::launch_swa_writeback(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status_t csa_indexer_score_paged(const csa_shape_t* sh, const void* q_idx, const float* w,
+                                     const void* k_pool, const float* k_scale,
+                                     const csa_pages_t* pages, const int32_t* start_pos,
+                                     float* scores, void* stream) {
+  bool empty = false;
+  csa_status_t st = check_common(sh, &empty);
+  if (st != CSA_OK || empty) return st;
+  if (!q_idx || !w || !k_pool || !start_pos || !scores) return CSA_ERR_NULL_PTR;
+  if (k_scale && sh->dtype != CSA_DTYPE_BF16) return CSA_ERR_BAD_DTYPE;  // FP8 keys: bf16 queries
+  if (sh->idx_dim != 64 && sh->idx_dim != 128) return CSA_ERR_UNSUPPORTED;
+  if (sh->idx_heads > 64 || (sh->q_per_req + 63) / 64 > 65535) return CSA_ERR_UNSUPPORTED;
+  if ((st = check_selection(sh)) != CSA_OK) return st;
+  int shift = 0;
+  const int64_t row = k_scale ? sh->idx_dim : (int64_t)sh->idx_dim * (sh->dtype == CSA_DTYPE_BF16 ? 2 : 4);
+  if ((st = check_pages(sh, pages, row, INT64_MAX, &shift)) != CSA_OK) return st;
+  if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_pool) || !aligned16(start_pos) ||
+      !aligned16(scores) || (k_scale && !aligned16(k_scale)))
+    return CSA_ERR_ALIGNMENT;
+  csa::ScoreArgs a{q_idx, w, k_pool, start_pos, scores, sh->batch, sh->q_per_req, sh->idx_heads,
+                   sh->idx_dim, sh->n_cap, sh->topk, sh->ratio, sh->max_len, sh->dtype, k_scale, 0,
+                   pages->block_table, pages->blocks_per_req, shift, pages->n_blocks};
+  (void)hipGetLastError();
+  return to_status(csa::launch_indexer_score(a, static_cast<hipStream_t>(stream)));
+}
+
+csa_status_t csa_sparse_attn_decode_paged(const csa_shape_t* sh, const void* q,
+                                          const void* k_win, const void* v_win, const void* k_pool,
+                                          const void* v_pool, const csa_pages_t* pages,
+                                          const int32_t* topk_idx, const int32_t* start_pos,
+                                          const float* rope_cos, const float* rope_sin,
+                                          int32_t rope_rows, float softmax_scale, void* out,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  csa_status_t st = check_common(sh, &empty);
+  if (st != CSA_OK || empty) return st;
+  if (!pages) return CSA_ERR_NULL_PTR;
+  int shift = 0;
+  const int64_t row = (int64_t)sh->head_dim * (sh->dtype == CSA_DTYPE_BF16 ? 2 : 4);
+  if ((st = check_pages(sh, pages, row, csa::kMaxSliceBytes, &shift)) != CSA_OK) return st;
+  return attn_decode(sh, q, k_win, v_win, k_pool, v_pool, topk_idx, start_pos, rope_cos, rope_sin,
+                     rope_rows, softmax_scale, out, ws, ws_bytes, stream, pages, shift);
 }
 
 const char* csa_status_string(csa_status_t s) {

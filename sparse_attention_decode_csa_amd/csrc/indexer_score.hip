@@ -87,7 +87,12 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // bf16 exactly in registers, the bf16 query is unchanged, and the row's scale
 // multiplies its head sum (relu is positively homogeneous, so
 // scale * sum_h w_h relu(q_h . c) = sum_h w_h relu(q_h . (scale * c))).
-template <typename T, int DI, int MT, int HI, bool KF8>
+// PG: the key cache (and the FP8 scales) are pools of blocks located through
+// a per-request block table; the workgroup loads the table entries of its
+// 1024 keys once, one per lane, and each lane maps its logical row with a
+// cross-lane move (blocks are at least 16 rows, so a 16-row tile never
+// straddles two of them).
+template <typename T, int DI, int MT, int HI, bool KF8, bool PG>
 __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   constexpr int ES = sizeof(T);
   constexpr int QROW = DI * ES;              // bytes per query row
@@ -122,6 +127,32 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   const int key0 = blockIdx.x * kScoreKeysPerBlock;
   if (key0 >= nmax) return;  // whole workgroup: nothing visible in this chunk
 
+  // Row of the key cache (or scale array) holding logical row j of request b,
+  // where jt = min(first row of j's 16-row tile, nmax - 1) is wave-uniform.
+  // Dense: b * n_cap + j.  Paged: the workgroup's slice of the block table is
+  // held one entry per lane (logical block (key0 >> shift) + lane, clamped
+  // into the pool); blocks are at least 16 rows, so every row a tile loads
+  // (rows past nmax are clamped to nmax - 1 = jt) lies in jt's block, which
+  // one lane read gives.
+  int pblk = 0;
+  if constexpr (PG) {
+    const int lb = min((key0 >> a.block_shift) + lane, a.blocks_per_req - 1);
+    const int e = a.block_table[(size_t)b * a.blocks_per_req + lb];
+    pblk = (int)min((int64_t)max(e, 0), a.n_blocks - 1);
+  }
+  auto key_row = [&](int jt, int j) -> size_t {
+    if constexpr (PG) {
+      const int blk = __builtin_amdgcn_readlane(pblk, (jt >> a.block_shift) - (key0 >> a.block_shift));
+      return ((size_t)blk << a.block_shift) + (size_t)(j & ((1 << a.block_shift) - 1));
+    } else {
+      (void)jt;
+      return (size_t)b * a.n_cap + j;
+    }
+  };
+  // wave-uniform first row of tile t of this wave (clamped to a real row)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto tile_key0 = [&](int t) { return key0 + (t * kScoreWaves + wave_u) * 16; };
+
   // per-row scales of this lane's key in each tile (FP8 keys), loaded first:
   // every load issued before the tile DMAs is older than them, so the tile
   // waits below can count DMA instructions only
@@ -129,7 +160,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   if constexpr (KF8) {
 #pragma unroll
     for (int t = 0; t < kScoreTilesPerWave; ++t)
-      ks[t] = a.k_scale[(size_t)b * a.n_cap + min(key0 + (t * kScoreWaves + wave) * 16 + n16, nmax - 1)];
+      ks[t] = a.k_scale[key_row(min(tile_key0(t), nmax - 1), min(tile_key0(t) + n16, nmax - 1))];
   }
 
   // A operand: query row qr = mt*16 + n16 (token qr / Hi, head qr % Hi).
@@ -165,21 +196,22 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
     tok_of[mt] = s;
     nv_of[mt] = s < S ? min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap) : 0;
   }
-  const char* kbase = static_cast<const char*>(a.k_idx) + (size_t)b * a.n_cap * ROW;
-  // Tiles are interleaved over the 4 waves so that at each step the block
-  // reads 4 consecutive 16-row tiles.
-  auto tile_key0 = [&](int t) { return key0 + (t * kScoreWaves + wave) * 16; };
+  const char* kbase = static_cast<const char*>(a.k_idx);   // rows addressed by key_row()
+  // Tiles are interleaved over the 4 waves (tile_key0) so that at each step
+  // the block reads 4 consecutive 16-row tiles.
   auto issue_tile = [&](int t) {
-    const int k0 = tile_key0(t);
+    const int k0 = tile_key0(t), jt = min(k0, nmax - 1);
     char* dst = tiles[wave][t % kScoreBufs];
 #pragma unroll
     for (int k = 0; k < TL::NPT; ++k) {
       const int r = k * TL::RPI + lane / TL::NPR;            // tile row this lane fetches
       const int piece = (lane % TL::NPR) ^ (r % TL::NPR);
       const int j = min(k0 + r, nmax - 1);                   // clamp: a real row
-      __builtin_amdgcn_global_load_lds(kbase + (size_t)j * ROW + 16 * piece,
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * k), 16, 0,
-                                       kNonTemporal);
+      // (the address is formed outside the builtin's argument list: a lambda
+      // call inside it keeps the host pass from emitting the kernel's stub)
+      const char* src = kbase + key_row(jt, j) * ROW + 16 * piece;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * k),
+                                       16, 0, kNonTemporal);
     }
   };
   // the query loads above are older than every tile DMA, so waiting for them
@@ -273,27 +305,41 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   }
 }
 
-template <typename T, int DI, int HI, bool KF8>
+template <typename T, int DI, int HI, bool KF8, bool PG>
 hipError_t launch_mt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   const int mt = (a.tok_per_block * a.idx_heads + 15) / 16;
   switch (mt) {
-    case 1: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 1, HI, KF8>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 2, HI, KF8>), grid, dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 3, HI, KF8>), grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 4, HI, KF8>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 1, HI, KF8, PG>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 2, HI, KF8, PG>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 3, HI, KF8, PG>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((indexer_score_kernel<T, DI, 4, HI, KF8, PG>), grid, dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T, int DI, bool KF8 = false>
+template <typename T, int DI, bool KF8, bool PG>
 hipError_t launch_hi(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   switch (a.idx_heads) {
-    case 4: return launch_mt<T, DI, 4, KF8>(a, grid, st);
-    case 8: return launch_mt<T, DI, 8, KF8>(a, grid, st);
-    case 16: return launch_mt<T, DI, 16, KF8>(a, grid, st);
-    default: return launch_mt<T, DI, 0, KF8>(a, grid, st);
+    case 4: return launch_mt<T, DI, 4, KF8, PG>(a, grid, st);
+    case 8: return launch_mt<T, DI, 8, KF8, PG>(a, grid, st);
+    case 16: return launch_mt<T, DI, 16, KF8, PG>(a, grid, st);
+    default: return launch_mt<T, DI, 0, KF8, PG>(a, grid, st);
   }
+}
+
+template <bool PG>
+hipError_t launch_layout(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  if (a.k_scale) {  // FP8 key cache, bf16 queries (checked by the caller)
+    return a.idx_dim == 128 ? launch_hi<__bf16, 128, true, PG>(a, grid, st)
+                            : launch_hi<__bf16, 64, true, PG>(a, grid, st);
+  }
+  if (a.dtype == 1) {
+    return a.idx_dim == 128 ? launch_hi<__bf16, 128, false, PG>(a, grid, st)
+                            : launch_hi<__bf16, 64, false, PG>(a, grid, st);
+  }
+  return a.idx_dim == 128 ? launch_hi<float, 128, false, PG>(a, grid, st)
+                          : launch_hi<float, 64, false, PG>(a, grid, st);
 }
 
 }  // namespace
@@ -308,13 +354,7 @@ hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
   const int row_blocks = (a.q_per_req + a.tok_per_block - 1) / a.tok_per_block;
   if (row_blocks > 65535) return hipErrorInvalidValue;
   dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch, row_blocks);
-  if (a.k_scale) {  // FP8 key cache, bf16 queries (checked by the caller)
-    return a.idx_dim == 128 ? launch_hi<__bf16, 128, true>(a, grid, st) : launch_hi<__bf16, 64, true>(a, grid, st);
-  }
-  if (a.dtype == 1) {
-    return a.idx_dim == 128 ? launch_hi<__bf16, 128>(a, grid, st) : launch_hi<__bf16, 64>(a, grid, st);
-  }
-  return a.idx_dim == 128 ? launch_hi<float, 128>(a, grid, st) : launch_hi<float, 64>(a, grid, st);
+  return a.block_table ? launch_layout<true>(a, grid, st) : launch_layout<false>(a, grid, st);
 }
 
 }  // namespace csa

@@ -18,6 +18,12 @@ struct ScoreArgs {
   int batch, q_per_req, idx_heads, idx_dim, n_cap, topk, ratio, max_len, dtype;
   const float* k_scale;     // [B][n_cap] per-row scale of an FP8 key cache, else null
   int tok_per_block;        // query tokens per workgroup (set by the launcher)
+  // paged key cache (block_table non-null): k_idx / k_scale are pools of
+  // (1 << block_shift)-row blocks; logical row j of request b is pool row
+  // block_table[b * blocks_per_req + (j >> block_shift)] << block_shift | (j & mask)
+  const int32_t* block_table;
+  int blocks_per_req, block_shift;
+  int64_t n_blocks;
 };
 
 struct TopkArgs {
@@ -44,6 +50,11 @@ struct AttnArgs {
       max_len, dtype;
   float scale_log2;         // softmax_scale * log2(e)
   int chunks_per_wave, n_split_win, n_split_cmp;
+  // paged compressed K/V (block_table non-null): k_cmp / v_cmp are pools, as
+  // for ScoreArgs
+  const int32_t* block_table;
+  int blocks_per_req, block_shift;
+  int64_t n_blocks;
 };
 
 struct WritebackArgs {

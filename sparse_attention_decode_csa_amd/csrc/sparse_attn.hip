@@ -301,14 +301,27 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
     e_hi = min(a.topk, e_lo + RPW);
     const int e = e_lo + lane;
     const int j = (lane < RPW && e < e_hi) ? a.topk_idx[(size_t)tok * a.topk + e] : -1;
-    rowoff = (j >= 0 && j < a.n_cap) ? (uint32_t)j * G::ROW : kOutOfRange;
+    const bool ok = j >= 0 && j < a.n_cap;
+    if (a.block_table) {  // paged: pool row through the block table (clamped into the pool)
+      const int blk = a.block_table[(size_t)b * a.blocks_per_req + (ok ? (j >> a.block_shift) : 0)];
+      const int64_t pb = min((int64_t)max(blk, 0), a.n_blocks - 1);
+      const int64_t prow = (pb << a.block_shift) + (j & ((1 << a.block_shift) - 1));
+      rowoff = ok ? (uint32_t)(prow * G::ROW) : kOutOfRange;
+    } else {
+      rowoff = ok ? (uint32_t)j * G::ROW : kOutOfRange;
+    }
   }
   const int nrows_wave = e_hi - e_lo;  // may be <= 0
 
+  // the request's slice of its cache, or for a paged compressed cache the
+  // whole pool; the host keeps either below 2^31 bytes
+  const bool pooled = !win && a.block_table;
   const size_t rows_req = win ? (size_t)a.w_cap : (size_t)a.n_cap;
-  const char* kreq = static_cast<const char*>(win ? a.k_win : a.k_cmp) + (size_t)b * rows_req * G::ROW;
-  const char* vreq = static_cast<const char*>(win ? a.v_win : a.v_cmp) + (size_t)b * rows_req * G::ROW;
-  const int range = (int)(rows_req * G::ROW);  // the host keeps this below 2^31
+  const size_t base_row = pooled ? 0 : (size_t)b * rows_req;
+  const size_t range_rows = pooled ? (size_t)(a.n_blocks << a.block_shift) : rows_req;
+  const char* kreq = static_cast<const char*>(win ? a.k_win : a.k_cmp) + base_row * G::ROW;
+  const char* vreq = static_cast<const char*>(win ? a.v_win : a.v_cmp) + base_row * G::ROW;
+  const int range = (int)(range_rows * G::ROW);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kreq, range);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vreq, range);
 

@@ -395,6 +395,35 @@ def page_cache(dense: np.ndarray, block_size: int, seed: int, spare_blocks: int 
     return pool, table
 
 
+def page_inputs(inp: dict, block_size: int, seed: int, idx: bool = True, cmp: bool = True,
+                spare_blocks: int = 3) -> dict:
+    """A copy of a seeded input dict with the indexer key cache (idx) and/or
+    the compressed K/V cache (cmp) moved into block pools (page_cache).
+    Names: k_idx_pool (or k_idx8_pool + k_scale_pool), idx_table,
+    idx_block_size; k_cmp_pool + v_cmp_pool sharing cmp_table, cmp_block_size.
+    The dense arrays that were paged are dropped."""
+    out = dict(inp)
+    if idx:
+        if "k_idx8" in inp:
+            out["k_idx8_pool"], out["idx_table"] = page_cache(inp["k_idx8"], block_size, seed,
+                                                              spare_blocks, fill=0x7E)
+            out["k_scale_pool"], _ = page_cache(inp["k_scale"], block_size, seed, spare_blocks)
+            del out["k_idx8"], out["k_scale"]
+            out.pop("k_idx", None)
+        else:
+            out["k_idx_pool"], out["idx_table"] = page_cache(inp["k_idx"], block_size, seed,
+                                                             spare_blocks)
+            del out["k_idx"]
+        out["idx_block_size"] = block_size
+    if cmp:
+        out["k_cmp_pool"], out["cmp_table"] = page_cache(inp["k_cmp"], block_size, seed + 1,
+                                                         spare_blocks)
+        out["v_cmp_pool"], _ = page_cache(inp["v_cmp"], block_size, seed + 1, spare_blocks)
+        del out["k_cmp"], out["v_cmp"]
+        out["cmp_block_size"] = block_size
+    return out
+
+
 def ring_slot_mapping(shape: Shape, start_pos: np.ndarray) -> np.ndarray:
     """Slot mapping of the step's new tokens into the per-request window rings
     viewed as one flat cache [B*w_cap][D]: token (b, s) at position

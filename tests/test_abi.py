@@ -178,7 +178,8 @@ def test_attn_capacity_workspace_alignment():
     p = [FAKE] * 10
     p[7] = None                                          # rope table with rope_dim > 0
     assert call_attn(sh, p) == 1
-    assert call_attn(shape(rope_dim=0), [FAKE] * 7 + [None, None, FAKE], ws_bytes=1 << 40) != 1
+    # no RoPE: NULL tables pass the pointer checks (refused later, for the workspace)
+    assert call_attn(shape(rope_dim=0), [FAKE] * 7 + [None, None, FAKE], ws_bytes=0) == 6
 
 
 def test_empty_problem_is_ok_without_gpu_work():
@@ -201,3 +202,70 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         C.topk(shape(), t, t, t)
+
+
+# --------------------------------------------------------------------------
+# paged compressed caches
+# --------------------------------------------------------------------------
+
+def pages(bpr=16, bs=16, n_blocks=1000, table=FAKE):
+    return C.CPages(table, bpr, bs, n_blocks)
+
+
+def call_score_paged(sh, pg, ptrs=None, k_scale=None):
+    p = ptrs or [FAKE] * 5
+    return C.lib().csa_indexer_score_paged(
+        None if sh is None else ctypes.byref(C.CShape.of(sh)), p[0], p[1], p[2], k_scale,
+        None if pg is None else ctypes.byref(pg), p[3], p[4], None)
+
+
+def call_attn_paged(sh, pg, ptrs=None, ws_bytes=1 << 40):
+    p = ptrs or [FAKE] * 10
+    return C.lib().csa_sparse_attn_decode_paged(
+        ctypes.byref(C.CShape.of(sh)), p[0], p[1], p[2], p[3], p[4],
+        None if pg is None else ctypes.byref(pg), p[5], p[6], p[7], p[8], 1 << 20, 0.1, p[9],
+        FAKE, ws_bytes, None)
+
+
+# shape(): n_cap 256 rows, so block size 16 needs 16 table entries per request
+PAGE_REFUSALS = [
+    (dict(bs=8), 2), (dict(bs=48), 2), (dict(bs=8192), 2), (dict(bs=0), 2),
+    (dict(n_blocks=0), 2), (dict(bpr=0), 2),
+    (dict(bpr=15), 4), (dict(bpr=1, bs=128), 4),
+    (dict(n_blocks=1 << 28, bs=16), 8),          # 2^32 pool rows: past int32
+    (dict(table=MISALIGNED), 5), (dict(table=None), 1),
+]
+
+
+@pytest.mark.parametrize("kw,code", PAGE_REFUSALS)
+def test_indexer_score_paged_refusals(kw, code):
+    assert call_score_paged(shape(), pages(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", PAGE_REFUSALS + [
+    (dict(n_blocks=(1 << 31) // (16 * 256), bs=16), 8),   # bf16 D=128 pool reaching 2^31 bytes
+])
+def test_attn_paged_refusals(kw, code):
+    assert call_attn_paged(shape(), pages(**kw)) == code
+
+
+def test_paged_null_dtype_alignment_workspace():
+    assert call_score_paged(None, pages()) == 1
+    assert call_score_paged(shape(), None) == 1
+    assert call_score_paged(shape(), pages(), [FAKE, FAKE, None, FAKE, FAKE]) == 1   # pool
+    assert call_score_paged(shape(), pages(), [FAKE, FAKE, MISALIGNED, FAKE, FAKE]) == 5
+    assert call_score_paged(shape(dtype=I.F32), pages(), k_scale=FAKE) == 3         # FP8: bf16 q
+    assert call_score_paged(shape(), pages(), k_scale=MISALIGNED) == 5
+    assert call_score_paged(shape(n_cap=200), pages()) == 4     # capacity for max_len first
+    assert call_score_paged(shape(batch=0), None, [None] * 5) == 0   # empty problem
+    assert call_attn_paged(shape(), None) == 1
+    p = [FAKE] * 10
+    p[3] = None                                                  # k_pool
+    assert call_attn_paged(shape(), pages(), p) == 1
+    p = [FAKE] * 10
+    p[4] = MISALIGNED                                            # v_pool
+    assert call_attn_paged(shape(), pages(), p) == 5
+    sh = shape()
+    assert call_attn_paged(sh, pages(), ws_bytes=C.sparse_attn_workspace_bytes(sh) - 1) == 6
+    # the largest pool the 32-bit offsets allow passes the page checks
+    assert call_attn_paged(sh, pages(n_blocks=(0x7FFFF000 // (16 * 256))), ws_bytes=0) == 6

@@ -48,7 +48,12 @@ def gpu_step(shape, inp, supplied=False, topk_idx=None, scores=None, jobs=("scor
     if scores is not None:
         bufs["scores"].copy_(torch.from_numpy(scores))
     if "score" in jobs:
-        if "k_idx8" in d:   # FP8 indexer key cache
+        if "idx_table" in d:   # paged indexer key cache
+            fp8 = "k_idx8_pool" in d
+            C.indexer_score_paged(shape, d["q_idx"], d["w"], d["k_idx8_pool" if fp8 else "k_idx_pool"],
+                                  d["k_scale_pool"] if fp8 else None, d["idx_table"],
+                                  d["start_pos"], bufs["scores"])
+        elif "k_idx8" in d:   # FP8 indexer key cache
             C.indexer_score_fp8(shape, d["q_idx"], d["w"], d["k_idx8"], d["k_scale"], d["start_pos"],
                                 bufs["scores"])
         else:
@@ -60,7 +65,11 @@ def gpu_step(shape, inp, supplied=False, topk_idx=None, scores=None, jobs=("scor
         ti = torch.from_numpy(np.ascontiguousarray(topk_idx, np.int32)).cuda()
     elif supplied:
         ti = d["topk_idx"]
-    if "attn" in jobs:
+    if "attn" in jobs and "cmp_table" in d:   # paged compressed K/V cache
+        C.sparse_attn_decode_paged(shape, d["q"], d["k_win"], d["v_win"], d["k_cmp_pool"],
+                                   d["v_cmp_pool"], d["cmp_table"], ti, d["start_pos"],
+                                   d["rope_cos"], d["rope_sin"], scale, bufs["out"], bufs["attn_ws"])
+    elif "attn" in jobs:
         C.sparse_attn_decode(shape, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"], ti,
                              d["start_pos"], d["rope_cos"], d["rope_sin"], scale, bufs["out"],
                              bufs["attn_ws"])
@@ -184,6 +193,90 @@ def test_end_to_end_fp8_keys():
     exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
                                inp["start_pos"])
     print(f"fp8 config {cid}: {len(exempt)} boundary exemptions {exempt}")
+    assert len(exempt) <= max(1, sh.batch * sh.q_per_req // 32)
+    ex = {b * sh.q_per_req + s for (b, s, _) in exempt}
+    keep = [t for t in range(sh.batch * sh.q_per_req) if t not in ex]
+    U.compare_outputs(sh, got["out"], ref["out"], tokens=keep)
+
+
+# --------------------------------------------------------------------------
+# paged compressed caches: pools of blocks located through block tables
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid,bs,fmt", [(3, 16, "bf16"), (3, 256, "fp8"), (4, 64, "bf16"),
+                                        (4, 4096, "fp8"), (0, 16, "bf16")])
+def test_paged_scores_match_oracle(cid, bs, fmt):
+    sh = I.CONFIGS[cid].shape
+    dense = I.make_inputs(cid, key_format=fmt)
+    inp = I.page_inputs(dense, bs, seed=cid * 10 + bs, cmp=False)
+    ref = oracle.run_paged(sh, inp, jobs=oracle.JOB_SCORE, nthreads=NTHREADS)
+    got = gpu_step(sh, inp, jobs=("score",))
+    check_scores(sh, dense, got, ref)
+    # the paged kernel does the dense kernel's arithmetic in the same order
+    assert np.array_equal(got["scores"], gpu_step(sh, dense, jobs=("score",))["scores"],
+                          equal_nan=True)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_paged_scores_exact_grid_ragged(fmt):
+    # n_cap not a multiple of the block size, spare table columns pointing
+    # at poisoned blocks, dyadic inputs: bitwise equality with the oracle.
+    cfg = small_cfg(q_per_req=3, idx_heads=8, idx_dim=128, n_cap=600, topk=32, max_len=2400)
+    inp = I.make_inputs(cfg, key_format=fmt)
+    g = np.random.default_rng(77)
+    inp["q_idx"] = I.f32_to_bf16_bits((g.integers(-8, 9, inp["q_idx"].shape) / 4.0).astype(np.float32))
+    inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    if fmt == "fp8":
+        live = inp["k_scale"] < 1.0
+        codes = I.f32_to_e4m3_bits((g.integers(-8, 9, inp["k_idx8"].shape) / 4.0).astype(np.float32))
+        inp["k_idx8"] = np.where(live[..., None], codes, inp["k_idx8"])
+    else:
+        kg = I.f32_to_bf16_bits((g.integers(-8, 9, inp["k_idx"].shape) / 4.0).astype(np.float32))
+        inp["k_idx"] = np.where(inp["k_idx"] == I.f32_to_bf16_bits(np.float32([I.POISON]))[0],
+                                inp["k_idx"], kg)
+    paged = I.page_inputs(inp, 64, seed=5, cmp=False)
+    t = paged["idx_table"]
+    spare = np.setdiff1d(np.arange(paged["k_idx8_pool" if fmt == "fp8" else "k_idx_pool"].shape[0]),
+                         t.reshape(-1)).astype(np.int32)
+    paged["idx_table"] = np.concatenate([t, np.tile(spare[:1], (t.shape[0], 7))], axis=1)
+    sh = cfg.shape
+    ref = oracle.run_paged(sh, paged, jobs=oracle.JOB_SCORE, nthreads=NTHREADS)
+    got = gpu_step(sh, paged, jobs=("score",))
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+
+
+@pytest.mark.parametrize("cid,bs", [(0, 16), (1, 32), (2, 16), (4, 128)])
+def test_paged_attention_matches_oracle(cid, bs):
+    cfg = I.CONFIGS[cid]
+    sh = cfg.shape
+    dense = I.make_inputs(cid)
+    inp = I.page_inputs(dense, bs, seed=cid + 40, idx=False)
+    ref = oracle.run_paged(sh, inp, nthreads=NTHREADS,
+                           jobs=(oracle.JOB_ATTN if cfg.supplied_topk
+                                 else oracle.JOB_SCORE | oracle.JOB_TOPK | oracle.JOB_ATTN))
+    got = gpu_step(sh, inp, topk_idx=ref["topk_idx"], jobs=("attn",))
+    worst = U.compare_outputs(sh, got["out"], ref["out"])
+    print(f"paged config {cid} block {bs}: worst error {worst:.3g}")
+    # same rows in the same order as the dense path: identical outputs
+    dgot = gpu_step(sh, dense, topk_idx=ref["topk_idx"], jobs=("attn",))
+    assert np.array_equal(got["out"], dgot["out"])
+
+
+@pytest.mark.parametrize("fmt,bs", [("bf16", 64), ("fp8", 16)])
+def test_end_to_end_paged(fmt, bs):
+    # score, select and attend with both caches paged, on the wide Top-K
+    # configuration, against the oracle over the gathered caches
+    cid = 4
+    sh = I.CONFIGS[cid].shape
+    dense = I.make_inputs(cid, key_format=fmt)
+    inp = I.page_inputs(dense, bs, seed=9)
+    ref = oracle.run_paged(sh, inp, nthreads=NTHREADS)
+    got = gpu_step(sh, inp)
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, dense, rows)
+    exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
+                               inp["start_pos"])
+    print(f"paged {fmt} block {bs}: {len(exempt)} boundary exemptions {exempt}")
     assert len(exempt) <= max(1, sh.batch * sh.q_per_req // 32)
     ex = {b * sh.q_per_req + s for (b, s, _) in exempt}
     keep = [t for t in range(sh.batch * sh.q_per_req) if t not in ex]

@@ -378,6 +378,26 @@ def test_paged_oracle_equals_dense(bs):
         assert np.array_equal(got[k], ref[k], equal_nan=True), k
 
 
+@pytest.mark.parametrize("bs,ragged", [(16, False), (32, True)])
+def test_paged_fp8_oracle_equals_dense(bs, ragged):
+    # the FP8 key cache (codes and scales share one table) and the compressed
+    # K/V pools paged by page_inputs; n_cap = 72 leaves a ragged last block
+    sh = small_shape(dtype=I.BF16, topk=8, n_cap=72 if ragged else 64)
+    inp = small_inputs(sh, key_format="fp8")
+    ref = oracle.run(sh, inp)
+    paged = I.page_inputs(inp, bs, seed=3)
+    assert "k_idx8" not in paged and "k_cmp" not in paged
+    assert paged["idx_table"].shape == (sh.batch, -(-sh.n_cap // bs))
+    got = oracle.run_paged(sh, paged)
+    for k in ("scores", "topk_idx", "out"):
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+    # a table entry swapped for a spare (poisoned) block changes the result
+    bad = dict(paged, cmp_table=paged["cmp_table"].copy())
+    spare = np.setdiff1d(np.arange(paged["k_cmp_pool"].shape[0]), paged["cmp_table"].ravel())
+    bad["cmp_table"][:, 0] = spare[0]
+    assert not np.array_equal(oracle.run_paged(sh, bad)["out"], ref["out"])
+
+
 # --------------------------------------------------------------------------
 # attention: library attention on the concatenated rows, closed forms
 # --------------------------------------------------------------------------
