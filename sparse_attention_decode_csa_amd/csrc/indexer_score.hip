@@ -12,12 +12,14 @@
 // as N.  A prefill chunk (many query tokens per request, the prefill indexer
 // of "Fix: port the DeepSeek-V4 MoE, hc_pre and prefill fixes to DSpark",
 // description) is cut into blocks of at most 64 query rows, a third grid
-// dimension; each block reads the keys its own tokens see, mostly from L2.  Key tiles stream HBM -> LDS by DMA in whole rows, several tiles in
-// flight per wave, and each lane reads its 16-byte MFMA operand pieces back
-// from LDS.  The per-head relu and weighted sum
-// runs in registers when the head count is 4, 8 or 16 (each lane's four
-// result rows are heads of one token), else through a small per-wave LDS
-// tile; either way in a fixed head order.
+// dimension; each block reads the keys its own tokens see, mostly from L2.
+// Key tiles stream HBM -> LDS by DMA in whole rows, several tiles in flight
+// per wave, and each lane reads its 16-byte MFMA operand pieces back from LDS.
+// The per-head relu and weighted sum runs in registers when the head count is
+// 4, 8 or 16 (each lane's four result rows are heads of one token), else
+// through a small per-wave LDS tile; either way in a fixed head order.  On the
+// register path the block's scores are written after its key stream, through
+// LDS, as contiguous streaming stores.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -89,9 +91,8 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // scale * sum_h w_h relu(q_h . c) = sum_h w_h relu(q_h . (scale * c))).
 // PG: the key cache (and the FP8 scales) are pools of blocks located through
 // a per-request block table; the workgroup loads the table entries of its
-// 1024 keys once, one per lane, and each lane maps its logical row with a
-// cross-lane move (blocks are at least 16 rows, so a 16-row tile never
-// straddles two of them).
+// 1024 keys once, one per lane, and each tile takes its block from one lane
+// (blocks are at least 16 rows, so a 16-row tile never straddles two).
 template <typename T, int DI, int MT, int HI, bool KF8, bool PG>
 __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   constexpr int ES = sizeof(T);
@@ -104,7 +105,10 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   constexpr int ROWS = MT * 16;      // padded query rows
   constexpr int RP = 17;             // padded LDS row length (floats)
 
-  __shared__ __attribute__((aligned(1024))) char tiles[kScoreWaves][kScoreBufs][TL::BYTES];
+  // tiles in flight per wave, as many as asked for within 128 KiB of tile buffers
+  constexpr int NB = kScoreBufs * kScoreWaves * TL::BYTES <= 128 * 1024 ? kScoreBufs
+                                                                         : 128 * 1024 / (kScoreWaves * TL::BYTES);
+  __shared__ __attribute__((aligned(1024))) char tiles[kScoreWaves][NB][TL::BYTES];
   __shared__ float red[HI ? 1 : kScoreWaves][HI ? 1 : ROWS][RP];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   // the block reads 4 consecutive 16-row tiles.
   auto issue_tile = [&](int t) {
     const int k0 = tile_key0(t), jt = min(k0, nmax - 1);
-    char* dst = tiles[wave][t % kScoreBufs];
+    char* dst = tiles[wave][t % NB];
 #pragma unroll
     for (int k = 0; k < TL::NPT; ++k) {
       const int r = k * TL::RPI + lane / TL::NPR;            // tile row this lane fetches
@@ -217,24 +221,31 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   // the query loads above are older than every tile DMA, so waiting for them
   // does not wait for the tiles
 #pragma unroll
-  for (int t = 0; t < kScoreBufs && t < kScoreTilesPerWave; ++t) issue_tile(t);
+  for (int t = 0; t < NB && t < kScoreTilesPerWave; ++t) issue_tile(t);
 
   float* srow = a.scores + tok0 * a.n_cap;
+  // register path: each tile's head sums, written after the tile loop
+  float outv[kScoreTilesPerWave][HI > 0 ? MT : 1];
 
 #pragma unroll
   for (int t = 0; t < kScoreTilesPerWave; ++t) {
     // Tile t has landed once at most the DMA instructions of the younger tiles
     // in flight are outstanding (other memory operations only make this wait
     // longer, never shorter).
-    constexpr int kAhead = kScoreBufs - 1;
+    constexpr int kAhead = NB - 1;
     const int younger = (t + kAhead < kScoreTilesPerWave ? kAhead : kScoreTilesPerWave - 1 - t);
+    static_assert(kAhead <= 7 && 7 * TL::NPT <= 63, "tile waits cover at most 7 younger tiles");
     switch (younger) {  // t is a compile-time constant after unrolling
       case 0: wait_vmcnt<0>(); break;
       case 1: wait_vmcnt<1 * TL::NPT>(); break;
       case 2: wait_vmcnt<2 * TL::NPT>(); break;
-      default: wait_vmcnt<3 * TL::NPT>(); break;
+      case 3: wait_vmcnt<3 * TL::NPT>(); break;
+      case 4: wait_vmcnt<4 * TL::NPT>(); break;
+      case 5: wait_vmcnt<5 * TL::NPT>(); break;
+      case 6: wait_vmcnt<6 * TL::NPT>(); break;
+      default: wait_vmcnt<7 * TL::NPT>(); break;
     }
-    const char* src = tiles[wave][t % kScoreBufs];
+    const char* src = tiles[wave][t % NB];
     u32x4_t kb[CH];
     if constexpr (KF8) {
 #pragma unroll
@@ -251,9 +262,9 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         kb[c] = *reinterpret_cast<const u32x4_t*>(src + n16 * ROW + 16 * slot);
       }
     }
-    if (t + kScoreBufs < kScoreTilesPerWave) {
+    if (t + NB < kScoreTilesPerWave) {
       wait_lgkmcnt0();  // the operand reads of this buffer are done: refill it
-      issue_tile(t + kScoreBufs);
+      issue_tile(t + NB);
     }
     const int tkey0 = tile_key0(t);
     f32x4_t acc[MT];
@@ -266,7 +277,6 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
     // lane holds dot(query row mt*16+4g+i, key tkey0+n16)
     if constexpr (HI > 0) {
       // heads in ascending order: the lane's four, then pairs of lanes
-      const int j = tkey0 + n16;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         float sum = 0.0f;
@@ -278,9 +288,7 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         if constexpr (HI >= 8) sum += __shfl_xor(sum, 16);
         if constexpr (HI >= 16) sum += __shfl_xor(sum, 32);
         if constexpr (KF8) sum *= ks[t];
-        const bool writer = (g & (HI / 4 - 1)) == 0;
-        if (writer && tok_of[mt] < S && nv_of[mt] > a.topk && j < nv_of[mt])
-          srow[(size_t)tok_of[mt] * a.n_cap + j] = sum;
+        outv[t][mt] = sum;
       }
     } else {
 #pragma unroll
@@ -301,6 +309,49 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         if (nv > a.topk && j < nv) srow[(size_t)s * a.n_cap + j] = sum;
       }
       wave_lds_fence();
+    }
+  }
+
+  if constexpr (HI > 0) {
+    // The block's scores of each token are staged through the tile buffers
+    // (idle once every wave has left the tile loop) and written as contiguous
+    // 16-byte pieces with the streaming hint.  One scattered 64-byte write
+    // per tile and token, interleaved with the key stream, cost more than
+    // their share of the traffic.
+    constexpr int kStageTok = (int)sizeof(tiles) / (kScoreKeysPerBlock * 4);  // tokens per pass
+    static_assert(kStageTok >= 1, "the tile buffers hold at least one token's scores");
+    float* stage = reinterpret_cast<float*>(&tiles[0][0][0]);
+    const bool writer = (g & (HI / 4 - 1)) == 0;  // lanes holding a finished head sum
+    for (int s0p = 0; s0p < S; s0p += kStageTok) {
+      __syncthreads();  // the tile buffers (or the previous pass) are free
+#pragma unroll
+      for (int t = 0; t < kScoreTilesPerWave; ++t) {
+        const int kl = (t * kScoreWaves + wave) * 16 + n16;  // key - key0
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int ts = tok_of[mt] - s0p;
+          if (writer && ts >= 0 && ts < kStageTok) stage[ts * kScoreKeysPerBlock + kl] = outv[t][mt];
+        }
+      }
+      __syncthreads();
+      const int np = min(kStageTok, S - s0p);
+      for (int e = threadIdx.x; e < np * (kScoreKeysPerBlock / 4); e += kScoreWaves * kWave) {
+        const int ts = e / (kScoreKeysPerBlock / 4), q4 = e - ts * (kScoreKeysPerBlock / 4);
+        const int s = s0p + ts;
+        const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
+        const int j0 = key0 + 4 * q4;
+        if (nv <= a.topk || j0 >= nv) continue;  // Top-K bypass, or past the visible rows
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + ts * kScoreKeysPerBlock + 4 * q4);
+        float* dst = srow + (size_t)s * a.n_cap + j0;
+        if (j0 + 4 <= nv && (a.n_cap & 3) == 0) {  // whole piece, 16-byte aligned row
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dst));
+        } else {
+          __builtin_nontemporal_store(v[0], dst);  // j0 < nv
+          if (j0 + 1 < nv) __builtin_nontemporal_store(v[1], dst + 1);
+          if (j0 + 2 < nv) __builtin_nontemporal_store(v[2], dst + 2);
+          if (j0 + 3 < nv) __builtin_nontemporal_store(v[3], dst + 3);
+        }
+      }
     }
   }
 }
