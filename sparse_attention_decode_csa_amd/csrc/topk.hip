@@ -185,8 +185,9 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// Exclusive prefix sum of one int per thread over the block, in thread order;
-// also returns the block total.  `red` holds one int per wave.
+// Exclusive prefix sum of one int per thread over a block of NW waves, in
+// thread order; also returns the block total.  `red` holds one int per wave.
+template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int inc = wave_inclusive_scan(v);
@@ -195,7 +196,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total)
   int before = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int t = red[w];
     before += w < wave ? t : 0;
     total += t;
@@ -220,6 +221,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 
 // block_exclusive_scan that also reduces a maximum over the block through
 // the same barriers.  `red` holds two ints per wave.
+template <int NW>
 __device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int* red, int& total,
                                                         uint32_t& block_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -234,7 +236,7 @@ __device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int*
   total = 0;
   block_max = 0u;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int t = red[2 * w];
     before += w < wave ? t : 0;
     total += t;
@@ -247,15 +249,17 @@ __device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int*
 // Histograms of the block-wide selections, double buffered by pass parity so
 // that zeroing the next pass's histogram needs no barrier of its own.
 constexpr int kHistStride = 257;   // per-wave copies sit off the bank period
+template <int NW>
 struct alignas(16) SelectSmem {  // 16-byte aligned: the bin scan reads uint4
-  uint32_t hist[2][kTopkWaves * kHistStride];
+  uint32_t hist[2][NW * kHistStride];
   uint32_t cnt[2][256];
   int res[2][2];   // per pass parity: (bin, keys above the bin)
-  int red[2 * kTopkWaves];
+  int red[2 * NW];
 };
 
 // Block-wide minimum and maximum of one key per thread (invalid threads pass
 // UINT32_MAX / 0).  `red` holds two ints per wave.
+template <int NW>
 __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red, uint32_t& mn,
                                               uint32_t& mx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -272,7 +276,7 @@ __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red
   mn = 0xFFFFFFFFu;
   mx = 0u;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     mn = min(mn, (uint32_t)red[2 * w]);
     mx = max(mx, (uint32_t)red[2 * w + 1]);
   }
@@ -291,17 +295,18 @@ __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red
 // the lower edge of the bin holding the k-th key (at least k keys are >= T).
 // (12-bit digits were measured too: the single-wave scan of 4096 bins cost
 // more than the pass they save.)  No floating point anywhere.
-template <bool PER_WAVE, int NK, typename Key, typename Valid>
+template <int NW, bool PER_WAVE, int NK, typename Key, typename Valid>
 __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uint32_t hi,
-                                   SelectSmem& sm, uint32_t& T, int& keq, int max_passes = 4) {
-  constexpr int DB = 8, kBins = 1 << DB;
+                                   SelectSmem<NW>& sm, uint32_t& T, int& keq, int max_passes = 4) {
+  constexpr int DB = 8, kBins = 1 << DB, NT = NW * kWave;
+  static_assert(NT >= kBins, "one thread per bin sums the per-wave histograms");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int kWords = PER_WAVE ? kTopkWaves * kHistStride : kBins;
+  constexpr int kWords = PER_WAVE ? NW * kHistStride : kBins;
   const int nb = lo == hi ? 0 : 32 - __clz(lo ^ hi);   // bits still to decide
   uint32_t pmask = nb == 32 ? 0u : ~((1u << nb) - 1u);
   uint32_t prefix = lo & pmask;
   int krem = k;
-  for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[0][i] = 0u;
+  for (int i = tid; i < kWords; i += NT) sm.hist[0][i] = 0u;
   __syncthreads();
   int pass = 0;
   for (int top = nb; top > 0; top -= DB, ++pass) {
@@ -316,14 +321,14 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
       if (valid(r) && (kv & pmask) == prefix) atomicAdd(&wh[(kv >> shift) & dmask], 1u);
     }
     // the other buffer was last read before the previous pass's final barrier
-    for (int i = tid; i < kWords; i += kTopkThreads) sm.hist[par ^ 1][i] = 0u;
+    for (int i = tid; i < kWords; i += NT) sm.hist[par ^ 1][i] = 0u;
     __syncthreads();
     const uint32_t* c = h;
     if (PER_WAVE) {
       if (tid < 256) {
         uint32_t t = 0u;
 #pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w) t += h[w * kHistStride + tid];
+        for (int w = 0; w < NW; ++w) t += h[w * kHistStride + tid];
         sm.cnt[par][tid] = t;
       }
       __syncthreads();
@@ -360,14 +365,13 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
 // Candidate buffer: rows whose key clears the sampled threshold, kept as
 // (key, row index) pairs in ascending row order.
 constexpr int kCandCap = 8192;
-constexpr int kCandPerThread = kCandCap / kTopkThreads;
 constexpr int kCandSlots = kCandCap + kWave;  // + one spare slot per lane
 
 
 // Ascending-index emission of the selection {key > T} plus the keq
 // lowest-indexed keys equal to T, over items that thread t holds as a
 // contiguous run in index order: item(j) for j < cnt gives (key, row index).
-template <int NJ, typename Item>
+template <int NW, int NJ, typename Item>
 __device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, int keq,
                                                int32_t* out, int K, int* red) {
   int gt = 0, eq = 0;
@@ -381,7 +385,7 @@ __device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, i
   }
   int tot;
   // both counts packed in one int: each block total is at most 32768 < 2^16
-  const int before = block_exclusive_scan(gt | (eq << 16), red, tot);
+  const int before = block_exclusive_scan<NW>(gt | (eq << 16), red, tot);
   int eq_rank = before >> 16;
   int dst = (before & 0xFFFF) + min(eq_rank, keq);
 #pragma unroll
@@ -397,12 +401,17 @@ __device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, i
   }
 }
 
-// Thread t owns the contiguous slice [t*KPT, t*KPT + KPT) of the row; with
-// VEC4 the slice is read with 16-byte loads (rows 16-byte aligned).
-template <int KPT, bool VEC4>
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
-  __shared__ SelectSmem sm;
-  __shared__ uint2 cand[kCandSlots];  // (key, row index)
+// A block of NW waves per token.  Thread t owns the contiguous slice
+// [t*KPT, t*KPT + KPT) of the row; with VEC4 the slice is read with 16-byte
+// loads (rows 16-byte aligned).  Blocks whose rows can exceed the candidate
+// buffer carry it (and the sampled-threshold path); smaller ones go straight
+// to the whole-row selection and keep their LDS small, so that many of them
+// share a CU when a launch holds many tokens (prefill chunks).
+template <int NW, int KPT, bool VEC4>
+__global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
+  constexpr int NT = NW * kWave;
+  constexpr bool kCandPath = NT * KPT > kCandCap;
+  __shared__ SelectSmem<NW> sm;
 
   const int tid = threadIdx.x;
   const int tok = blockIdx.x;
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
   int32_t* out = a.topk_idx + (size_t)tok * K;
 
   if (n <= K) {  // fits: every visible row, no scoring needed
-    for (int i = tid; i < K; i += kTopkThreads) out[i] = i < n ? i : -1;
+    for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
     return;
   }
 
@@ -446,7 +455,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 1; j < KPT; ++j) kmax = max(kmax, key[j]);
 
-  if (n > kCandCap) {
+  if constexpr (kCandPath) if (n > kCandCap) {
+    __shared__ uint2 cand[kCandSlots];  // (key, row index)
+    constexpr int kCandPerThread = kCandCap / NT;
     // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT,
     // which exists for the first m threads (closed form, no scan).
     // Two 8-bit passes over the full key range fix the top 16 key bits: the
@@ -458,15 +469,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     for (int j = 0; j < KPT; ++j) sk = j == js ? key[j] : sk;
     const bool sval = valid(js);
     const int q = n / KPT, rr = n % KPT;
-    const int m = min(q, kTopkThreads) + ((q < kTopkThreads && q % KPT < rr) ? 1 : 0);
+    const int m = min(q, NT) + ((q < NT && q % KPT < rr) ? 1 : 0);
     // sample rank expected at row rank K, plus three standard deviations, so
     // that the threshold keeps at least K rows
     const int ks0 = (int)(((long long)K * m + n - 1) / n);
     const int ks = min(m, ks0 + 3 * (int)sqrtf((float)ks0) + 4);
     uint32_t tau;
     int unused;
-    block_radix_select<false, 1>([&](int) { return sk; }, [&](int) { return sval; }, ks, 0u,
-                                 0xFFFFFFFFu, sm, tau, unused, 2);
+    block_radix_select<NW, false, 1>([&](int) { return sk; }, [&](int) { return sval; }, ks, 0u,
+                                     0xFFFFFFFFu, sm, tau, unused, 2);
     // ---- rows at or above the threshold, compacted in row order; the same
     // barriers give the row maximum
     int mine = 0;
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
     for (int j = 0; j < KPT; ++j) mine += (valid(j) && key[j] >= tau) ? 1 : 0;
     int c;
     uint32_t row_max;
-    int pos = block_exclusive_scan_max(mine, kmax, sm.red, c, row_max);
+    int pos = block_exclusive_scan_max<NW>(mine, kmax, sm.red, c, row_max);
     if (c >= K && c <= kCandCap) {  // block-uniform
       // branch-free: every slot is written, a non-candidate into this lane's
       // spare slot past the buffer
@@ -490,13 +501,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
       // shared histogram
       uint32_t T;
       int keq;
-      block_radix_select<false, kCandPerThread>(
-          [&](int r) { return cand[min(r * kTopkThreads + tid, c - 1)].x; },
-          [&](int r) { return r * kTopkThreads + tid < c; }, K, tau, row_max, sm, T, keq);
+      block_radix_select<NW, false, kCandPerThread>(
+          [&](int r) { return cand[min(r * NT + tid, c - 1)].x; },
+          [&](int r) { return r * NT + tid < c; }, K, tau, row_max, sm, T, keq);
       // emission over the candidates only: thread t takes a contiguous run
-      const int cpt = (c + kTopkThreads - 1) / kTopkThreads;
+      const int cpt = (c + NT - 1) / NT;
       const int c0 = min(c, tid * cpt), cnt = min(c, c0 + cpt) - c0;
-      emit_selection<kCandPerThread>([&](int j) { return cand[c0 + j]; }, cnt, T, keq, out, K, sm.red);
+      emit_selection<NW, kCandPerThread>([&](int j) { return cand[c0 + j]; }, cnt, T, keq, out, K,
+                                         sm.red);
       return;
     }
   }
@@ -505,45 +517,54 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 1; j < KPT; ++j) kmin = min(kmin, key[j]);
   uint32_t row_min, row_max;
-  block_min_max(kmin, kmax, sm.red, row_min, row_max);
+  block_min_max<NW>(kmin, kmax, sm.red, row_min, row_max);
   uint32_t T;
   int keq;
-  block_radix_select<true, KPT>([&](int j) { return key[j]; }, valid, K, row_min, row_max, sm, T,
-                                keq);
+  block_radix_select<NW, true, KPT>([&](int j) { return key[j]; }, valid, K, row_min, row_max, sm,
+                                    T, keq);
   const int cnt = max(0, min(KPT, n - i0));
-  emit_selection<KPT>([&](int j) { return make_uint2(key[j], (uint32_t)(i0 + j)); }, cnt, T, keq,
-                      out, K, sm.red);
+  emit_selection<NW, KPT>([&](int j) { return make_uint2(key[j], (uint32_t)(i0 + j)); }, cnt, T,
+                          keq, out, K, sm.red);
 }
 
-template <int KPT>
-void launch_reg(const TopkArgs& a, bool vec4, dim3 grid, dim3 block, hipStream_t st) {
+template <int NW, int KPT>
+void launch_reg(const TopkArgs& a, bool vec4, hipStream_t st) {
+  const dim3 grid(a.batch * a.q_per_req), block(NW * kWave);
   if (vec4)
-    hipLaunchKernelGGL((topk_reg_kernel<KPT, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<NW, KPT, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((topk_reg_kernel<KPT, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((topk_reg_kernel<NW, KPT, false>), grid, block, 0, st, a);
+}
+
+// Rows of up to 32 keys per thread: the smallest slice that holds n_bound.
+template <int NW>
+bool launch_reg_sized(const TopkArgs& a, int n_bound, bool vec4, hipStream_t st) {
+  constexpr int NT = NW * kWave;
+  if (n_bound <= 4 * NT) launch_reg<NW, 4>(a, vec4, st);
+  else if (n_bound <= 8 * NT) launch_reg<NW, 8>(a, vec4, st);
+  else if (n_bound <= 16 * NT) launch_reg<NW, 16>(a, vec4, st);
+  else if (n_bound <= 32 * NT) launch_reg<NW, 32>(a, vec4, st);
+  else return false;
+  return true;
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int n_bound = std::min(a.n_cap, a.max_len / a.ratio);
-  const dim3 grid(a.batch * a.q_per_req), block(kTopkThreads);
+  const long long tokens = (long long)a.batch * a.q_per_req;
   // rows start 16-byte aligned when n_cap is a multiple of 4 floats
-#ifndef CSA_TOPK_VEC4_MAX_KPT
-#define CSA_TOPK_VEC4_MAX_KPT 32
+  const bool vec4 = (a.n_cap & 3) == 0;
+  // A decode step has few tokens: one 16-wave block per token, for latency.
+  // A prefill chunk has thousands: 4-wave blocks (several per CU) when every
+  // row fits in their registers.
+#ifndef CSA_TOPK_SMALL_BLOCK_TOKENS
+#define CSA_TOPK_SMALL_BLOCK_TOKENS 2048
 #endif
-  const bool vec4 = (a.n_cap & 3) == 0 && n_bound <= CSA_TOPK_VEC4_MAX_KPT * kTopkThreads;
-  if (n_bound <= 4 * kTopkThreads) {
-    launch_reg<4>(a, vec4, grid, block, st);
-  } else if (n_bound <= 8 * kTopkThreads) {
-    launch_reg<8>(a, vec4, grid, block, st);
-  } else if (n_bound <= 16 * kTopkThreads) {
-    launch_reg<16>(a, vec4, grid, block, st);
-  } else if (n_bound <= 32 * kTopkThreads) {
-    launch_reg<32>(a, vec4, grid, block, st);
-  } else {
-    hipLaunchKernelGGL(topk_global_kernel, grid, block, 0, st, a);
-  }
+  if (tokens >= CSA_TOPK_SMALL_BLOCK_TOKENS && launch_reg_sized<4>(a, n_bound, vec4, st))
+    return hipGetLastError();
+  if (!launch_reg_sized<kTopkWaves>(a, n_bound, vec4, st))
+    hipLaunchKernelGGL(topk_global_kernel, dim3(a.batch * a.q_per_req), dim3(kTopkThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -434,6 +434,26 @@ def test_topk_exact_synthetic(kind, n_cap, topk):
     assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
 
 
+@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero"])
+@pytest.mark.parametrize("n_cap,topk", [(8192, 1024), (1000, 100), (4100, 1024), (2049, 2048)])
+def test_topk_many_tokens(kind, n_cap, topk):
+    # 2080 tokens: the launch takes the small-block selection (several blocks
+    # per CU).  Causal rows of every length from below K to n_cap, bypass
+    # tokens included; 4100 is not a multiple of the per-thread slice.
+    B, S = 4, 520
+    sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=S + 8,
+                 heads=1, head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1,
+                 max_len=4 * n_cap, dtype=I.BF16)
+    top = 4 * n_cap - S
+    sp = np.clip(np.array([top, 4 * topk - 300, 0, 2 * n_cap], np.int64), 0, top).astype(np.int32)
+    scores = I.random_scores(n_cap * 7 + topk, B, S, n_cap, kind)
+    ref = oracle.run(sh, dict(start_pos=sp), jobs=oracle.JOB_TOPK, scores=scores, nthreads=NTHREADS)
+    out = torch.full((B, S, topk), -7, dtype=torch.int32, device="cuda")
+    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
+
+
 @pytest.mark.parametrize("topk", [256, 257, 1024])
 def test_topk_winners_past_256(topk):
     n_cap = 8192
