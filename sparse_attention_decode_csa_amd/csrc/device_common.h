@@ -120,6 +120,16 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier for LDS only: this wave's LDS operations complete, then
+// s_barrier.  __syncthreads() also fences global memory, which on this target
+// waits for every outstanding vector memory operation (vmcnt(0)), including
+// LDS DMA prefetches still in flight; callers of this barrier wait for the DMA
+// they need themselves.  The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void block_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Workgroups are dealt to the 8 XCDs round-robin by dispatch order.  This maps
 // a dispatch index to a logical index such that each XCD receives one
 // contiguous run of logical indices, so neighbouring logical work items share

@@ -356,6 +356,218 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill shape: many query rows per request (a chunk of tokens).  The
+// decode-shaped kernel above gives each wave its own key tiles against at
+// most 64 query rows.  Here a block of 4 waves takes 256 query rows (64 per
+// wave) and the waves read one shared ring of key steps (32 keys, >= 4 KiB),
+// so a key row leaves L2 once per 256 query rows.  Each wave issues its share
+// of every step's DMA and one LDS barrier per step publishes the step.
+//
+// The contraction is v_mfma_f32_32x32x16_bf16 with the query rows permuted so
+// that the 16 result rows a lane holds are whole tokens (Hi = 4, 8 or 16):
+// the head sum needs no cross-lane exchange, and each score store writes two
+// contiguous 128-byte runs (32 keys of two tokens).  The stores are buffer
+// stores issued unconditionally (masked lanes get an offset past the buffer),
+// so every step issues the same number of vector memory instructions and the
+// DMA waits can count them exactly: vector memory operations retire in order,
+// so a wait for a step also waits for whatever was issued before it.
+constexpr int kGemmWaves = 4;
+constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kGemmRows = kGemmWaves * 64;        // query rows per block
+constexpr int kGemmKeys = 1024;                   // keys per block
+constexpr int kGemmBufs = 8;                      // key steps in the ring
+constexpr int kGemmStepKeys = 32;                 // one 32-key MFMA N tile
+
+// s_waitcnt vmcnt(n) for a run-time n in [0, 63]
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {
+#define CSA_VMCNT_CASE(N) case N: wait_vmcnt<N>(); break;
+#define CSA_VMCNT_CASE8(B) CSA_VMCNT_CASE(B) CSA_VMCNT_CASE(B + 1) CSA_VMCNT_CASE(B + 2) CSA_VMCNT_CASE(B + 3) \
+    CSA_VMCNT_CASE(B + 4) CSA_VMCNT_CASE(B + 5) CSA_VMCNT_CASE(B + 6) CSA_VMCNT_CASE(B + 7)
+    CSA_VMCNT_CASE8(0) CSA_VMCNT_CASE8(8) CSA_VMCNT_CASE8(16) CSA_VMCNT_CASE8(24)
+    CSA_VMCNT_CASE8(32) CSA_VMCNT_CASE8(40) CSA_VMCNT_CASE8(48) CSA_VMCNT_CASE8(56)
+#undef CSA_VMCNT_CASE8
+#undef CSA_VMCNT_CASE
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+template <int DI, int HI, bool PG>
+__global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(ScoreArgs a) {
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  constexpr int ROW = DI * 2;                          // bytes per query / key row
+  constexpr int KS = DI / 16;                          // 16-dim MFMA k-steps
+  constexpr int MT = 2;                                // 32-row M tiles per wave
+  constexpr int TPL = 16 / HI;                         // tokens per lane per M tile
+  using TL = ScoreTile<ROW>;                           // 16-row tile layout (piece swizzle)
+  constexpr int STEP_BYTES = 2 * TL::BYTES;            // 32 keys
+  constexpr int NSTEPS = kGemmKeys / kGemmStepKeys;
+  constexpr int DPW = 2 * TL::NPT / kGemmWaves;        // DMA instructions per wave per step
+  constexpr int NST = MT * TPL;                        // score stores per wave per step
+  static_assert(DPW >= 1 && DPW * kGemmWaves == 2 * TL::NPT, "a step splits evenly over the waves");
+  static_assert(HI == 4 || HI == 8 || HI == 16, "whole tokens per lane");
+
+  __shared__ __attribute__((aligned(1024))) char ring[kGemmBufs][STEP_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int b = blockIdx.y;
+  constexpr int TOK = kGemmRows / HI;                  // tokens per block
+  const int s0 = blockIdx.z * TOK;
+  const int S = min(a.q_per_req - s0, TOK), SH = S * HI;
+  const int sp = a.start_pos[b] + s0;
+  const size_t tok0 = (size_t)b * a.q_per_req + s0;
+
+  int nmax = 0;  // rows scored for this block: the largest visible count among non-fitting tokens
+  for (int s = 0; s < S; ++s) {
+    const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
+    if (nv > a.topk) nmax = max(nmax, nv);
+  }
+  const int key0 = blockIdx.x * kGemmKeys;
+  if (key0 >= nmax) return;  // whole block
+  const int nsteps = min(NSTEPS, (nmax - key0 + kGemmStepKeys - 1) / kGemmStepKeys);
+
+  // block table slice, one entry per lane (see the kernel above)
+  int pblk = 0;
+  if constexpr (PG) {
+    const int lb = min((key0 >> a.block_shift) + lane, a.blocks_per_req - 1);
+    const int e = a.block_table[(size_t)b * a.blocks_per_req + lb];
+    pblk = (int)min((int64_t)max(e, 0), a.n_blocks - 1);
+  }
+
+  // A operand.  M tile mt of this wave holds block rows wave*64 + mt*32 ...;
+  // MFMA row m (lane l32 supplies row l32) carries token
+  // (m % 8 / 4) * TPL + i / HI and head i % HI of the tile, i = m / 8 * 4 + m % 4,
+  // so that result slot v of lane (l32, half) is token half*TPL + v/HI, head
+  // v % HI.  Rows past the block's tokens copy the last real row.
+  u32x4_t qa[MT][KS];
+  float wv[MT][16];
+  int nvt[MT][TPL];
+  const char* qbase = static_cast<const char*>(a.q_idx) + tok0 * HI * ROW;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int tile_row0 = wave * 64 + mt * 32;
+    {
+      const int m = l32, i = (m >> 3) * 4 + (m & 3);
+      const int row = tile_row0 + ((m >> 2) & 1) * TPL * HI + i;  // token*HI + head, in block rows
+      const char* qp = qbase + (size_t)min(row, SH - 1) * ROW + 16 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qa[mt][ks] = ld16(qp + 32 * ks);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      wv[mt][v] = a.w[tok0 * HI + min(tile_row0 + half * TPL * HI + v, SH - 1)];
+#pragma unroll
+    for (int tt = 0; tt < TPL; ++tt) {
+      const int s = (tile_row0 + (half * TPL + tt) * HI) / HI;
+      const int nv = s < S ? min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap) : 0;
+      nvt[mt][tt] = nv > a.topk ? nv : 0;  // 0: not scored (past the block, or fits Top-K)
+    }
+  }
+  // scores of this block's tokens, addressed by buffer stores (32-bit offsets)
+  float* sblk = a.scores + tok0 * a.n_cap;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sblk, (int)((size_t)S * a.n_cap * 4));
+
+  // DMA of step st: instruction i = wave*DPW + d fills tile u = i / NPT, rows
+  // k*RPI + lane/NPR (k = i % NPT) with the piece swizzle of the kernel above.
+  int lrow[DPW], loff[DPW];  // the lane's row within the step and its byte offset
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) {
+    const int i = wave * DPW + d, u = i / TL::NPT, k = i % TL::NPT;
+    const int r = k * TL::RPI + lane / TL::NPR;
+    const int piece = (lane % TL::NPR) ^ (r % TL::NPR);
+    lrow[d] = u * 16 + r;
+    loff[d] = 16 * piece;
+  }
+  const char* kbase = static_cast<const char*>(a.k_idx);
+  auto issue_step = [&](int st) {
+    char* dst = ring[st % kGemmBufs];
+    const int step0 = key0 + st * kGemmStepKeys;
+    const bool full = step0 + kGemmStepKeys <= nmax;  // uniform
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int i = wave * DPW + d, u = i / TL::NPT, k = i % TL::NPT;
+      const char* src;
+      if (!PG && full) {
+        src = kbase + ((size_t)b * a.n_cap + step0) * ROW + (lrow[d] * ROW + loff[d]);
+      } else {
+        const int jt = min(step0 + u * 16, nmax - 1), j = min(step0 + lrow[d], nmax - 1);
+        size_t row;
+        if constexpr (PG) {
+          const int blk = __builtin_amdgcn_readlane(pblk, (jt >> a.block_shift) - (key0 >> a.block_shift));
+          row = ((size_t)blk << a.block_shift) + (size_t)(j & ((1 << a.block_shift) - 1));
+        } else {
+          (void)jt;
+          row = (size_t)b * a.n_cap + j;
+        }
+        src = kbase + row * ROW + loff[d];
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + u * TL::BYTES + 1024 * k),
+                                       16, 0, kNonTemporal);
+    }
+  };
+  // A fixed number of steps in flight (steps past nsteps read clamped rows
+  // and are never consumed), then one wait that covers the query and weight
+  // loads, which are older than every DMA.
+#pragma unroll
+  for (int st = 0; st < kGemmBufs - 1; ++st) issue_step(st);
+  wait_vmcnt<(kGemmBufs - 1) * DPW>();
+
+  for (int st = 0; st < nsteps; ++st) {
+    // Step st is in once at most the younger operations are outstanding: the
+    // DMA of the younger steps in flight and the score stores issued since
+    // (NST per step, all steps so far, at most kGemmBufs - 1 of them after it).
+    wait_vmcnt_rt(min(63, DPW * min(kGemmBufs - 2, nsteps - 1 - st) + NST * min(st, kGemmBufs - 1)));
+    block_lds_barrier();  // every wave's share of step st is in; step st - 1 is read by all
+    if (st + kGemmBufs - 1 < nsteps) issue_step(st + kGemmBufs - 1);  // into step st - 1's buffer
+    const char* src = ring[st % kGemmBufs];
+    // B operand: key l32 of the step, dims 16*ks + 8*half .. +8
+    const int u = l32 >> 4, r = l32 & 15;
+    f32x16_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int slot = (2 * ks + half) ^ (r % TL::NPR);
+      const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(src + u * TL::BYTES + r * ROW + 16 * slot);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[mt][ks]),
+                                                          __builtin_bit_cast(bf16x8_t, kb), acc[mt], 0, 0, 0);
+    }
+    const int j = key0 + st * kGemmStepKeys + l32;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) {
+        float sum = 0.0f;  // heads in ascending order
+#pragma unroll
+        for (int h = 0; h < HI; ++h) {
+          const float d = acc[mt][tt * HI + h];
+          sum += wv[mt][tt * HI + h] * (d > 0.0f ? d : 0.0f);
+        }
+        const int s = (wave * 64 + mt * 32) / HI + half * TPL + tt;   // token in the block
+        const uint32_t off = j < nvt[mt][tt] ? (uint32_t)(s * a.n_cap + j) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), srs, off, 0, kNonTemporal);
+      }
+    }
+  }
+}
+
+template <int DI, bool PG>
+hipError_t launch_gemm(const ScoreArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.idx_heads) {
+    case 4: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 4, PG>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 8, PG>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 16, PG>), grid, dim3(kGemmThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int DI, int HI, bool KF8, bool PG>
 hipError_t launch_mt(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   const int mt = (a.tok_per_block * a.idx_heads + 15) / 16;
@@ -398,6 +610,24 @@ hipError_t launch_layout(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
   const int n_bound = std::min(in.n_cap, in.max_len / in.ratio);
   if (n_bound <= in.topk) return hipSuccess;  // every token fits Top-K: nothing to score
+  // Prefill chunks (at least two blocks of 256 query rows per request) with
+  // bf16 keys and 4, 8 or 16 heads: the shared-key-step kernel.
+#ifndef CSA_SCORE_GEMM_MIN_ROWS
+#define CSA_SCORE_GEMM_MIN_ROWS 512
+#endif
+  const long long rows_req = (long long)in.q_per_req * in.idx_heads;
+  if (in.dtype == 1 && !in.k_scale && rows_req >= CSA_SCORE_GEMM_MIN_ROWS &&
+      (in.idx_heads == 4 || in.idx_heads == 8 || in.idx_heads == 16)) {
+    const int tok_per_block = kGemmRows / in.idx_heads;
+    const int row_blocks = (in.q_per_req + tok_per_block - 1) / tok_per_block;
+    // a block's score rows are addressed with 32-bit byte offsets
+    if (row_blocks <= 65535 && (long long)tok_per_block * in.n_cap * 4 < 0x7FFFF000LL) {
+      const dim3 grid((n_bound + kGemmKeys - 1) / kGemmKeys, in.batch, row_blocks);
+      if (in.block_table)
+        return in.idx_dim == 128 ? launch_gemm<128, true>(in, grid, st) : launch_gemm<64, true>(in, grid, st);
+      return in.idx_dim == 128 ? launch_gemm<128, false>(in, grid, st) : launch_gemm<64, false>(in, grid, st);
+    }
+  }
   // Query rows per workgroup: all of a request's when they fit in 64 (decode),
   // else blocks of floor(64 / Hi) tokens (prefill chunks).
   ScoreArgs a = in;

@@ -287,9 +287,9 @@ def test_end_to_end_paged(fmt, bs):
 # prefill indexer: many query tokens per request (q_per_req = chunk length)
 # --------------------------------------------------------------------------
 
-def prefill_cfg(T, K, Hi, start, B=2, grid=False):
+def prefill_cfg(T, K, Hi, start, B=2, grid=False, Di=128):
     max_len = start + T
-    cfg = small_cfg(name="prefill", batch=B, q_per_req=T, topk=K, idx_heads=Hi,
+    cfg = small_cfg(name="prefill", batch=B, q_per_req=T, topk=K, idx_heads=Hi, idx_dim=Di,
                     n_cap=max(256, max_len // 4), win=64, w_cap=64 + T, heads=4,
                     max_len=max_len)
     inp = I.make_inputs(cfg, start_pos=np.full(B, start, np.int32))
@@ -323,9 +323,22 @@ def test_prefill_indexer_topk(T, K, Hi, start):
     assert np.array_equal(got2["topk_idx"], ref["topk_idx"])
 
 
-def test_prefill_indexer_exact_grid():
-    sh, inp = prefill_cfg(600, 256, 8, 1500, grid=True)
+@pytest.mark.parametrize("T,K,Hi,start,Di,bs", [
+    (600, 256, 8, 1500, 128, 0),      # partial last row block and key step
+    (333, 100, 4, 5000, 64, 0),
+    (200, 64, 16, 9000, 128, 0),
+    (700, 512, 8, 9300, 128, 0),      # several key blocks of 1024
+    (600, 256, 8, 1500, 128, 16),     # paged indexer cache
+    (333, 100, 4, 5000, 64, 64),
+])
+def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
+    # Dyadic inputs: every partial sum is exact on both sides, so scores and
+    # lists are bitwise equal.  Chunks of at least 512 query rows per request
+    # with 4, 8 or 16 heads take the shared-key-step score kernel.
+    sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
     ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    if bs:
+        inp = I.page_inputs(inp, bs, seed=T + bs, cmp=False)
     got = gpu_step(sh, inp, jobs=("score", "topk"))
     assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
     assert np.array_equal(got["topk_idx"], ref["topk_idx"])
