@@ -39,6 +39,13 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 // a cast of element 0 for every e, so vector elements must be extracted to a
 // scalar first.
 __device__ __forceinline__ float u32_as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+// relu(x) = x > 0 ? x : +0 as one integer max on the bits (negative floats,
+// -0 included, are negative integers).  Takes a scalar: pass vector elements
+// through a float variable (a bit cast written on an ext-vector element has
+// compiled to element 0 for every index).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
   return __builtin_bit_cast(float, h << 16);
@@ -118,6 +125,21 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS DMA: 16 bytes per lane from global memory (or a buffer) to LDS at
+// lds + 16 * lane.  Kept in device functions: a call of these builtins
+// written directly in a kernel body can keep the host compilation pass from
+// emitting the kernel's launch stub.
+template <int AUX>
+__device__ __forceinline__ void dma16_global(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, AUX);
+}
+template <int AUX>
+__device__ __forceinline__ void dma16_buffer(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voffset,
+                                             uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset,
+                                           soffset, 0, AUX);
 }
 
 // Workgroup barrier for LDS only: this wave's LDS operations complete, then

@@ -20,6 +20,8 @@
 // through a small per-wave LDS tile; either way in a fixed head order.  On the
 // register path the block's scores are written after its key stream, through
 // LDS, as contiguous streaming stores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -379,17 +381,18 @@ constexpr int kGemmKeys = 1024;                   // keys per block
 constexpr int kGemmBufs = 8;                      // key steps in the ring
 constexpr int kGemmStepKeys = 32;                 // one 32-key MFMA N tile
 
-// s_waitcnt vmcnt(n) for a run-time n in [0, 63]
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  switch (n) {
-#define CSA_VMCNT_CASE(N) case N: wait_vmcnt<N>(); break;
-#define CSA_VMCNT_CASE8(B) CSA_VMCNT_CASE(B) CSA_VMCNT_CASE(B + 1) CSA_VMCNT_CASE(B + 2) CSA_VMCNT_CASE(B + 3) \
-    CSA_VMCNT_CASE(B + 4) CSA_VMCNT_CASE(B + 5) CSA_VMCNT_CASE(B + 6) CSA_VMCNT_CASE(B + 7)
-    CSA_VMCNT_CASE8(0) CSA_VMCNT_CASE8(8) CSA_VMCNT_CASE8(16) CSA_VMCNT_CASE8(24)
-    CSA_VMCNT_CASE8(32) CSA_VMCNT_CASE8(40) CSA_VMCNT_CASE8(48) CSA_VMCNT_CASE8(56)
-#undef CSA_VMCNT_CASE8
-#undef CSA_VMCNT_CASE
-    default: wait_vmcnt<0>(); break;
+// wait_vmcnt for counts above the counter's range: waiting for more is safe
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_sat() {
+  wait_vmcnt<(N < 63 ? N : 63)>();
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, in order
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
 }
 
@@ -402,14 +405,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(Sco
   constexpr int MT = 2;                                // 32-row M tiles per wave
   constexpr int TPL = 16 / HI;                         // tokens per lane per M tile
   using TL = ScoreTile<ROW>;                           // 16-row tile layout (piece swizzle)
+  constexpr int NB = kGemmBufs;
   constexpr int STEP_BYTES = 2 * TL::BYTES;            // 32 keys
   constexpr int NSTEPS = kGemmKeys / kGemmStepKeys;
   constexpr int DPW = 2 * TL::NPT / kGemmWaves;        // DMA instructions per wave per step
   constexpr int NST = MT * TPL;                        // score stores per wave per step
   static_assert(DPW >= 1 && DPW * kGemmWaves == 2 * TL::NPT, "a step splits evenly over the waves");
   static_assert(HI == 4 || HI == 8 || HI == 16, "whole tokens per lane");
+  static_assert(NSTEPS >= 2 * NB, "a block spans at least two ring rounds");
 
-  __shared__ __attribute__((aligned(1024))) char ring[kGemmBufs][STEP_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[NB][STEP_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -445,7 +450,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(Sco
   // v % HI.  Rows past the block's tokens copy the last real row.
   u32x4_t qa[MT][KS];
   float wv[MT][16];
-  int nvt[MT][TPL];
+  uint32_t sbase[MT][TPL];   // byte offset of (token, key l32) in the block's score rows
+  int slim[MT][TPL];         // store while key0 + st*32 < slim (visible count - l32; 0: never)
   const char* qbase = static_cast<const char*>(a.q_idx) + tok0 * HI * ROW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -462,99 +468,154 @@ __global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(Sco
       wv[mt][v] = a.w[tok0 * HI + min(tile_row0 + half * TPL * HI + v, SH - 1)];
 #pragma unroll
     for (int tt = 0; tt < TPL; ++tt) {
-      const int s = (tile_row0 + (half * TPL + tt) * HI) / HI;
+      const int s = tile_row0 / HI + half * TPL + tt;
       const int nv = s < S ? min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap) : 0;
-      nvt[mt][tt] = nv > a.topk ? nv : 0;  // 0: not scored (past the block, or fits Top-K)
+      sbase[mt][tt] = (uint32_t)(min(s, S - 1) * a.n_cap + l32) * 4u;
+      slim[mt][tt] = nv > a.topk ? nv - l32 : INT32_MIN;   // past the block, or fits Top-K: never
     }
   }
   // scores of this block's tokens, addressed by buffer stores (32-bit offsets)
-  float* sblk = a.scores + tok0 * a.n_cap;
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sblk, (int)((size_t)S * a.n_cap * 4));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scores + tok0 * a.n_cap, (int)((size_t)S * a.n_cap * 4));
 
   // DMA of step st: instruction i = wave*DPW + d fills tile u = i / NPT, rows
   // k*RPI + lane/NPR (k = i % NPT) with the piece swizzle of the kernel above.
-  int lrow[DPW], loff[DPW];  // the lane's row within the step and its byte offset
+  // Dense keys: buffer loads against the request's key rows (rows past n_cap
+  // read as zero; rows past nmax are read and never used).  Paged keys: rows
+  // clamped to nmax - 1 and mapped through the block table.
+  int lrow[DPW];
+  uint32_t loff[DPW];
 #pragma unroll
   for (int d = 0; d < DPW; ++d) {
     const int i = wave * DPW + d, u = i / TL::NPT, k = i % TL::NPT;
     const int r = k * TL::RPI + lane / TL::NPR;
     const int piece = (lane % TL::NPR) ^ (r % TL::NPR);
     lrow[d] = u * 16 + r;
-    loff[d] = 16 * piece;
+    loff[d] = (uint32_t)(lrow[d] * ROW + 16 * piece);
   }
-  const char* kbase = static_cast<const char*>(a.k_idx);
-  auto issue_step = [&](int st) {
-    char* dst = ring[st % kGemmBufs];
+  const char* kreq = static_cast<const char*>(a.k_idx) + (PG ? 0 : (size_t)b * a.n_cap * ROW);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kreq, PG ? 0 : a.n_cap * ROW);
+  auto issue_step = [&](int st, int slot) {
+    char* dst = ring[slot];
     const int step0 = key0 + st * kGemmStepKeys;
-    const bool full = step0 + kGemmStepKeys <= nmax;  // uniform
 #pragma unroll
     for (int d = 0; d < DPW; ++d) {
       const int i = wave * DPW + d, u = i / TL::NPT, k = i % TL::NPT;
-      const char* src;
-      if (!PG && full) {
-        src = kbase + ((size_t)b * a.n_cap + step0) * ROW + (lrow[d] * ROW + loff[d]);
-      } else {
+      char* lds = dst + u * TL::BYTES + 1024 * k;
+      if constexpr (PG) {
         const int jt = min(step0 + u * 16, nmax - 1), j = min(step0 + lrow[d], nmax - 1);
-        size_t row;
-        if constexpr (PG) {
-          const int blk = __builtin_amdgcn_readlane(pblk, (jt >> a.block_shift) - (key0 >> a.block_shift));
-          row = ((size_t)blk << a.block_shift) + (size_t)(j & ((1 << a.block_shift) - 1));
-        } else {
-          (void)jt;
-          row = (size_t)b * a.n_cap + j;
-        }
-        src = kbase + row * ROW + loff[d];
+        const int blk = __builtin_amdgcn_readlane(pblk, (jt >> a.block_shift) - (key0 >> a.block_shift));
+        const size_t row = ((size_t)blk << a.block_shift) + (size_t)(j & ((1 << a.block_shift) - 1));
+        dma16_global<kNonTemporal>(kreq + row * ROW + (loff[d] - (uint32_t)(lrow[d] * ROW)), lds);
+      } else {
+        dma16_buffer<kNonTemporal>(krs, lds, loff[d], (uint32_t)(step0 * ROW));
       }
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + u * TL::BYTES + 1024 * k),
-                                       16, 0, kNonTemporal);
     }
   };
-  // A fixed number of steps in flight (steps past nsteps read clamped rows
-  // and are never consumed), then one wait that covers the query and weight
-  // loads, which are older than every DMA.
-#pragma unroll
-  for (int st = 0; st < kGemmBufs - 1; ++st) issue_step(st);
-  wait_vmcnt<(kGemmBufs - 1) * DPW>();
 
-  for (int st = 0; st < nsteps; ++st) {
-    // Step st is in once at most the younger operations are outstanding: the
-    // DMA of the younger steps in flight and the score stores issued since
-    // (NST per step, all steps so far, at most kGemmBufs - 1 of them after it).
-    wait_vmcnt_rt(min(63, DPW * min(kGemmBufs - 2, nsteps - 1 - st) + NST * min(st, kGemmBufs - 1)));
+  // One step: publish it, refill the buffer freed by the previous step, run
+  // its 16 MFMAs, and meanwhile finish the previous step: head sums and NST
+  // unconditional score stores (the first step's are dummies past the buffer,
+  // so every step issues the same count).  The two are independent, so the
+  // matrix core and the vector ALU overlap within the wave.
+  f32x16_t acc_prev[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc_prev[mt] = f32x16_t{};
+  auto finish = [&](const f32x16_t (&acc)[MT], int st_done) {
+    const int jb = key0 + st_done * kGemmStepKeys;  // key of lane l32 = jb + l32; st_done < 0: dummy
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int tt = 0; tt < TPL; ++tt) {
+        // heads in ascending order; relu as one integer max on the bits
+        float sum = 0.0f;
+#pragma unroll
+        for (int h = 0; h < HI; ++h) {
+          const float x = acc[mt][tt * HI + h];
+          sum += wv[mt][tt * HI + h] * relu_bits(x);
+        }
+        const uint32_t off = st_done >= 0 && jb < slim[mt][tt] ? sbase[mt][tt] + (uint32_t)jb * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), srs, off, 0, kNonTemporal);
+      }
+    }
+  };
+  auto run_step = [&](int st, int slot, int issue_slot, bool issue) {
     block_lds_barrier();  // every wave's share of step st is in; step st - 1 is read by all
-    if (st + kGemmBufs - 1 < nsteps) issue_step(st + kGemmBufs - 1);  // into step st - 1's buffer
-    const char* src = ring[st % kGemmBufs];
-    // B operand: key l32 of the step, dims 16*ks + 8*half .. +8
-    const int u = l32 >> 4, r = l32 & 15;
+    if (issue) issue_step(st + NB - 1, issue_slot);
+    const char* src = ring[slot];
+    const int u = l32 >> 4, r = l32 & 15;  // B operand: key l32, dims 16*ks + 8*half .. +8
     f32x16_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int slot = (2 * ks + half) ^ (r % TL::NPR);
-      const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(src + u * TL::BYTES + r * ROW + 16 * slot);
+      const int sl = (2 * ks + half) ^ (r % TL::NPR);
+      const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(src + u * TL::BYTES + r * ROW + 16 * sl);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[mt][ks]),
                                                           __builtin_bit_cast(bf16x8_t, kb), acc[mt], 0, 0, 0);
     }
-    const int j = key0 + st * kGemmStepKeys + l32;
+    finish(acc_prev, st - 1);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) acc_prev[mt] = acc[mt];
+  };
+
+  // A fixed number of steps in flight (steps past nsteps load rows that are
+  // never consumed; the last wait covers them), then one wait that covers the
+  // query and weight loads, which are older than every DMA.
 #pragma unroll
-      for (int tt = 0; tt < TPL; ++tt) {
-        float sum = 0.0f;  // heads in ascending order
-#pragma unroll
-        for (int h = 0; h < HI; ++h) {
-          const float d = acc[mt][tt * HI + h];
-          sum += wv[mt][tt * HI + h] * (d > 0.0f ? d : 0.0f);
-        }
-        const int s = (wave * 64 + mt * 32) / HI + half * TPL + tt;   // token in the block
-        const uint32_t off = j < nvt[mt][tt] ? (uint32_t)(s * a.n_cap + j) * 4u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), srs, off, 0, kNonTemporal);
-      }
+  for (int st = 0; st < NB - 1; ++st) issue_step(st, st);
+  wait_vmcnt<(NB - 1) * DPW>();
+
+  // Step st is in once at most the younger operations are outstanding: the
+  // DMA of up to NB - 2 younger steps and the stores of the up to NB - 1
+  // steps computed since its DMA was issued (vector memory operations retire
+  // in order).  Full rounds of NB steps run unrolled with constant waits and
+  // buffers; the tail counts at run time (fewer stores counted: a longer,
+  // still correct wait).
+  int st = 0;
+  if (nsteps >= 2 * NB - 1) {  // first round: all NB - 2 younger steps issued, st stores since
+    static_for<0, NB>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      wait_vmcnt_sat<DPW * (NB - 2) + NST * u>();
+      run_step(u, u, (u + NB - 1) % NB, true);
+    });
+    st = NB;
+    for (; st + 2 * NB - 1 <= nsteps; st += NB) {  // steady rounds
+      static_for<0, NB>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        wait_vmcnt_sat<DPW * (NB - 2) + NST * (NB - 1)>();
+        run_step(st + u, u, (u + NB - 1) % NB, true);
+      });
     }
   }
+  for (; st < nsteps; ++st) {  // tail
+    const int younger = min(NB - 2, nsteps - 1 - st);
+    if (st >= NB - 1) {
+      switch (younger) {
+        case 0: wait_vmcnt_sat<NST * (NB - 1)>(); break;
+        case 1: wait_vmcnt_sat<DPW * 1 + NST * (NB - 1)>(); break;
+        case 2: wait_vmcnt_sat<DPW * 2 + NST * (NB - 1)>(); break;
+        case 3: wait_vmcnt_sat<DPW * 3 + NST * (NB - 1)>(); break;
+        case 4: wait_vmcnt_sat<DPW * 4 + NST * (NB - 1)>(); break;
+        case 5: wait_vmcnt_sat<DPW * 5 + NST * (NB - 1)>(); break;
+        default: wait_vmcnt_sat<DPW * 6 + NST * (NB - 1)>(); break;
+      }
+    } else {
+      switch (younger) {
+        case 0: wait_vmcnt_sat<0>(); break;
+        case 1: wait_vmcnt_sat<DPW * 1>(); break;
+        case 2: wait_vmcnt_sat<DPW * 2>(); break;
+        case 3: wait_vmcnt_sat<DPW * 3>(); break;
+        case 4: wait_vmcnt_sat<DPW * 4>(); break;
+        case 5: wait_vmcnt_sat<DPW * 5>(); break;
+        default: wait_vmcnt_sat<DPW * 6>(); break;
+      }
+    }
+    run_step(st, st % NB, (st + NB - 1) % NB, st + NB - 1 < nsteps);
+  }
+  finish(acc_prev, nsteps - 1);
+  wait_vmcnt<0>();  // no DMA may still be writing this block's LDS when it exits
 }
 
 template <int DI, bool PG>
@@ -620,8 +681,9 @@ hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
       (in.idx_heads == 4 || in.idx_heads == 8 || in.idx_heads == 16)) {
     const int tok_per_block = kGemmRows / in.idx_heads;
     const int row_blocks = (in.q_per_req + tok_per_block - 1) / tok_per_block;
-    // a block's score rows are addressed with 32-bit byte offsets
-    if (row_blocks <= 65535 && (long long)tok_per_block * in.n_cap * 4 < 0x7FFFF000LL) {
+    // a block's score rows and a request's key rows are addressed with 32-bit byte offsets
+    if (row_blocks <= 65535 && (long long)tok_per_block * in.n_cap * 4 < 0x7FFFF000LL &&
+        (long long)in.n_cap * in.idx_dim * 2 < 0x7FFFF000LL) {
       const dim3 grid((n_bound + kGemmKeys - 1) / kGemmKeys, in.batch, row_blocks);
       if (in.block_table)
         return in.idx_dim == 128 ? launch_gemm<128, true>(in, grid, st) : launch_gemm<64, true>(in, grid, st);
