@@ -416,6 +416,17 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
   const int tid = threadIdx.x;
   const int tok = blockIdx.x;
   const int S = a.q_per_req, b = tok / S, s = tok % S;
+  const float* row = a.scores + (size_t)tok * a.n_cap;
+  const int i0 = tid * KPT;
+  // The 16-byte loads of the thread's slice do not depend on the position,
+  // so they are issued before it arrives (a token that fits Top-K discards
+  // them); nothing past n_cap is read.
+  const bool vec_slice = VEC4 && i0 + KPT <= a.n_cap;
+  float4 raw[VEC4 ? KPT / 4 : 1];
+  if (vec_slice) {
+#pragma unroll
+    for (int j = 0; j < KPT; j += 4) raw[j / 4] = *reinterpret_cast<const float4*>(row + i0 + j);
+  }
   const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
   const int n = min(n_visible(p, a.ratio), a.n_cap);
   const int K = a.topk;
@@ -427,15 +438,12 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
   }
 
   // ---- the row, in registers.  Slots past n hold a copy of a valid key of
-  // the same thread (or of row n-1), so they never widen the key range;
-  // nothing past n_cap is read.
-  const float* row = a.scores + (size_t)tok * a.n_cap;
-  const int i0 = tid * KPT;
+  // the same thread (or of row n-1), so they never widen the key range.
   uint32_t key[KPT];
-  if (VEC4 && i0 + KPT <= a.n_cap) {
+  if (vec_slice) {
 #pragma unroll
     for (int j = 0; j < KPT; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i0 + j);
+      const float4 v = raw[j / 4];
       key[j] = order_key(v.x);
       key[j + 1] = order_key(v.y);
       key[j + 2] = order_key(v.z);
@@ -462,7 +470,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
     // which exists for the first m threads (closed form, no scan).
     // Two 8-bit passes over the full key range fix the top 16 key bits: the
     // threshold is the lower edge of the 16-bit bin holding the sample rank,
-    // which only keeps a few more rows.
+    // which keeps somewhat more rows than the sample rank alone.
     const int js = tid % KPT;
     uint32_t sk = 0u;  // key[js] without a dynamic register index
 #pragma unroll
