@@ -364,8 +364,14 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
 
 // Candidate buffer: rows whose key clears the sampled threshold, kept as
 // (key, row index) pairs in ascending row order.
-constexpr int kCandCap = 8192;
-constexpr int kCandSlots = kCandCap + kWave;  // + one spare slot per lane
+// Candidate capacity of a block of NW waves: 16-wave blocks (decode) keep
+// up to 8192 candidates; 4-wave blocks (launches of many tokens) 2048, so
+// that their LDS stays small and several share a CU (4096 measured slower on
+// prefill chunks: 141 us against 110 us for 8192 rows of 7168-8192 keys).
+#ifndef CSA_TOPK_SMALL_CAND_CAP
+#define CSA_TOPK_SMALL_CAND_CAP 2048
+#endif
+constexpr int cand_cap(int nw) { return nw >= 16 ? 8192 : CSA_TOPK_SMALL_CAND_CAP; }
 
 
 // Ascending-index emission of the selection {key > T} plus the keq
@@ -410,6 +416,8 @@ __device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, i
 template <int NW, int KPT, bool VEC4>
 __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
   constexpr int NT = NW * kWave;
+  constexpr int kCandCap = cand_cap(NW);
+  constexpr int kCandSlots = kCandCap + kWave;  // + one spare slot per lane
   constexpr bool kCandPath = NT * KPT > kCandCap;
   __shared__ SelectSmem<NW> sm;
 
@@ -463,7 +471,9 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 1; j < KPT; ++j) kmax = max(kmax, key[j]);
 
-  if constexpr (kCandPath) if (n > kCandCap) {
+  // (a sampled threshold keeps somewhat more than K rows: only tried while
+  // K leaves room for that in the buffer)
+  if constexpr (kCandPath) if (n > kCandCap && 2 * K <= kCandCap) {
     __shared__ uint2 cand[kCandSlots];  // (key, row index)
     constexpr int kCandPerThread = kCandCap / NT;
     // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT,
@@ -569,7 +579,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 #ifndef CSA_TOPK_SMALL_BLOCK_TOKENS
 #define CSA_TOPK_SMALL_BLOCK_TOKENS 2048
 #endif
-  if (tokens >= CSA_TOPK_SMALL_BLOCK_TOKENS && launch_reg_sized<4>(a, n_bound, vec4, st))
+#ifndef CSA_TOPK_SMALL_BLOCK_WAVES
+#define CSA_TOPK_SMALL_BLOCK_WAVES 4
+#endif
+  if (tokens >= CSA_TOPK_SMALL_BLOCK_TOKENS && launch_reg_sized<CSA_TOPK_SMALL_BLOCK_WAVES>(a, n_bound, vec4, st))
     return hipGetLastError();
   if (!launch_reg_sized<kTopkWaves>(a, n_bound, vec4, st))
     hipLaunchKernelGGL(topk_global_kernel, dim3(a.batch * a.q_per_req), dim3(kTopkThreads), 0, st, a);

@@ -447,12 +447,15 @@ def test_topk_exact_synthetic(kind, n_cap, topk):
     assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
 
 
-@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero"])
-@pytest.mark.parametrize("n_cap,topk", [(8192, 1024), (1000, 100), (4100, 1024), (2049, 2048)])
+@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero", "spiked16"])
+@pytest.mark.parametrize("n_cap,topk", [(8192, 1024), (1000, 100), (4100, 1024), (2049, 2048),
+                                        (8192, 700), (3000, 1000)])
 def test_topk_many_tokens(kind, n_cap, topk):
     # 2080 tokens: the launch takes the small-block selection (several blocks
-    # per CU).  Causal rows of every length from below K to n_cap, bypass
-    # tokens included; 4100 is not a multiple of the per-thread slice.
+    # per CU; rows past 2048 keys try a sampled threshold over a 2048-entry
+    # candidate buffer, and fall back to the whole row when it misleads).
+    # Causal rows of every length from below K to n_cap, bypass tokens
+    # included; 4100 is not a multiple of the per-thread slice.
     B, S = 4, 520
     sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=S + 8,
                  heads=1, head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1,
