@@ -330,6 +330,7 @@ def test_prefill_indexer_topk(T, K, Hi, start):
     (700, 512, 8, 9300, 128, 0),      # several key blocks of 1024
     (600, 256, 8, 1500, 128, 16),     # paged indexer cache
     (333, 100, 4, 5000, 64, 64),
+    (300, 150, 8, 500, 128, 0),       # blocks mixing tokens that fit Top-K with scored ones
 ])
 def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
     # Dyadic inputs: every partial sum is exact on both sides, so scores and
