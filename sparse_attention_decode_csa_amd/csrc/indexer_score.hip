@@ -378,7 +378,16 @@ constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = kGemmWaves * kWave;
 constexpr int kGemmRows = kGemmWaves * 64;        // query rows per block
 constexpr int kGemmKeys = 1024;                   // keys per block
-constexpr int kGemmBufs = 8;                      // key steps in the ring
+#ifndef CSA_GEMM_BUFS
+#define CSA_GEMM_BUFS 8
+#endif
+#ifndef CSA_GEMM_BLOCKS_PER_CU
+#define CSA_GEMM_BLOCKS_PER_CU 2
+#endif
+#ifndef CSA_GEMM_OVERLAP
+#define CSA_GEMM_OVERLAP 1
+#endif
+constexpr int kGemmBufs = CSA_GEMM_BUFS;          // key steps in the ring
 constexpr int kGemmStepKeys = 32;                 // one 32-key MFMA N tile
 
 // wait_vmcnt for counts above the counter's range: waiting for more is safe
@@ -397,7 +406,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int DI, int HI, bool PG>
-__global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_score_gemm_kernel(ScoreArgs a) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
   constexpr int ROW = DI * 2;                          // bytes per query / key row
@@ -555,9 +564,13 @@ __global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(Sco
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[mt][ks]),
                                                           __builtin_bit_cast(bf16x8_t, kb), acc[mt], 0, 0, 0);
     }
+#if CSA_GEMM_OVERLAP
     finish(acc_prev, st - 1);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc_prev[mt] = acc[mt];
+#else
+    finish(acc, st);
+#endif
   };
 
   // A fixed number of steps in flight (steps past nsteps load rows that are
@@ -614,7 +627,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void indexer_score_gemm_kernel(Sco
     }
     run_step(st, st % NB, (st + NB - 1) % NB, st + NB - 1 < nsteps);
   }
+#if CSA_GEMM_OVERLAP
   finish(acc_prev, nsteps - 1);
+#endif
   wait_vmcnt<0>();  // no DMA may still be writing this block's LDS when it exits
 }
 
