@@ -109,8 +109,15 @@ def _check(fn: str, code: int):
         raise CsaError(fn, code, status_string(code))
 
 
-def _dev(t: Optional[torch.Tensor], name: str):
-    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+def _dev(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None,
+         dtype: Optional[torch.dtype] = None, esize: Optional[int] = None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL).
+
+    The C ABI takes pointers only, so a tensor smaller than the shape implies
+    would be read or written past its end on the device: with `numel` the
+    tensor must hold at least that many elements, with `dtype` exactly that
+    element type, with `esize` elements of that many bytes (for copies, which
+    take any type of the right width)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
@@ -119,6 +126,12 @@ def _dev(t: Optional[torch.Tensor], name: str):
         raise ValueError(f"{name}: tensor must live on the GPU (no CPU path exists)")
     if not t.is_contiguous():
         raise ValueError(f"{name}: tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if esize is not None and t.element_size() != esize:
+        raise TypeError(f"{name}: expected {esize}-byte elements, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the shape needs {numel}")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -140,25 +153,39 @@ def sparse_attn_workspace_bytes(shape) -> int:
     return int(lib().csa_sparse_attn_workspace_bytes(ctypes.byref(CShape.of(shape))))
 
 
+def _sizes(shape) -> dict:
+    """Element counts the shape implies for each tensor of the step."""
+    B, S, Hi, Di = shape.batch, shape.q_per_req, shape.idx_heads, shape.idx_dim
+    return dict(q_idx=B * S * Hi * Di, w=B * S * Hi, k_idx=B * shape.n_cap * Di, start_pos=B,
+                scores=B * S * shape.n_cap, topk_idx=B * S * shape.topk,
+                q=B * S * shape.heads * shape.head_dim, win=B * shape.w_cap * shape.head_dim,
+                cmp=B * shape.n_cap * shape.head_dim, k_scale=B * shape.n_cap)
+
+
 def indexer_score(shape, q_idx, w, k_idx, start_pos, scores, stream=None) -> None:
-    cs = CShape.of(shape)
+    cs, n, dt = CShape.of(shape), _sizes(shape), torch_dtype(shape)
     _check("csa_indexer_score", lib().csa_indexer_score(
-        ctypes.byref(cs), _dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx, "k_idx"),
-        _dev(start_pos, "start_pos"), _dev(scores, "scores"), _stream(stream)))
+        ctypes.byref(cs), _dev(q_idx, "q_idx", n["q_idx"], dt), _dev(w, "w", n["w"], torch.float32),
+        _dev(k_idx, "k_idx", n["k_idx"], dt), _dev(start_pos, "start_pos", n["start_pos"], torch.int32),
+        _dev(scores, "scores", n["scores"], torch.float32), _stream(stream)))
 
 
 def indexer_score_fp8(shape, q_idx, w, k_idx8, k_scale, start_pos, scores, stream=None) -> None:
-    cs = CShape.of(shape)
+    cs, n = CShape.of(shape), _sizes(shape)
     _check("csa_indexer_score_fp8", lib().csa_indexer_score_fp8(
-        ctypes.byref(cs), _dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_idx8, "k_idx8"),
-        _dev(k_scale, "k_scale"), _dev(start_pos, "start_pos"), _dev(scores, "scores"),
-        _stream(stream)))
+        ctypes.byref(cs), _dev(q_idx, "q_idx", n["q_idx"], torch.bfloat16),
+        _dev(w, "w", n["w"], torch.float32), _dev(k_idx8, "k_idx8", n["k_idx"], torch.uint8),
+        _dev(k_scale, "k_scale", n["k_scale"], torch.float32),
+        _dev(start_pos, "start_pos", n["start_pos"], torch.int32),
+        _dev(scores, "scores", n["scores"], torch.float32), _stream(stream)))
 
 
-def _pages(pool, block_table, name: str) -> CPages:
+def _pages(shape, pool, block_table, name: str) -> CPages:
     """csa_pages_t of a pool [n_blocks, block_size, ...] and its table [B, blocks_per_req]."""
     if pool.dim() < 2 or block_table.dim() != 2 or block_table.dtype != torch.int32:
         raise ValueError(f"{name}: pool [n_blocks, block_size, ...] and int32 table [B, bpr] expected")
+    if block_table.shape[0] < shape.batch:
+        raise ValueError(f"{name}: block table has {block_table.shape[0]} rows for {shape.batch} requests")
     return CPages(_dev(block_table, name + " block_table"), int(block_table.shape[1]),
                   int(pool.shape[1]), int(pool.shape[0]))
 
@@ -167,32 +194,51 @@ def indexer_score_paged(shape, q_idx, w, k_pool, k_scale, block_table, start_pos
                         stream=None) -> None:
     """k_pool [n_blocks, block_size, Di] (shape.dtype keys, or uint8 E4M3 codes
     with k_scale [n_blocks, block_size] float32); block_table [B, bpr] int32."""
-    cs = CShape.of(shape)
-    pg = _pages(k_pool, block_table, "k_pool")
+    cs, n, dt = CShape.of(shape), _sizes(shape), torch_dtype(shape)
+    pg = _pages(shape, k_pool, block_table, "k_pool")
+    rows = pg.n_blocks * pg.block_size
+    kdt = torch.uint8 if k_scale is not None else dt
     _check("csa_indexer_score_paged", lib().csa_indexer_score_paged(
-        ctypes.byref(cs), _dev(q_idx, "q_idx"), _dev(w, "w"), _dev(k_pool, "k_pool"),
-        _dev(k_scale, "k_scale"), ctypes.byref(pg), _dev(start_pos, "start_pos"),
-        _dev(scores, "scores"), _stream(stream)))
+        ctypes.byref(cs), _dev(q_idx, "q_idx", n["q_idx"], torch.bfloat16 if k_scale is not None else dt),
+        _dev(w, "w", n["w"], torch.float32), _dev(k_pool, "k_pool", rows * shape.idx_dim, kdt),
+        _dev(k_scale, "k_scale", rows, torch.float32), ctypes.byref(pg),
+        _dev(start_pos, "start_pos", n["start_pos"], torch.int32),
+        _dev(scores, "scores", n["scores"], torch.float32), _stream(stream)))
 
 
 def topk(shape, scores, start_pos, topk_idx, ws=None, stream=None) -> None:
-    cs = CShape.of(shape)
+    cs, n = CShape.of(shape), _sizes(shape)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("csa_topk", lib().csa_topk(
-        ctypes.byref(cs), _dev(scores, "scores"), _dev(start_pos, "start_pos"),
-        _dev(topk_idx, "topk_idx"), _dev(ws, "ws"), nbytes, _stream(stream)))
+        ctypes.byref(cs), _dev(scores, "scores", n["scores"], torch.float32),
+        _dev(start_pos, "start_pos", n["start_pos"], torch.int32),
+        _dev(topk_idx, "topk_idx", n["topk_idx"], torch.int32), _dev(ws, "ws"), nbytes,
+        _stream(stream)))
+
+
+def _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out):
+    """Pointers of the arguments both attention entries share, size-checked."""
+    n, dt = _sizes(shape), torch_dtype(shape)
+    rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
+    half = shape.rope_dim // 2
+    return dict(q=_dev(q, "q", n["q"], dt), k_win=_dev(k_win, "k_win", n["win"], dt),
+                v_win=_dev(v_win, "v_win", n["win"], dt),
+                topk_idx=_dev(topk_idx, "topk_idx", n["topk_idx"], torch.int32),
+                start_pos=_dev(start_pos, "start_pos", n["start_pos"], torch.int32),
+                rope_cos=_dev(rope_cos, "rope_cos", rope_rows * half, torch.float32),
+                rope_sin=_dev(rope_sin, "rope_sin", rope_rows * half, torch.float32),
+                rope_rows=rope_rows, out=_dev(out, "out", n["q"], dt))
 
 
 def sparse_attn_decode(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos, rope_cos,
                        rope_sin, softmax_scale, out, ws, stream=None) -> None:
-    cs = CShape.of(shape)
-    rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
+    cs, n, dt = CShape.of(shape), _sizes(shape), torch_dtype(shape)
+    c = _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("csa_sparse_attn_decode", lib().csa_sparse_attn_decode(
-        ctypes.byref(cs), _dev(q, "q"), _dev(k_win, "k_win"), _dev(v_win, "v_win"),
-        _dev(k_cmp, "k_cmp"), _dev(v_cmp, "v_cmp"), _dev(topk_idx, "topk_idx"),
-        _dev(start_pos, "start_pos"), _dev(rope_cos, "rope_cos"), _dev(rope_sin, "rope_sin"),
-        rope_rows, float(softmax_scale), _dev(out, "out"), _dev(ws, "ws"), nbytes,
+        ctypes.byref(cs), c["q"], c["k_win"], c["v_win"], _dev(k_cmp, "k_cmp", n["cmp"], dt),
+        _dev(v_cmp, "v_cmp", n["cmp"], dt), c["topk_idx"], c["start_pos"], c["rope_cos"],
+        c["rope_sin"], c["rope_rows"], float(softmax_scale), c["out"], _dev(ws, "ws"), nbytes,
         _stream(stream)))
 
 
@@ -200,31 +246,34 @@ def sparse_attn_decode_paged(shape, q, k_win, v_win, k_pool, v_pool, block_table
                              start_pos, rope_cos, rope_sin, softmax_scale, out, ws,
                              stream=None) -> None:
     """k_pool/v_pool [n_blocks, block_size, D] sharing block_table [B, bpr] int32."""
-    cs = CShape.of(shape)
+    cs, dt = CShape.of(shape), torch_dtype(shape)
     if k_pool.shape != v_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
-    pg = _pages(k_pool, block_table, "k_pool")
-    rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
+    pg = _pages(shape, k_pool, block_table, "k_pool")
+    rows = pg.n_blocks * pg.block_size
+    c = _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("csa_sparse_attn_decode_paged", lib().csa_sparse_attn_decode_paged(
-        ctypes.byref(cs), _dev(q, "q"), _dev(k_win, "k_win"), _dev(v_win, "v_win"),
-        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), ctypes.byref(pg),
-        _dev(topk_idx, "topk_idx"), _dev(start_pos, "start_pos"), _dev(rope_cos, "rope_cos"),
-        _dev(rope_sin, "rope_sin"), rope_rows, float(softmax_scale), _dev(out, "out"),
-        _dev(ws, "ws"), nbytes, _stream(stream)))
+        ctypes.byref(cs), c["q"], c["k_win"], c["v_win"],
+        _dev(k_pool, "k_pool", rows * shape.head_dim, dt), _dev(v_pool, "v_pool", rows * shape.head_dim, dt),
+        ctypes.byref(pg), c["topk_idx"], c["start_pos"], c["rope_cos"], c["rope_sin"],
+        c["rope_rows"], float(softmax_scale), c["out"], _dev(ws, "ws"), nbytes, _stream(stream)))
 
 
 def swa_writeback(shape, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """k_new/v_new [B*S, D]; k_cache/v_cache [n_slots, D] (any leading shape
     whose rows are D elements, e.g. the [B, w_cap, D] rings)."""
     cs = CShape.of(shape)
+    es = 2 if shape.dtype == BF16 else 4  # a row copy: any element type of that width
     if k_cache.numel() != v_cache.numel():
         raise ValueError("k_cache and v_cache must hold the same number of rows")
     n_slots = k_cache.numel() // shape.head_dim
+    T = shape.batch * shape.q_per_req
     _check("csa_swa_writeback", lib().csa_swa_writeback(
-        ctypes.byref(cs), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
-        _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        n_slots, _stream(stream)))
+        ctypes.byref(cs), _dev(k_new, "k_new", T * shape.head_dim, esize=es),
+        _dev(v_new, "v_new", T * shape.head_dim, esize=es),
+        _dev(slot_mapping, "slot_mapping", T, torch.int32), _dev(k_cache, "k_cache", esize=es),
+        _dev(v_cache, "v_cache", esize=es), n_slots, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

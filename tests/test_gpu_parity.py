@@ -604,11 +604,37 @@ def test_empty_batch_is_a_noop():
     sh = small_cfg().shape.replace(batch=0)
     z = torch.zeros(16, dtype=torch.int32, device="cuda")
     f = torch.zeros(16, dtype=torch.float32, device="cuda")
-    C.indexer_score(sh, f, f, f, z, f)
+    h = torch.zeros(16, dtype=torch.bfloat16, device="cuda")   # the shape's dtype is bf16
+    r = torch.zeros((1, sh.rope_dim // 2), dtype=torch.float32, device="cuda")  # one table row
+    C.indexer_score(sh, h, f, h, z, f)
     C.topk(sh, f, z, z)
-    C.sparse_attn_decode(sh, f, f, f, f, f, z, z, f, f, 0.1, f, f)
+    C.sparse_attn_decode(sh, h, h, h, h, h, z, z, r, r, 0.1, h, f)
     torch.cuda.synchronize()
-    assert int(z.abs().sum()) == 0 and float(f.abs().sum()) == 0.0
+    assert int(z.abs().sum()) == 0 and float(f.abs().sum()) == 0.0 and float(h.float().abs().sum()) == 0.0
+
+
+def test_binding_refuses_short_or_mistyped_tensors():
+    # the C ABI takes pointers only: the binding checks every tensor against
+    # the shape before any launch, so nothing runs past a buffer's end
+    cfg = small_cfg()
+    sh, inp = cfg.shape, I.make_inputs(cfg)
+    d = C.to_device(inp, sh)
+    bufs = C.alloc_outputs(sh)
+    with pytest.raises(ValueError, match="k_idx"):
+        C.indexer_score(sh, d["q_idx"], d["w"], d["k_idx"][:-1], d["start_pos"], bufs["scores"])
+    with pytest.raises(TypeError, match="w"):
+        C.indexer_score(sh, d["q_idx"], d["w"].double(), d["k_idx"], d["start_pos"], bufs["scores"])
+    with pytest.raises(ValueError, match="topk_idx"):
+        C.topk(sh, bufs["scores"], d["start_pos"], bufs["topk_idx"].reshape(-1)[:-1])
+    with pytest.raises(ValueError, match="v_cmp"):
+        C.sparse_attn_decode(sh, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"][:1],
+                             bufs["topk_idx"], d["start_pos"], d["rope_cos"], d["rope_sin"],
+                             I.softmax_scale(sh), bufs["out"], bufs["attn_ws"])
+    with pytest.raises(ValueError, match="rope_sin"):
+        C.sparse_attn_decode(sh, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"],
+                             bufs["topk_idx"], d["start_pos"], d["rope_cos"], d["rope_sin"][:, :1].contiguous(),
+                             I.softmax_scale(sh), bufs["out"], bufs["attn_ws"])
+    torch.cuda.synchronize()
 
 
 def test_refused_call_leaves_outputs_untouched():
