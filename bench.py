@@ -39,7 +39,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=3,
+                    help="least number of oracle runs for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle runs repeat until this much CPU time has passed")
     ap.add_argument("--key-format", choices=("bf16", "fp8"), default="bf16",
                     help="indexer key cache: bf16 rows, or FP8 E4M3 codes with a per-row scale")
     ap.add_argument("--writeback", action="store_true",
@@ -324,17 +327,20 @@ def main():
             jobs, n_tok, what = oracle.JOB_SCORE | oracle.JOB_TOPK, min(T, 1024), "scoring + Top-K"
         else:
             jobs, n_tok, what = (oracle.JOB_ATTN if cfg.supplied_topk else 7), T, "the full step"
-        for _ in range(max(1, args.cpu_reps)):
+        # at least cpu_reps runs and about cpu_seconds of oracle work in all
+        # (bounded: 200 runs, or one run past a minute)
+        while len(times) < 200:
             t0 = time.perf_counter()
             oracle.run(sh, inp, nthreads=nthreads, jobs=jobs, tokens=(0, n_tok))
             times.append(time.perf_counter() - t0)
-            if times[-1] > 60:
+            if times[-1] > 60 or (len(times) >= max(1, args.cpu_reps)
+                                  and sum(times) >= args.cpu_seconds):
                 break
         tc = float(np.median(times))
         cpu = {"value": round(n_tok / tc, 2), "unit": "query-tokens/s", "cores": nthreads,
                "kind": "oracle",
                "sample": f"{what} of {n_tok} of this workload's {T} query tokens, median of "
-                         f"{len(times)} runs, {tc:.2f} s each, fp64 oracle"}
+                         f"{len(times)} runs ({sum(times):.1f} s in all), {tc:.2f} s each, fp64 oracle"}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4

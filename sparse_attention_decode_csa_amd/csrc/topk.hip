@@ -417,7 +417,6 @@ template <int NW, int KPT, bool VEC4>
 __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
   constexpr int NT = NW * kWave;
   constexpr int kCandCap = cand_cap(NW);
-  constexpr int kCandSlots = kCandCap + kWave;  // + one spare slot per lane
   constexpr bool kCandPath = NT * KPT > kCandCap;
   __shared__ SelectSmem<NW> sm;
 
@@ -474,7 +473,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
   // (a sampled threshold keeps somewhat more than K rows: only tried while
   // K leaves room for that in the buffer)
   if constexpr (kCandPath) if (n > kCandCap && 2 * K <= kCandCap) {
-    __shared__ uint2 cand[kCandSlots];  // (key, row index)
+    __shared__ uint2 cand[kCandCap];  // (key, row index)
     constexpr int kCandPerThread = kCandCap / NT;
     // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT,
     // which exists for the first m threads (closed form, no scan).
@@ -505,13 +504,12 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
     uint32_t row_max;
     int pos = block_exclusive_scan_max<NW>(mine, kmax, sm.red, c, row_max);
     if (c >= K && c <= kCandCap) {  // block-uniform
-      // branch-free: every slot is written, a non-candidate into this lane's
-      // spare slot past the buffer
-      const int spare = kCandCap + (tid & (kWave - 1));
+      // only candidates are written (measured a little faster than writing
+      // every slot with the misses sent to a spare slot)
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const bool hit = valid(j) && key[j] >= tau;
-        cand[hit ? pos : spare] = make_uint2(key[j], (uint32_t)(i0 + j));
+        if (hit) cand[pos] = make_uint2(key[j], (uint32_t)(i0 + j));
         pos += hit ? 1 : 0;
       }
       __syncthreads();
