@@ -29,7 +29,7 @@ namespace csa {
 namespace {
 
 #ifndef CSA_SCORE_TILES_PER_WAVE
-#define CSA_SCORE_TILES_PER_WAVE 16
+#define CSA_SCORE_TILES_PER_WAVE 8
 #endif
 #ifndef CSA_SCORE_TILE_BUFFERS
 #define CSA_SCORE_TILE_BUFFERS 4
@@ -37,7 +37,7 @@ namespace {
 constexpr int kScoreWaves = 4;
 constexpr int kScoreTilesPerWave = CSA_SCORE_TILES_PER_WAVE;               // 16-key tiles
 constexpr int kScoreBufs = CSA_SCORE_TILE_BUFFERS;                         // tiles in flight per wave
-constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 1024
+constexpr int kScoreKeysPerBlock = kScoreWaves * kScoreTilesPerWave * 16;  // 512
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
@@ -93,7 +93,7 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // scale * sum_h w_h relu(q_h . c) = sum_h w_h relu(q_h . (scale * c))).
 // PG: the key cache (and the FP8 scales) are pools of blocks located through
 // a per-request block table; the workgroup loads the table entries of its
-// 1024 keys once, one per lane, and each tile takes its block from one lane
+// 512 keys once, one per lane, and each tile takes its block from one lane
 // (blocks are at least 16 rows, so a 16-row tile never straddles two).
 template <typename T, int DI, int MT, int HI, bool KF8, bool PG>
 __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
