@@ -46,7 +46,8 @@ csa_status_t check_pages(const csa_shape_t* sh, const csa_pages_t* pg, int64_t r
   if (bs < 16 || bs > 4096 || (bs & (bs - 1))) return CSA_ERR_BAD_SHAPE;
   if (pg->n_blocks < 1 || pg->blocks_per_req < 1) return CSA_ERR_BAD_SHAPE;
   if ((int64_t)pg->blocks_per_req * bs < sh->n_cap) return CSA_ERR_CAPACITY;
-  if (pg->n_blocks * bs > INT32_MAX || pg->n_blocks * bs * row_bytes > max_pool_bytes)
+  // (divisions, so that no product of caller sizes can overflow)
+  if (pg->n_blocks > INT32_MAX / bs || pg->n_blocks * bs > max_pool_bytes / row_bytes)
     return CSA_ERR_UNSUPPORTED;
   if ((int64_t)sh->batch * pg->blocks_per_req > INT32_MAX) return CSA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(pg->block_table) & 15u) != 0) return CSA_ERR_ALIGNMENT;

@@ -233,6 +233,7 @@ PAGE_REFUSALS = [
     (dict(n_blocks=0), 2), (dict(bpr=0), 2),
     (dict(bpr=15), 4), (dict(bpr=1, bs=128), 4),
     (dict(n_blocks=1 << 28, bs=16), 8),          # 2^32 pool rows: past int32
+    (dict(n_blocks=(1 << 62) + 1, bs=4096), 8),   # rows x bytes would overflow int64
     (dict(table=MISALIGNED), 5), (dict(table=None), 1),
 ]
 
