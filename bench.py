@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--query-sets", type=int, default=4,
                     help="query sets cycled over the steps (queries rolled along the batch), so "
                          "consecutive steps select different compressed rows")
+    ap.add_argument("--event-every", type=int, default=8, metavar="E",
+                    help="record the events around the dominant kernel on every E-th timed "
+                         "step (two event records cost about 6 us per step on this path)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -253,19 +256,23 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly K steps; HIP events on the launch stream around the
-    # dominant kernel only
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # dominant kernel of every E-th step (each event record is a packet of its
+    # own in the stream: on every step the pair would add a few microseconds
+    # to the step being measured)
+    every = max(1, args.event_every)
+    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for k in range(0, args.steps, every)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        run_step(evs[k], r=k, mode="dom")
+        run_step(evs.get(k), r=k, mode="dom")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1000.0 / args.steps
     if dominant == "indexer_score":
-        t_dom = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+        t_dom = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()])) * 1e-3
     else:
-        t_dom = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+        t_dom = float(np.mean([e[2].elapsed_time(e[3]) for e in evs.values()])) * 1e-3
 
     # stage breakdown (outside the timed region): events at every stage boundary
     nb = min(args.steps, 40)
@@ -308,7 +315,8 @@ def main():
         # every block of query rows: the contraction, not HBM, bounds it
         roofline = {"bound": "mfma", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
                     "achieved": round(sf / t_dom / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(sf / t_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                    "unit": "TFLOP/s", "frac": round(sf / t_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "kernel_launches_timed": len(evs)}
     traffic = None
     kf = ("_fp8" if fp8 and dominant == "indexer_score" else "") + ("_paged" if paged else "")
     tfile = os.path.join(PROFILES, f"traffic_{dominant}{kf}_config{args.config}.json")
@@ -374,7 +382,7 @@ def main():
                     {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "kernel_launches_timed": len(evs)},
         "stages": stages,
         "stages_note": "per-stage HIP events from a separate 40-step pass after the timed region; "
                        "their packets add gaps, so they sum above ms_per_step",
