@@ -14,7 +14,8 @@
 //      registers, thread t owning a contiguous slice, all loads issued at once.
 //   2. Exact K-th largest key by MSB-first 8-bit radix select over LDS
 //      histograms.  For long rows the select first runs on a strided sample
-//      of 1024 keys, to a sample rank that keeps somewhat more than K rows;
+//      (one or two keys per thread), to a sample rank that keeps somewhat
+//      more than K rows;
 //      the rows at or above that threshold are compacted, and the exact
 //      select runs on those candidates only.  When the sample misleads (fewer
 //      than K rows kept, or more than the candidate buffer holds) the exact
@@ -475,26 +476,44 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
   if constexpr (kCandPath) if (n > kCandCap && 2 * K <= kCandCap) {
     __shared__ uint2 cand[kCandCap];  // (key, row index)
     constexpr int kCandPerThread = kCandCap / NT;
-    // ---- threshold from a strided sample: thread t offers row t*KPT + t%KPT,
-    // which exists for the first m threads (closed form, no scan).
+    // ---- threshold from a strided sample.  Thread t offers NS rows, one from
+    // each sub-slice of SUB = KPT/NS registers: row t*KPT + i*SUB + t%SUB of
+    // sub-slice i.  How many of them exist has a closed form (no scan): all
+    // NS for threads whose slice lies below n, those with i*SUB + t%SUB < n%KPT
+    // for the thread straddling n, none past it.  16-wave blocks offer one row
+    // per thread (1024 samples); 4-wave blocks two (512), which measured
+    // 98 against 108 us on 8192 rows of 7168-8192 keys (four: 103 us, the
+    // sample's own histogram passes cost more).
     // Two 8-bit passes over the full key range fix the top 16 key bits: the
     // threshold is the lower edge of the 16-bit bin holding the sample rank,
     // which keeps somewhat more rows than the sample rank alone.
-    const int js = tid % KPT;
-    uint32_t sk = 0u;  // key[js] without a dynamic register index
+    constexpr int NS = NW >= 16 ? 1 : 2;
+    constexpr int SUB = KPT / NS;
+    static_assert(KPT % NS == 0, "whole sub-slices");
+    const int jo = tid % SUB;
+    uint32_t sk[NS];  // key[i*SUB + jo] without a dynamic register index
+    bool sv[NS];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) sk = j == js ? key[j] : sk;
-    const bool sval = valid(js);
+    for (int i = 0; i < NS; ++i) {
+      sk[i] = 0u;
+#pragma unroll
+      for (int jj = 0; jj < SUB; ++jj) sk[i] = jj == jo ? key[i * SUB + jj] : sk[i];
+      sv[i] = valid(i * SUB + jo);
+    }
     const int q = n / KPT, rr = n % KPT;
-    const int m = min(q, NT) + ((q < NT && q % KPT < rr) ? 1 : 0);
+    int m = NS * min(q, NT);
+    if (q < NT) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i) m += (i * SUB + q % SUB < rr) ? 1 : 0;
+    }
     // sample rank expected at row rank K, plus three standard deviations, so
     // that the threshold keeps at least K rows
     const int ks0 = (int)(((long long)K * m + n - 1) / n);
     const int ks = min(m, ks0 + 3 * (int)sqrtf((float)ks0) + 4);
     uint32_t tau;
     int unused;
-    block_radix_select<NW, false, 1>([&](int) { return sk; }, [&](int) { return sval; }, ks, 0u,
-                                     0xFFFFFFFFu, sm, tau, unused, 2);
+    block_radix_select<NW, false, NS>([&](int r) { return sk[r]; }, [&](int r) { return sv[r]; }, ks,
+                                      0u, 0xFFFFFFFFu, sm, tau, unused, 2);
     // ---- rows at or above the threshold, compacted in row order; the same
     // barriers give the row maximum
     int mine = 0;
