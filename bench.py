@@ -173,7 +173,11 @@ def main():
     inp = I.make_inputs(args.config, key_format=args.key_format)
     t_gen = time.time() - t0
     paged = args.paged > 0
-    dev = C.to_device(I.page_inputs(inp, args.paged, seed=11) if paged else inp, sh)
+    # --paged: the indexer keys, the compressed K/V and the window rings all
+    # live in block pools
+    pin = I.page_inputs(inp, args.paged, seed=11, win=True) if paged else inp
+    dev = C.to_device(pin, sh)
+    kwin, vwin = ("k_win_pool", "v_win_pool") if paged else ("k_win", "v_win")
     bufs = C.alloc_outputs(sh)
     scale = I.softmax_scale(sh)
     stream = torch.cuda.current_stream()
@@ -194,10 +198,12 @@ def main():
     # window writeback: the step's new rows (as the rings already hold them, so
     # the write is idempotent) to their ring slots
     if args.writeback:
-        B_, S_, Wc, D_ = sh.batch, sh.q_per_req, sh.w_cap, sh.head_dim
-        wb_slots = torch.from_numpy(I.ring_slot_mapping(sh, inp["start_pos"])).cuda()
-        k_new = dev["k_win"].reshape(B_ * Wc, D_)[wb_slots.long()].contiguous()
-        v_new = dev["v_win"].reshape(B_ * Wc, D_)[wb_slots.long()].contiguous()
+        D_ = sh.head_dim
+        slots = (I.paged_ring_slot_mapping(sh, inp["start_pos"], pin["win_table"], args.paged)
+                 if paged else I.ring_slot_mapping(sh, inp["start_pos"]))
+        wb_slots = torch.from_numpy(slots).cuda()
+        k_new = dev[kwin].reshape(-1, D_)[wb_slots.long()].contiguous()
+        v_new = dev[vwin].reshape(-1, D_)[wb_slots.long()].contiguous()
 
     # ev: events recorded around the stages, on the launch stream.  "dom" records
     # only the two around the dominant kernel (the timed region keeps its
@@ -205,7 +211,7 @@ def main():
     def run_step(ev=None, r=0, mode="all"):
         dev = qsets[r % R]
         if args.writeback:
-            C.swa_writeback(sh, k_new, v_new, wb_slots, dev["k_win"], dev["v_win"], stream)
+            C.swa_writeback(sh, k_new, v_new, wb_slots, dev[kwin], dev[vwin], stream)
         rec_all = ev is not None and mode == "all"
         rec_score = ev is not None and (mode == "all" or dominant == "indexer_score")
         rec_attn = ev is not None and (mode == "all" or dominant == "sparse_attn")
@@ -230,10 +236,10 @@ def main():
             ti = dev["topk_idx"]
         if rec_attn: ev[2].record(stream)
         if not cfg.indexer_only and paged:
-            C.sparse_attn_decode_paged(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp_pool"],
+            C.sparse_attn_decode_paged(sh, dev["q"], dev[kwin], dev[vwin], dev["k_cmp_pool"],
                                        dev["v_cmp_pool"], dev["cmp_table"], ti, dev["start_pos"],
                                        dev["rope_cos"], dev["rope_sin"], scale, bufs["out"],
-                                       bufs["attn_ws"], stream)
+                                       bufs["attn_ws"], stream, win_table=dev["win_table"])
         elif not cfg.indexer_only:
             C.sparse_attn_decode(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
                                  ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], scale,
@@ -377,6 +383,8 @@ def main():
                    "max_len": sh.max_len, "query_sets": R, "indexer_keys": args.key_format,
                    "window_writeback": bool(args.writeback),
                    "paged_block_rows": args.paged or None,
+                   "paged_caches": (["indexer keys", "compressed K/V", "window rings"]
+                                    if paged else None),
                    "parallelism": "single GPU"},
         "roofline": dict(roofline, traffic=traffic) if cfg.indexer_only else
                     {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),

@@ -276,16 +276,30 @@ csa_status_t csa_swa_writeback(const csa_shape_t* shape, const void* k_new, cons
                                const int32_t* slot_mapping, void* k_cache, void* v_cache,
                                int64_t n_slots, void* stream);
 
-/* csa_sparse_attn_decode with the compressed K and V caches paged.
+/* csa_sparse_attn_decode with the compressed K and V caches paged, and
+ * optionally the window rings too.  The pages keep their caches in
+ * allocator-mapped pools ("Fix: complete DeepSeek V4 TP CSA decode",
+ * description) and commit window rows through a slot mapping into one flat
+ * cache ("Perf: parallelize the DSpark TP-4 SWA decode hot tasks", review);
+ * reading the window through a block table is this library's reading.
  *
  *   k_pool, v_pool [n_blocks][block_size][D] dtype
  *   pages          the block table of the compressed K/V cache (see
  *                  csa_pages_t); entries reached by valid Top-K indices must
  *                  lie in [0, n_blocks) (outside the contract otherwise; the
  *                  device clamps them into the pool)
- * The window cache stays a per-request ring (rows placed by
- * csa_swa_writeback).  Every other argument, the workspace query and the
- * result as csa_sparse_attn_decode.
+ *   win_pages      NULL: k_win / v_win are the per-request rings
+ *                  [B][w_cap][D].  Otherwise the block table of the window
+ *                  rings and k_win / v_win are pools
+ *                  [win n_blocks][win block_size][D]: ring slot r (position
+ *                  pos, r = pos mod w_cap) of request b is pool row
+ *                  block_table[b * blocks_per_req + r / block_size]
+ *                  * block_size + r % block_size, and blocks_per_req *
+ *                  block_size >= w_cap (CSA_ERR_CAPACITY otherwise).  The
+ *                  other csa_pages_t rules apply as for `pages`.
+ * csa_swa_writeback places a step's new rows in either layout: its slot
+ * mapping names the pool row of each token's ring slot.  Every other
+ * argument, the workspace query and the result as csa_sparse_attn_decode.
  */
 csa_status_t csa_sparse_attn_decode_paged(const csa_shape_t* shape, const void* q,
                                           const void* k_win, const void* v_win, const void* k_pool,
@@ -293,7 +307,8 @@ csa_status_t csa_sparse_attn_decode_paged(const csa_shape_t* shape, const void* 
                                           const int32_t* topk_idx, const int32_t* start_pos,
                                           const float* rope_cos, const float* rope_sin,
                                           int32_t rope_rows, float softmax_scale, void* out,
-                                          void* ws, size_t ws_bytes, void* stream);
+                                          void* ws, size_t ws_bytes, void* stream,
+                                          const csa_pages_t* win_pages);
 
 /* Static text for a status code (never NULL). */
 const char* csa_status_string(csa_status_t status);
@@ -301,7 +316,7 @@ const char* csa_status_string(csa_status_t status);
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t csa_abi_version(void);
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -121,8 +121,9 @@ def run_paged(shape, inp: dict, **kw) -> dict:
     """The oracle on paged caches: the pools are first gathered to the dense
     per-request layout through the block tables, then `run` computes as usual.
     Paged names in `inp`: k_idx_pool (or k_idx8_pool + k_scale_pool) with
-    idx_table / idx_block_size, and k_cmp_pool + v_cmp_pool with cmp_table /
-    cmp_block_size."""
+    idx_table / idx_block_size, k_cmp_pool + v_cmp_pool with cmp_table /
+    cmp_block_size, and k_win_pool + v_win_pool with win_table /
+    win_block_size (the window rings, logical row = ring slot)."""
     d = {k: v for k, v in inp.items() if not k.endswith(("_pool", "_table", "_block_size"))}
     nc = shape.n_cap
     if "k_idx_pool" in inp:
@@ -133,6 +134,10 @@ def run_paged(shape, inp: dict, **kw) -> dict:
     if "k_cmp_pool" in inp:
         d["k_cmp"] = unpage(inp["k_cmp_pool"], inp["cmp_table"], inp["cmp_block_size"], nc)
         d["v_cmp"] = unpage(inp["v_cmp_pool"], inp["cmp_table"], inp["cmp_block_size"], nc)
+    if "k_win_pool" in inp:
+        wc = shape.w_cap
+        d["k_win"] = unpage(inp["k_win_pool"], inp["win_table"], inp["win_block_size"], wc)
+        d["v_win"] = unpage(inp["v_win_pool"], inp["win_table"], inp["win_block_size"], wc)
     return run(shape, d, **kw)
 
 

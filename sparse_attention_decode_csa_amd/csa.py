@@ -80,7 +80,7 @@ def lib() -> ctypes.CDLL:
         L.csa_indexer_score_paged.argtypes = [sp, vp, vp, vp, vp, pp, vp, vp, vp]
         L.csa_sparse_attn_decode_paged.restype = i32
         L.csa_sparse_attn_decode_paged.argtypes = [sp, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, i32,
-                                                   f32, vp, vp, sz, vp]
+                                                   f32, vp, vp, sz, vp, pp]
         L.csa_topk_workspace_bytes.restype = sz
         L.csa_topk_workspace_bytes.argtypes = [sp]
         L.csa_topk.restype = i32
@@ -216,13 +216,16 @@ def topk(shape, scores, start_pos, topk_idx, ws=None, stream=None) -> None:
         _stream(stream)))
 
 
-def _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out):
-    """Pointers of the arguments both attention entries share, size-checked."""
+def _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out,
+                 win_numel=None):
+    """Pointers of the arguments both attention entries share, size-checked
+    (win_numel: elements of a paged window pool instead of the dense rings)."""
     n, dt = _sizes(shape), torch_dtype(shape)
+    nw = n["win"] if win_numel is None else win_numel
     rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
     half = shape.rope_dim // 2
-    return dict(q=_dev(q, "q", n["q"], dt), k_win=_dev(k_win, "k_win", n["win"], dt),
-                v_win=_dev(v_win, "v_win", n["win"], dt),
+    return dict(q=_dev(q, "q", n["q"], dt), k_win=_dev(k_win, "k_win", nw, dt),
+                v_win=_dev(v_win, "v_win", nw, dt),
                 topk_idx=_dev(topk_idx, "topk_idx", n["topk_idx"], torch.int32),
                 start_pos=_dev(start_pos, "start_pos", n["start_pos"], torch.int32),
                 rope_cos=_dev(rope_cos, "rope_cos", rope_rows * half, torch.float32),
@@ -244,20 +247,30 @@ def sparse_attn_decode(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos
 
 def sparse_attn_decode_paged(shape, q, k_win, v_win, k_pool, v_pool, block_table, topk_idx,
                              start_pos, rope_cos, rope_sin, softmax_scale, out, ws,
-                             stream=None) -> None:
-    """k_pool/v_pool [n_blocks, block_size, D] sharing block_table [B, bpr] int32."""
+                             stream=None, win_table=None) -> None:
+    """k_pool/v_pool [n_blocks, block_size, D] sharing block_table [B, bpr] int32.
+    With win_table [B, wbpr] int32, k_win/v_win are pools [n_blocks, block_size, D]
+    of the window rings as well (ring slot r of request b is pool row
+    win_table[b, r // block_size] * block_size + r % block_size)."""
     cs, dt = CShape.of(shape), torch_dtype(shape)
     if k_pool.shape != v_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
     pg = _pages(shape, k_pool, block_table, "k_pool")
     rows = pg.n_blocks * pg.block_size
-    c = _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out)
+    wpg, win_numel = None, None
+    if win_table is not None:
+        if k_win.shape != v_win.shape:
+            raise ValueError("k_win and v_win pools must have the same shape")
+        wpg = _pages(shape, k_win, win_table, "k_win")
+        win_numel = wpg.n_blocks * wpg.block_size * shape.head_dim
+    c = _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out, win_numel)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("csa_sparse_attn_decode_paged", lib().csa_sparse_attn_decode_paged(
         ctypes.byref(cs), c["q"], c["k_win"], c["v_win"],
         _dev(k_pool, "k_pool", rows * shape.head_dim, dt), _dev(v_pool, "v_pool", rows * shape.head_dim, dt),
         ctypes.byref(pg), c["topk_idx"], c["start_pos"], c["rope_cos"], c["rope_sin"],
-        c["rope_rows"], float(softmax_scale), c["out"], _dev(ws, "ws"), nbytes, _stream(stream)))
+        c["rope_rows"], float(softmax_scale), c["out"], _dev(ws, "ws"), nbytes, _stream(stream),
+        None if wpg is None else ctypes.byref(wpg)))
 
 
 def swa_writeback(shape, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
@@ -332,11 +345,13 @@ def step(shape, dev: dict, bufs: dict, softmax_scale: float, stream=None,
                           bufs["scores"], stream)
         topk(shape, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
         ti = bufs["topk_idx"]
-    if "cmp_table" in dev:   # paged compressed K/V cache
-        sparse_attn_decode_paged(shape, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp_pool"],
+    if "cmp_table" in dev:   # paged compressed K/V cache (and maybe paged window rings)
+        paged_win = "win_table" in dev
+        sparse_attn_decode_paged(shape, dev["q"], dev["k_win_pool" if paged_win else "k_win"],
+                                 dev["v_win_pool" if paged_win else "v_win"], dev["k_cmp_pool"],
                                  dev["v_cmp_pool"], dev["cmp_table"], ti, dev["start_pos"],
                                  dev["rope_cos"], dev["rope_sin"], softmax_scale, bufs["out"],
-                                 bufs["attn_ws"], stream)
+                                 bufs["attn_ws"], stream, dev.get("win_table"))
         return
     sparse_attn_decode(shape, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
                        ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], softmax_scale,

@@ -37,15 +37,16 @@ csa_status_t check_selection(const csa_shape_t* sh) {
 csa_status_t to_status(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH; }
 
 // A block table and its pool: block size a power of two in [16, 4096], enough
-// blocks per request for n_cap rows, a pool whose row count fits int32 and
-// whose rows of row_bytes stay below max_pool_bytes.
-csa_status_t check_pages(const csa_shape_t* sh, const csa_pages_t* pg, int64_t row_bytes,
+// blocks per request for `rows` logical rows (n_cap, or w_cap for a window
+// ring), a pool whose row count fits int32 and whose rows of row_bytes stay
+// below max_pool_bytes.
+csa_status_t check_pages(const csa_shape_t* sh, const csa_pages_t* pg, int64_t rows, int64_t row_bytes,
                          int64_t max_pool_bytes, int* shift) {
   if (!pg || !pg->block_table) return CSA_ERR_NULL_PTR;
   const int32_t bs = pg->block_size;
   if (bs < 16 || bs > 4096 || (bs & (bs - 1))) return CSA_ERR_BAD_SHAPE;
   if (pg->n_blocks < 1 || pg->blocks_per_req < 1) return CSA_ERR_BAD_SHAPE;
-  if ((int64_t)pg->blocks_per_req * bs < sh->n_cap) return CSA_ERR_CAPACITY;
+  if ((int64_t)pg->blocks_per_req * bs < rows) return CSA_ERR_CAPACITY;
   // (divisions, so that no product of caller sizes can overflow)
   if (pg->n_blocks > INT32_MAX / bs || pg->n_blocks * bs > max_pool_bytes / row_bytes)
     return CSA_ERR_UNSUPPORTED;
@@ -132,7 +133,8 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
                                 const int32_t* topk_idx, const int32_t* start_pos,
                                 const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                                 float softmax_scale, void* out, void* ws, size_t ws_bytes,
-                                void* stream, const csa_pages_t* pages, int block_shift) {
+                                void* stream, const csa_pages_t* pages, int block_shift,
+                                const csa_pages_t* win_pages, int win_shift) {
   bool empty = false;
   csa_status_t st = check_common(sh, &empty);
   if (st != CSA_OK || empty) return st;
@@ -194,6 +196,12 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
     a.block_shift = block_shift;
     a.n_blocks = pages->n_blocks;
   }
+  if (win_pages) {
+    a.win_table = win_pages->block_table;
+    a.win_blocks_per_req = win_pages->blocks_per_req;
+    a.win_shift = win_shift;
+    a.win_n_blocks = win_pages->n_blocks;
+  }
   (void)hipGetLastError();
   return to_status(csa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
@@ -205,7 +213,7 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
                                     int32_t rope_rows, float softmax_scale, void* out, void* ws,
                                     size_t ws_bytes, void* stream) {
   return attn_decode(sh, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos, rope_cos, rope_sin,
-                     rope_rows, softmax_scale, out, ws, ws_bytes, stream, nullptr, 0);
+                     rope_rows, softmax_scale, out, ws, ws_bytes, stream, nullptr, 0, nullptr, 0);
 }
 
 csa_status_t csa_swa_writeback(const csa_shape_t* sh, const void* k_new, const void* v_new,
@@ -241,7 +249,7 @@ csa_status_t csa_indexer_score_paged(const csa_shape_t* sh, const void* q_idx, c
   if ((st = check_selection(sh)) != CSA_OK) return st;
   int shift = 0;
   const int64_t row = k_scale ? sh->idx_dim : (int64_t)sh->idx_dim * (sh->dtype == CSA_DTYPE_BF16 ? 2 : 4);
-  if ((st = check_pages(sh, pages, row, INT64_MAX, &shift)) != CSA_OK) return st;
+  if ((st = check_pages(sh, pages, sh->n_cap, row, INT64_MAX, &shift)) != CSA_OK) return st;
   if (!aligned16(q_idx) || !aligned16(w) || !aligned16(k_pool) || !aligned16(start_pos) ||
       !aligned16(scores) || (k_scale && !aligned16(k_scale)))
     return CSA_ERR_ALIGNMENT;
@@ -258,16 +266,21 @@ csa_status_t csa_sparse_attn_decode_paged(const csa_shape_t* sh, const void* q,
                                           const int32_t* topk_idx, const int32_t* start_pos,
                                           const float* rope_cos, const float* rope_sin,
                                           int32_t rope_rows, float softmax_scale, void* out,
-                                          void* ws, size_t ws_bytes, void* stream) {
+                                          void* ws, size_t ws_bytes, void* stream,
+                                          const csa_pages_t* win_pages) {
   bool empty = false;
   csa_status_t st = check_common(sh, &empty);
   if (st != CSA_OK || empty) return st;
   if (!pages) return CSA_ERR_NULL_PTR;
-  int shift = 0;
+  int shift = 0, win_shift = 0;
   const int64_t row = (int64_t)sh->head_dim * (sh->dtype == CSA_DTYPE_BF16 ? 2 : 4);
-  if ((st = check_pages(sh, pages, row, csa::kMaxSliceBytes, &shift)) != CSA_OK) return st;
+  if ((st = check_pages(sh, pages, sh->n_cap, row, csa::kMaxSliceBytes, &shift)) != CSA_OK) return st;
+  if (win_pages &&
+      (st = check_pages(sh, win_pages, sh->w_cap, row, csa::kMaxSliceBytes, &win_shift)) != CSA_OK)
+    return st;
   return attn_decode(sh, q, k_win, v_win, k_pool, v_pool, topk_idx, start_pos, rope_cos, rope_sin,
-                     rope_rows, softmax_scale, out, ws, ws_bytes, stream, pages, shift);
+                     rope_rows, softmax_scale, out, ws, ws_bytes, stream, pages, shift, win_pages,
+                     win_shift);
 }
 
 const char* csa_status_string(csa_status_t s) {

@@ -55,6 +55,12 @@ struct AttnArgs {
   const int32_t* block_table;
   int blocks_per_req, block_shift;
   int64_t n_blocks;
+  // paged window (win_table non-null): k_win / v_win are pools and ring slot
+  // r of request b is pool row
+  // win_table[b * win_blocks_per_req + (r >> win_shift)] << win_shift | (r & mask)
+  const int32_t* win_table;
+  int win_blocks_per_req, win_shift;
+  int64_t win_n_blocks;
 };
 
 struct WritebackArgs {

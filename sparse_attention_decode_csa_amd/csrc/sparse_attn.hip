@@ -295,7 +295,16 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
     e_lo = split * RPS + wave * RPW;
     e_hi = min(nrows, e_lo + RPW);
     const int e = e_lo + lane;
-    rowoff = (lane < RPW && e < e_hi) ? (uint32_t)((first_pos + e) % a.w_cap) * G::ROW : kOutOfRange;
+    const int slot = (first_pos + e) % a.w_cap;
+    const bool ok = lane < RPW && e < e_hi;
+    if (a.win_table) {  // paged ring: pool row through the window's table (clamped into the pool)
+      const int blk = a.win_table[(size_t)b * a.win_blocks_per_req + (ok ? (slot >> a.win_shift) : 0)];
+      const int64_t pb = min((int64_t)max(blk, 0), a.win_n_blocks - 1);
+      const int64_t prow = (pb << a.win_shift) + (slot & ((1 << a.win_shift) - 1));
+      rowoff = ok ? (uint32_t)(prow * G::ROW) : kOutOfRange;
+    } else {
+      rowoff = ok ? (uint32_t)slot * G::ROW : kOutOfRange;
+    }
   } else {
     e_lo = (split - NSW) * RPS + wave * RPW;
     e_hi = min(a.topk, e_lo + RPW);
@@ -313,12 +322,13 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
   }
   const int nrows_wave = e_hi - e_lo;  // may be <= 0
 
-  // the request's slice of its cache, or for a paged compressed cache the
-  // whole pool; the host keeps either below 2^31 bytes
-  const bool pooled = !win && a.block_table;
+  // the request's slice of its cache, or for a paged cache the whole pool;
+  // the host keeps either below 2^31 bytes
+  const bool pooled = win ? a.win_table != nullptr : a.block_table != nullptr;
   const size_t rows_req = win ? (size_t)a.w_cap : (size_t)a.n_cap;
   const size_t base_row = pooled ? 0 : (size_t)b * rows_req;
-  const size_t range_rows = pooled ? (size_t)(a.n_blocks << a.block_shift) : rows_req;
+  const size_t pool_rows = win ? (size_t)(a.win_n_blocks << a.win_shift) : (size_t)(a.n_blocks << a.block_shift);
+  const size_t range_rows = pooled ? pool_rows : rows_req;
   const char* kreq = static_cast<const char*>(win ? a.k_win : a.k_cmp) + base_row * G::ROW;
   const char* vreq = static_cast<const char*>(win ? a.v_win : a.v_cmp) + base_row * G::ROW;
   const int range = (int)(range_rows * G::ROW);

@@ -396,13 +396,20 @@ def page_cache(dense: np.ndarray, block_size: int, seed: int, spare_blocks: int 
 
 
 def page_inputs(inp: dict, block_size: int, seed: int, idx: bool = True, cmp: bool = True,
-                spare_blocks: int = 3) -> dict:
-    """A copy of a seeded input dict with the indexer key cache (idx) and/or
-    the compressed K/V cache (cmp) moved into block pools (page_cache).
-    Names: k_idx_pool (or k_idx8_pool + k_scale_pool), idx_table,
-    idx_block_size; k_cmp_pool + v_cmp_pool sharing cmp_table, cmp_block_size.
-    The dense arrays that were paged are dropped."""
+                spare_blocks: int = 3, win: bool = False) -> dict:
+    """A copy of a seeded input dict with the indexer key cache (idx), the
+    compressed K/V cache (cmp) and/or the window rings (win) moved into block
+    pools (page_cache).  Names: k_idx_pool (or k_idx8_pool + k_scale_pool),
+    idx_table, idx_block_size; k_cmp_pool + v_cmp_pool sharing cmp_table,
+    cmp_block_size; k_win_pool + v_win_pool sharing win_table, win_block_size
+    (logical row = ring slot).  The dense arrays that were paged are dropped."""
     out = dict(inp)
+    if win:
+        out["k_win_pool"], out["win_table"] = page_cache(inp["k_win"], block_size, seed + 2,
+                                                         spare_blocks)
+        out["v_win_pool"], _ = page_cache(inp["v_win"], block_size, seed + 2, spare_blocks)
+        del out["k_win"], out["v_win"]
+        out["win_block_size"] = block_size
     if idx:
         if "k_idx8" in inp:
             out["k_idx8_pool"], out["idx_table"] = page_cache(inp["k_idx8"], block_size, seed,
@@ -422,6 +429,20 @@ def page_inputs(inp: dict, block_size: int, seed: int, idx: bool = True, cmp: bo
         del out["k_cmp"], out["v_cmp"]
         out["cmp_block_size"] = block_size
     return out
+
+
+def paged_ring_slot_mapping(shape: Shape, start_pos: np.ndarray, win_table: np.ndarray,
+                            block_size: int) -> np.ndarray:
+    """Slot mapping of the step's new tokens into paged window rings: token
+    (b, s) at position p = start_pos[b] + s belongs in ring slot r = p mod w_cap,
+    which is pool row win_table[b, r // block_size] * block_size + r % block_size
+    of the pool viewed as one flat cache.  Shape [B*S] int32."""
+    B, S = shape.batch, shape.q_per_req
+    p = np.asarray(start_pos, dtype=np.int64)[:, None] + np.arange(S)[None, :]
+    r = p % shape.w_cap
+    tab = np.asarray(win_table, dtype=np.int64)
+    rows = tab[np.arange(B)[:, None], r // block_size] * block_size + r % block_size
+    return rows.reshape(-1).astype(np.int32)
 
 
 def ring_slot_mapping(shape: Shape, start_pos: np.ndarray) -> np.ndarray:

@@ -38,7 +38,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_status_strings():
-    assert C.lib().csa_abi_version() == 1
+    assert C.lib().csa_abi_version() == 2
     for code in range(9):
         assert C.status_string(code)
     assert C.status_string(99) == "unknown status"
@@ -219,12 +219,12 @@ def call_score_paged(sh, pg, ptrs=None, k_scale=None):
         None if pg is None else ctypes.byref(pg), p[3], p[4], None)
 
 
-def call_attn_paged(sh, pg, ptrs=None, ws_bytes=1 << 40):
+def call_attn_paged(sh, pg, ptrs=None, ws_bytes=1 << 40, win_pg=None):
     p = ptrs or [FAKE] * 10
     return C.lib().csa_sparse_attn_decode_paged(
         ctypes.byref(C.CShape.of(sh)), p[0], p[1], p[2], p[3], p[4],
         None if pg is None else ctypes.byref(pg), p[5], p[6], p[7], p[8], 1 << 20, 0.1, p[9],
-        FAKE, ws_bytes, None)
+        FAKE, ws_bytes, None, None if win_pg is None else ctypes.byref(win_pg))
 
 
 # shape(): n_cap 256 rows, so block size 16 needs 16 table entries per request
@@ -248,6 +248,30 @@ def test_indexer_score_paged_refusals(kw, code):
 ])
 def test_attn_paged_refusals(kw, code):
     assert call_attn_paged(shape(), pages(**kw)) == code
+
+
+# window rings paged: the csa_pages_t rules of the compressed pool, with the
+# capacity taken against w_cap (shape(): w_cap 128, so 16-row blocks need 8)
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=8), 2), (dict(bs=48), 2), (dict(bs=8192), 2), (dict(bs=0), 2),
+    (dict(n_blocks=0), 2), (dict(bpr=0), 2),
+    (dict(bpr=7), 4), (dict(bpr=1, bs=64), 4),
+    (dict(n_blocks=1 << 28, bs=16), 8),
+    (dict(n_blocks=(1 << 31) // (16 * 256), bs=16), 8),   # bf16 D=128 pool reaching 2^31 bytes
+    (dict(table=MISALIGNED), 5), (dict(table=None), 1),
+])
+def test_attn_paged_window_refusals(kw, code):
+    sh = shape()
+    assert sh.w_cap == 128
+    assert call_attn_paged(sh, pages(), win_pg=pages(**kw)) == code
+
+
+def test_attn_paged_window_tables_that_fit():
+    sh = shape()
+    # a window table covering exactly w_cap rows passes the page checks (the
+    # call then stops at the missing workspace, before any launch)
+    assert call_attn_paged(sh, pages(), ws_bytes=0, win_pg=pages(bpr=8, bs=16)) == 6
+    assert call_attn_paged(sh, pages(), ws_bytes=0, win_pg=pages(bpr=1, bs=128)) == 6
 
 
 def test_paged_null_dtype_alignment_workspace():

@@ -65,10 +65,13 @@ def gpu_step(shape, inp, supplied=False, topk_idx=None, scores=None, jobs=("scor
         ti = torch.from_numpy(np.ascontiguousarray(topk_idx, np.int32)).cuda()
     elif supplied:
         ti = d["topk_idx"]
-    if "attn" in jobs and "cmp_table" in d:   # paged compressed K/V cache
-        C.sparse_attn_decode_paged(shape, d["q"], d["k_win"], d["v_win"], d["k_cmp_pool"],
+    if "attn" in jobs and "cmp_table" in d:   # paged compressed K/V cache (window maybe paged)
+        pw = "win_table" in d
+        C.sparse_attn_decode_paged(shape, d["q"], d["k_win_pool" if pw else "k_win"],
+                                   d["v_win_pool" if pw else "v_win"], d["k_cmp_pool"],
                                    d["v_cmp_pool"], d["cmp_table"], ti, d["start_pos"],
-                                   d["rope_cos"], d["rope_sin"], scale, bufs["out"], bufs["attn_ws"])
+                                   d["rope_cos"], d["rope_sin"], scale, bufs["out"], bufs["attn_ws"],
+                                   win_table=d.get("win_table"))
     elif "attn" in jobs:
         C.sparse_attn_decode(shape, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"], ti,
                              d["start_pos"], d["rope_cos"], d["rope_sin"], scale, bufs["out"],
@@ -245,31 +248,34 @@ def test_paged_scores_exact_grid_ragged(fmt):
     assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
 
 
-@pytest.mark.parametrize("cid,bs", [(0, 16), (1, 32), (2, 16), (4, 128)])
-def test_paged_attention_matches_oracle(cid, bs):
+@pytest.mark.parametrize("cid,bs,win", [(0, 16, False), (1, 32, False), (2, 16, False), (4, 128, False),
+                                        (0, 16, True), (2, 16, True), (3, 32, True), (4, 64, True)])
+def test_paged_attention_matches_oracle(cid, bs, win):
+    # compressed K/V paged, and with win=True the window rings too
     cfg = I.CONFIGS[cid]
     sh = cfg.shape
     dense = I.make_inputs(cid)
-    inp = I.page_inputs(dense, bs, seed=cid + 40, idx=False)
+    inp = I.page_inputs(dense, bs, seed=cid + 40, idx=False, win=win)
     ref = oracle.run_paged(sh, inp, nthreads=NTHREADS,
                            jobs=(oracle.JOB_ATTN if cfg.supplied_topk
                                  else oracle.JOB_SCORE | oracle.JOB_TOPK | oracle.JOB_ATTN))
     got = gpu_step(sh, inp, topk_idx=ref["topk_idx"], jobs=("attn",))
     worst = U.compare_outputs(sh, got["out"], ref["out"])
-    print(f"paged config {cid} block {bs}: worst error {worst:.3g}")
+    print(f"paged config {cid} block {bs} window paged {win}: worst error {worst:.3g}")
     # same rows in the same order as the dense path: identical outputs
     dgot = gpu_step(sh, dense, topk_idx=ref["topk_idx"], jobs=("attn",))
     assert np.array_equal(got["out"], dgot["out"])
 
 
-@pytest.mark.parametrize("fmt,bs", [("bf16", 64), ("fp8", 16)])
-def test_end_to_end_paged(fmt, bs):
-    # score, select and attend with both caches paged, on the wide Top-K
-    # configuration, against the oracle over the gathered caches
+@pytest.mark.parametrize("fmt,bs,win", [("bf16", 64, True), ("fp8", 16, False)])
+def test_end_to_end_paged(fmt, bs, win):
+    # score, select and attend with the indexer and compressed caches paged
+    # (and the window rings with win=True), on the wide Top-K configuration,
+    # against the oracle over the gathered caches
     cid = 4
     sh = I.CONFIGS[cid].shape
     dense = I.make_inputs(cid, key_format=fmt)
-    inp = I.page_inputs(dense, bs, seed=9)
+    inp = I.page_inputs(dense, bs, seed=9, win=win)
     ref = oracle.run_paged(sh, inp, nthreads=NTHREADS)
     got = gpu_step(sh, inp)
     rows = U.token_rows(sh, inp["start_pos"])
@@ -402,6 +408,39 @@ def test_writeback_then_attention():
     C.sparse_attn_decode(sh, d["q"], d["k_win"], d["v_win"], d["k_cmp"], d["v_cmp"], ti,
                          d["start_pos"], d["rope_cos"], d["rope_sin"], I.softmax_scale(sh),
                          bufs["out"], bufs["attn_ws"])
+    torch.cuda.synchronize()
+    U.compare_outputs(sh, bufs["out"].float().cpu().numpy(), ref["out"])
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_writeback_then_attention_paged_window(bs):
+    # the window rings live in a pool; the step's new entries start poisoned
+    # there, the GPU writeback through the paged slot mapping restores them and
+    # the paged attention must then give the oracle's output
+    cfg = small_cfg(batch=4, q_per_req=3, win=48, w_cap=53, max_len=1024)
+    sh = cfg.shape
+    dense = I.make_inputs(cfg)
+    ref = oracle_step(sh, dense)
+    inp = I.page_inputs(dense, bs, seed=21, idx=False, win=True)
+    D = sh.head_dim
+    slots = I.paged_ring_slot_mapping(sh, dense["start_pos"], inp["win_table"], bs)
+    kflat = inp["k_win_pool"].reshape(-1, D)
+    vflat = inp["v_win_pool"].reshape(-1, D)
+    k_new, v_new = kflat[slots].copy(), vflat[slots].copy()
+    poison = I.f32_to_bf16_bits(np.float32([I.POISON]))[0]
+    kp, vp = kflat.copy(), vflat.copy()
+    kp[slots] = poison
+    vp[slots] = poison
+    d = C.to_device(dict(inp, k_win_pool=kp.reshape(inp["k_win_pool"].shape),
+                         v_win_pool=vp.reshape(inp["v_win_pool"].shape)), sh)
+    bufs = C.alloc_outputs(sh)
+    C.swa_writeback(sh, C.to_device(dict(x=k_new), sh)["x"], C.to_device(dict(x=v_new), sh)["x"],
+                    to_gpu(slots), d["k_win_pool"], d["v_win_pool"])
+    ti = to_gpu(ref["topk_idx"])
+    C.sparse_attn_decode_paged(sh, d["q"], d["k_win_pool"], d["v_win_pool"], d["k_cmp_pool"],
+                               d["v_cmp_pool"], d["cmp_table"], ti, d["start_pos"], d["rope_cos"],
+                               d["rope_sin"], I.softmax_scale(sh), bufs["out"], bufs["attn_ws"],
+                               win_table=d["win_table"])
     torch.cuda.synchronize()
     U.compare_outputs(sh, bufs["out"].float().cpu().numpy(), ref["out"])
 

@@ -376,6 +376,30 @@ def test_paged_oracle_equals_dense(bs):
     got = oracle.run_paged(sh, paged)
     for k in ("scores", "topk_idx", "out"):
         assert np.array_equal(got[k], ref[k], equal_nan=True), k
+    # the window rings paged as well (logical row = ring slot)
+    pw = I.page_inputs(inp, bs, seed=3, win=True)
+    assert "k_win" not in pw and pw["win_table"].shape == (sh.batch, -(-sh.w_cap // bs))
+    got = oracle.run_paged(sh, pw)
+    for k in ("scores", "topk_idx", "out"):
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+    # a window table entry aimed at a poisoned spare block changes the output
+    bad = dict(pw, win_table=pw["win_table"].copy())
+    spare = np.setdiff1d(np.arange(pw["k_win_pool"].shape[0]), pw["win_table"].ravel())
+    bad["win_table"][:, :] = spare[0]
+    assert not np.array_equal(oracle.run_paged(sh, bad)["out"], ref["out"], equal_nan=True)
+
+
+def test_paged_ring_slot_mapping_hand_worked():
+    # w_cap 8 in blocks of 4: ring slots 0-3 of request 0 sit in pool block 5,
+    # slots 4-7 in block 2; request 1 uses blocks 0 and 7.  Position 13 is
+    # slot 5 (block 2, row 1: pool row 9); position 6 of request 1 is slot 6
+    # (block 7, row 2: pool row 30).
+    sh = I.Shape(batch=2, q_per_req=2, ratio=4, n_cap=4, topk=4, win=4, w_cap=8, heads=1,
+                 head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1, max_len=16,
+                 dtype=I.BF16)
+    table = np.array([[5, 2], [0, 7]], dtype=np.int32)
+    got = I.paged_ring_slot_mapping(sh, np.array([12, 6]), table, 4)
+    assert got.tolist() == [8, 9, 30, 31]
 
 
 @pytest.mark.parametrize("bs,ragged", [(16, False), (32, True)])
