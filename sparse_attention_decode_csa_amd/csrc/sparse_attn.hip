@@ -179,48 +179,64 @@ __device__ __forceinline__ void merge_into(StreamState& st, float m, float l, fl
   st.m = mn;
 }
 
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int tok, int h, int d, int D, StreamState& w,
+// (max, sum, dim pair of the partial sum) of splits b0 .. b0+kMergeBatch-1
+// for one (token, head, dim pair); splits past the last read as empty.
+struct SplitBatch {
+  float m[kMergeBatch], l[kMergeBatch];
+  float2 o[kMergeBatch];
+};
+
+__device__ __forceinline__ void load_splits(const AttnArgs& a, int tok, int h, int d, int D, int b0,
+                                            SplitBatch& sb) {
+  const int NS = a.n_split_win + a.n_split_cmp;
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const int sp = min(b0 + k, NS - 1);
+    const size_t r = ((size_t)tok * NS + sp) * a.heads + h;
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * r);
+    sb.m[k] = ml.x;
+    sb.l[k] = b0 + k < NS ? ml.y : 0.0f;
+    sb.o[k] = *reinterpret_cast<const float2*>(a.ws_o + r * D + d);
+  }
+}
+
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int b0, const SplitBatch& sb, StreamState& w,
                                              StreamState& c) {
-  const int NSW = a.n_split_win, NS = a.n_split_win + a.n_split_cmp;
-  w = StreamState{-INFINITY, 0.0f, 0.0f, 0.0f};
-  c = w;
-  for (int b0 = 0; b0 < NS; b0 += kMergeBatch) {
-    float m[kMergeBatch], l[kMergeBatch];
-    float2 ov[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const int sp = min(b0 + k, NS - 1);
-      const size_t r = ((size_t)tok * NS + sp) * a.heads + h;
-      const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * r);
-      m[k] = ml.x;
-      l[k] = b0 + k < NS ? ml.y : 0.0f;
-      ov[k] = *reinterpret_cast<const float2*>(a.ws_o + r * D + d);
-    }
-#pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      if (b0 + k < NSW) merge_into(w, m[k], l[k], ov[k]);
-      else merge_into(c, m[k], l[k], ov[k]);
-    }
+  for (int k = 0; k < kMergeBatch; ++k) {
+    if (b0 + k < a.n_split_win) merge_into(w, sb.m[k], sb.l[k], sb.o[k]);
+    else merge_into(c, sb.m[k], sb.l[k], sb.o[k]);
   }
 }
 
 // Final output of one (token, head, dim pair) from all of the token's split
 // partials: stream merges, normalisation, inverse RoPE, one rounding, packed
-// group layout.
+// group layout.  The first batch of partials does not depend on the token's
+// position, so it is read before the position and the RoPE table row that
+// depends on it: the two reads overlap instead of adding up.
 template <typename T, int D>
-__device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int p, int item) {
+__device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int item) {
   const int H = a.heads, G = a.out_groups, Hg = H / G;
   const int T_ = a.batch * a.q_per_req;
   const int r0 = D - a.rope_dim;
   const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
+  const int NS = a.n_split_win + a.n_split_cmp;
+  SplitBatch sb;
+  load_splits(a, tok, h, d, D, 0, sb);
+  const int S = a.q_per_req;
+  const int p = clamp_pos(a.start_pos[tok / S] + tok % S, a.max_len);
   float cs = 1.0f, sn = 0.0f;
-  if (d >= r0) {  // issue the table loads early
+  if (d >= r0) {
     const int i = (d - r0) >> 1;
     cs = a.rope_cos[(size_t)p * (a.rope_dim >> 1) + i];
     sn = a.rope_sin[(size_t)p * (a.rope_dim >> 1) + i];
   }
-  StreamState w, c;
-  merge_splits(a, tok, h, d, D, w, c);
+  StreamState w{-INFINITY, 0.0f, 0.0f, 0.0f}, c = w;
+  merge_splits(a, 0, sb, w, c);
+  for (int b0 = kMergeBatch; b0 < NS; b0 += kMergeBatch) {
+    load_splits(a, tok, h, d, D, b0, sb);
+    merge_splits(a, b0, sb, w, c);
+  }
   // stream merge: an empty stream (sum 0) carries no weight
   const float M = fmaxf(w.m, c.m);
   const float fw = w.l > 0.0f ? exp2f(w.m - M) : 0.0f;
@@ -408,9 +424,7 @@ __global__ __launch_bounds__(kFinishThreads) void attn_finish_kernel(AttnArgs a)
   const int tok = blockIdx.x;
   const int item = blockIdx.y * kFinishThreads + threadIdx.x;
   if (item >= a.heads * (D / 2)) return;
-  const int S = a.q_per_req;
-  const int p = clamp_pos(a.start_pos[tok / S] + tok % S, a.max_len);
-  finish_item<T, D>(a, tok, p, item);
+  finish_item<T, D>(a, tok, item);
 }
 
 template <typename T, int D>
