@@ -573,6 +573,62 @@ def test_end_to_end_exact_grid(n_cap, topk, S, Hi):
     U.compare_outputs(sh, got["out"], ref["out"])
 
 
+def random_grid_case(seed, prefill=False):
+    """A seeded random shape inside the supported ranges, with dyadic-grid
+    indexer inputs (every score exact on both sides) and, for some seeds,
+    every cache paged.  prefill: hundreds of tokens per request with 4, 8 or
+    16 bf16 indexer heads, the shape of the GEMM-shaped score kernel."""
+    g = np.random.default_rng([seed, 77, int(prefill)])
+    dt = I.F32 if (g.random() < 0.25 and not prefill) else I.BF16
+    ratio = int(g.choice([1, 2, 4, 8])) if not prefill else 4
+    B = int(g.integers(1, 7)) if not prefill else int(g.integers(1, 3))
+    S = int(g.integers(1, 7)) if not prefill else int(g.integers(128, 701))
+    K = int(g.choice([1, 7, 64, 200, 256, 257, 513, 1024]))
+    n_cap = int(g.integers(16, 3001)) if not prefill else int(g.integers(S // 4 + 1, 3001))
+    max_len = int(g.integers(S, n_cap * ratio + 1))
+    win = int(g.integers(1, 301))
+    heads = int(g.integers(1, 17))
+    divs = [d for d in range(1, heads + 1) if heads % d == 0]
+    D = int(g.choice([64, 128]))
+    Hi = (int(g.choice([1, 2, 3, 4, 5, 8, 16, 33, 64])) if not prefill
+          else int(g.choice([4, 8, 16])))
+    cfg = small_cfg(name="random", seed=seed, batch=B, q_per_req=S, ratio=ratio, n_cap=n_cap,
+                    topk=K, win=win, w_cap=win + S - 1 + int(g.integers(0, 50)), heads=heads,
+                    head_dim=D, rope_dim=int(g.choice([0, 2, 32, D])), idx_heads=Hi,
+                    idx_dim=int(g.choice([64, 128])), out_groups=int(g.choice(divs)),
+                    max_len=max_len, dtype=dt)
+    sh = cfg.shape
+    sp = g.integers(0, max_len - S + 1, size=B).astype(np.int32)
+    inp = I.make_inputs(cfg, start_pos=sp)
+    def grid(shape):
+        v = (g.integers(-8, 9, shape) / 4.0).astype(np.float32)
+        return I.f32_to_bf16_bits(v) if dt == I.BF16 else v
+    inp["q_idx"] = grid(inp["q_idx"].shape)
+    poison = (I.f32_to_bf16_bits(np.float32([I.POISON]))[0] if dt == I.BF16
+              else np.float32(I.POISON))
+    inp["k_idx"] = np.where(inp["k_idx"] == poison, inp["k_idx"], grid(inp["k_idx"].shape))
+    inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    if g.random() < 0.3:
+        inp = I.page_inputs(inp, int(g.choice([16, 32, 64])), seed=seed, win=True)
+    return sh, inp
+
+
+@pytest.mark.parametrize("seed,prefill", [(k, False) for k in range(64)] + [(k, True) for k in range(8)])
+def test_random_shapes_exact_grid(seed, prefill):
+    # scores and lists bitwise, attention within tolerance, over random
+    # shapes: ratio, batch, tokens per request, K (bypass and not), capacities,
+    # head and group counts, RoPE dims, fp32 and bf16, dense and paged caches;
+    # prefill-shaped cases reach the GEMM-shaped score kernel
+    sh, inp = random_grid_case(seed, prefill)
+    paged = "cmp_table" in inp
+    print(f"seed {seed}: {sh} paged={paged}", flush=True)
+    ref = oracle.run_paged(sh, inp, nthreads=NTHREADS) if paged else oracle_step(sh, inp)
+    got = gpu_step(sh, inp)
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+    U.compare_outputs(sh, got["out"], ref["out"])
+
+
 def test_determinism(config_inputs):
     cid = 3
     sh, inp = I.CONFIGS[cid].shape, config_inputs(cid)
