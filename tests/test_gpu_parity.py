@@ -608,6 +608,15 @@ def random_grid_case(seed, prefill=False):
               else np.float32(I.POISON))
     inp["k_idx"] = np.where(inp["k_idx"] == poison, inp["k_idx"], grid(inp["k_idx"].shape))
     inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
+    if dt == I.BF16 and not prefill and g.random() < 0.3:
+        # FP8 key cache: every grid value m/4 (|m| <= 8) is an E4M3 value, so
+        # codes with scale 1 hold the same keys (poisoned rows: the largest
+        # finite code, 448)
+        kf = I.bf16_bits_to_f32(inp["k_idx"])
+        codes = I.f32_to_e4m3_bits(np.where(kf == np.float32(I.POISON), np.float32(448.0), kf))
+        inp["k_idx8"] = codes
+        inp["k_scale"] = np.ones(inp["k_idx"].shape[:2], dtype=np.float32)
+        del inp["k_idx"]
     if g.random() < 0.3:
         inp = I.page_inputs(inp, int(g.choice([16, 32, 64])), seed=seed, win=True)
     return sh, inp
