@@ -351,6 +351,29 @@ def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
     assert np.array_equal(got["topk_idx"], ref["topk_idx"])
 
 
+@pytest.mark.parametrize("T,K,Hi,start,Di,bs", [
+    (600, 256, 8, 1500, 128, 0),
+    (333, 100, 4, 5000, 64, 16),      # paged FP8 codes and scales
+    (200, 64, 16, 9000, 128, 0),
+    (300, 150, 5, 500, 64, 0),        # 5 heads: the LDS head-sum path; tokens that fit Top-K
+])
+def test_prefill_indexer_fp8_exact_grid(T, K, Hi, start, Di, bs):
+    # A prefill chunk over an FP8 indexer key cache: the grid keys m/4 are
+    # E4M3 values, so codes with scale 1 hold them exactly and scores and
+    # lists stay bitwise equal (the chunk's token blocks run the FP8 variant
+    # of the decode-shaped score kernel).
+    sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
+    kf = I.bf16_bits_to_f32(inp.pop("k_idx"))
+    inp["k_idx8"] = I.f32_to_e4m3_bits(kf)          # poison saturates to 448: never read
+    inp["k_scale"] = np.ones(kf.shape[:2], dtype=np.float32)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    if bs:
+        inp = I.page_inputs(inp, bs, seed=T + bs, cmp=False)
+    got = gpu_step(sh, inp, jobs=("score", "topk"))
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+
+
 # --------------------------------------------------------------------------
 # window-cache writeback
 # --------------------------------------------------------------------------
