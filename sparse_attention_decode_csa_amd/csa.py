@@ -31,6 +31,9 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL_PTR", 2: "CSA_ERR_BAD_SHAPE", 3: "CSA_ER
           4: "CSA_ERR_CAPACITY", 5: "CSA_ERR_ALIGNMENT", 6: "CSA_ERR_WORKSPACE",
           7: "CSA_ERR_LAUNCH", 8: "CSA_ERR_UNSUPPORTED"}
 
+# The argument lists below are those of this ABI version (CSA_ABI_VERSION).
+ABI_VERSION = 2
+
 EXPORTS = ("csa_indexer_score", "csa_indexer_score_fp8", "csa_indexer_score_paged",
            "csa_topk_workspace_bytes", "csa_topk", "csa_sparse_attn_workspace_bytes",
            "csa_sparse_attn_decode", "csa_sparse_attn_decode_paged", "csa_swa_writeback",
@@ -96,6 +99,11 @@ def lib() -> ctypes.CDLL:
         L.csa_status_string.argtypes = [i32]
         L.csa_abi_version.restype = i32
         L.csa_abi_version.argtypes = []
+        got = L.csa_abi_version()
+        if got != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} implements ABI version {got}, this binding expects "
+                              f"{ABI_VERSION}: rebuild it with "
+                              "`python -m sparse_attention_decode_csa_amd.build`")
         _lib = L
     return _lib
 

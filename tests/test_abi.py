@@ -38,7 +38,8 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_status_strings():
-    assert C.lib().csa_abi_version() == 2
+    header_version = int(re.search(r"#define CSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert C.lib().csa_abi_version() == C.ABI_VERSION == header_version
     for code in range(9):
         assert C.status_string(code)
     assert C.status_string(99) == "unknown status"
