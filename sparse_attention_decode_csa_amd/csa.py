@@ -232,6 +232,10 @@ def _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin
     nw = n["win"] if win_numel is None else win_numel
     rope_rows = 0 if rope_cos is None else int(rope_cos.shape[0])
     half = shape.rope_dim // 2
+    for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        # rows of Dr/2 pairs, one row per position
+        if t is not None and (t.dim() != 2 or t.shape[1] != half or t.shape[0] != rope_rows):
+            raise ValueError(f"{name}: expected [{rope_rows or 'rows'}, {half}], got {list(t.shape)}")
     return dict(q=_dev(q, "q", n["q"], dt), k_win=_dev(k_win, "k_win", nw, dt),
                 v_win=_dev(v_win, "v_win", nw, dt),
                 topk_idx=_dev(topk_idx, "topk_idx", n["topk_idx"], torch.int32),

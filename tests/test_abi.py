@@ -205,6 +205,20 @@ def test_binding_refuses_cpu_tensors():
         C.topk(shape(), t, t, t)
 
 
+def test_binding_refuses_rope_tables_of_the_wrong_layout():
+    # the tables hold Dr/2 (cos, sin) pairs per position; a full-width table
+    # or mismatched row counts would be read with the wrong stride
+    import torch
+    sh = shape()
+    t = torch.zeros(4)
+    half = sh.rope_dim // 2
+    for cos, sin in ((torch.zeros(sh.max_len, sh.rope_dim), torch.zeros(sh.max_len, half)),
+                     (torch.zeros(sh.max_len, half), torch.zeros(sh.max_len - 1, half)),
+                     (torch.zeros(sh.max_len * half), torch.zeros(sh.max_len * half))):
+        with pytest.raises(ValueError, match="rope_"):
+            C.sparse_attn_decode(sh, t, t, t, t, t, t, t, cos, sin, 0.1, t, t)
+
+
 # --------------------------------------------------------------------------
 # paged compressed caches
 # --------------------------------------------------------------------------
