@@ -188,10 +188,12 @@ def indexer_score_fp8(shape, q_idx, w, k_idx8, k_scale, start_pos, scores, strea
         _dev(scores, "scores", n["scores"], torch.float32), _stream(stream)))
 
 
-def _pages(shape, pool, block_table, name: str) -> CPages:
-    """csa_pages_t of a pool [n_blocks, block_size, ...] and its table [B, blocks_per_req]."""
+def _pages(shape, pool, block_table, name: str, row: int) -> CPages:
+    """csa_pages_t of a pool [n_blocks, block_size, row] and its table [B, blocks_per_req]."""
     if pool.dim() < 2 or block_table.dim() != 2 or block_table.dtype != torch.int32:
         raise ValueError(f"{name}: pool [n_blocks, block_size, ...] and int32 table [B, bpr] expected")
+    if pool.shape[2:].numel() != row:
+        raise ValueError(f"{name}: pool rows of {pool.shape[2:].numel()} elements, the shape needs {row}")
     if block_table.shape[0] < shape.batch:
         raise ValueError(f"{name}: block table has {block_table.shape[0]} rows for {shape.batch} requests")
     return CPages(_dev(block_table, name + " block_table"), int(block_table.shape[1]),
@@ -203,7 +205,7 @@ def indexer_score_paged(shape, q_idx, w, k_pool, k_scale, block_table, start_pos
     """k_pool [n_blocks, block_size, Di] (shape.dtype keys, or uint8 E4M3 codes
     with k_scale [n_blocks, block_size] float32); block_table [B, bpr] int32."""
     cs, n, dt = CShape.of(shape), _sizes(shape), torch_dtype(shape)
-    pg = _pages(shape, k_pool, block_table, "k_pool")
+    pg = _pages(shape, k_pool, block_table, "k_pool", shape.idx_dim)
     rows = pg.n_blocks * pg.block_size
     kdt = torch.uint8 if k_scale is not None else dt
     _check("csa_indexer_score_paged", lib().csa_indexer_score_paged(
@@ -267,13 +269,13 @@ def sparse_attn_decode_paged(shape, q, k_win, v_win, k_pool, v_pool, block_table
     cs, dt = CShape.of(shape), torch_dtype(shape)
     if k_pool.shape != v_pool.shape:
         raise ValueError("k_pool and v_pool must have the same shape")
-    pg = _pages(shape, k_pool, block_table, "k_pool")
+    pg = _pages(shape, k_pool, block_table, "k_pool", shape.head_dim)
     rows = pg.n_blocks * pg.block_size
     wpg, win_numel = None, None
     if win_table is not None:
         if k_win.shape != v_win.shape:
             raise ValueError("k_win and v_win pools must have the same shape")
-        wpg = _pages(shape, k_win, win_table, "k_win")
+        wpg = _pages(shape, k_win, win_table, "k_win", shape.head_dim)
         win_numel = wpg.n_blocks * wpg.block_size * shape.head_dim
     c = _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out, win_numel)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()

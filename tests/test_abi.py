@@ -219,6 +219,19 @@ def test_binding_refuses_rope_tables_of_the_wrong_layout():
             C.sparse_attn_decode(sh, t, t, t, t, t, t, t, cos, sin, 0.1, t, t)
 
 
+def test_binding_refuses_pools_of_the_wrong_row_width():
+    # pool rows are read at a stride of Di (indexer) or D (attention) elements
+    import torch
+    sh = shape()
+    t = torch.zeros(4)
+    table = torch.zeros(sh.batch, 64, dtype=torch.int32)
+    with pytest.raises(ValueError, match="pool rows"):
+        C.indexer_score_paged(sh, t, t, torch.zeros(8, 16, sh.idx_dim + 8), None, table, t, t)
+    bad = torch.zeros(8, 16, sh.head_dim // 2)
+    with pytest.raises(ValueError, match="pool rows"):
+        C.sparse_attn_decode_paged(sh, t, t, t, bad, bad, table, t, t, None, None, 0.1, t, t)
+
+
 # --------------------------------------------------------------------------
 # paged compressed caches
 # --------------------------------------------------------------------------
