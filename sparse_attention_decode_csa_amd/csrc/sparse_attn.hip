@@ -160,10 +160,10 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D>& ch, const u32x4
 }
 
 // Split partials of a token, merged in ascending split order into the state
-// of their stream (window splits first, then compressed).  Loads of up to
-// kMergeBatch splits are issued before any of them is used, so a token with
-// at most that many splits costs one round trip.
-constexpr int kMergeBatch = 8;
+// of their stream (window splits first, then compressed).  Loads of up to MB
+// splits (one batch) are issued before any of them is used, so a token with
+// at most MB splits costs one round trip.  The launch takes MB = 8 when every
+// token has at most 8 splits and MB = 16 otherwise.
 
 struct StreamState {
   float m, l, o0, o1;
@@ -179,18 +179,20 @@ __device__ __forceinline__ void merge_into(StreamState& st, float m, float l, fl
   st.m = mn;
 }
 
-// (max, sum, dim pair of the partial sum) of splits b0 .. b0+kMergeBatch-1
+// (max, sum, dim pair of the partial sum) of splits b0 .. b0+MB-1
 // for one (token, head, dim pair); splits past the last read as empty.
+template <int MB>
 struct SplitBatch {
-  float m[kMergeBatch], l[kMergeBatch];
-  float2 o[kMergeBatch];
+  float m[MB], l[MB];
+  float2 o[MB];
 };
 
+template <int MB>
 __device__ __forceinline__ void load_splits(const AttnArgs& a, int tok, int h, int d, int D, int b0,
-                                            SplitBatch& sb) {
+                                            SplitBatch<MB>& sb) {
   const int NS = a.n_split_win + a.n_split_cmp;
 #pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k) {
+  for (int k = 0; k < MB; ++k) {
     const int sp = min(b0 + k, NS - 1);
     const size_t r = ((size_t)tok * NS + sp) * a.heads + h;
     const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + 2 * r);
@@ -200,10 +202,11 @@ __device__ __forceinline__ void load_splits(const AttnArgs& a, int tok, int h, i
   }
 }
 
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int b0, const SplitBatch& sb, StreamState& w,
+template <int MB>
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int b0, const SplitBatch<MB>& sb, StreamState& w,
                                              StreamState& c) {
 #pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k) {
+  for (int k = 0; k < MB; ++k) {
     if (b0 + k < a.n_split_win) merge_into(w, sb.m[k], sb.l[k], sb.o[k]);
     else merge_into(c, sb.m[k], sb.l[k], sb.o[k]);
   }
@@ -214,15 +217,15 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int b0, const Sp
 // group layout.  The first batch of partials does not depend on the token's
 // position, so it is read before the position and the RoPE table row that
 // depends on it: the two reads overlap instead of adding up.
-template <typename T, int D>
+template <typename T, int D, int MB>
 __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int item) {
   const int H = a.heads, G = a.out_groups, Hg = H / G;
   const int T_ = a.batch * a.q_per_req;
   const int r0 = D - a.rope_dim;
   const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
   const int NS = a.n_split_win + a.n_split_cmp;
-  SplitBatch sb;
-  load_splits(a, tok, h, d, D, 0, sb);
+  SplitBatch<MB> sb;
+  load_splits<MB>(a, tok, h, d, D, 0, sb);
   const int S = a.q_per_req;
   const int p = clamp_pos(a.start_pos[tok / S] + tok % S, a.max_len);
   float cs = 1.0f, sn = 0.0f;
@@ -233,8 +236,8 @@ __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int item
   }
   StreamState w{-INFINITY, 0.0f, 0.0f, 0.0f}, c = w;
   merge_splits(a, 0, sb, w, c);
-  for (int b0 = kMergeBatch; b0 < NS; b0 += kMergeBatch) {
-    load_splits(a, tok, h, d, D, b0, sb);
+  for (int b0 = MB; b0 < NS; b0 += MB) {
+    load_splits<MB>(a, tok, h, d, D, b0, sb);
     merge_splits(a, b0, sb, w, c);
   }
   // stream merge: an empty stream (sum 0) carries no weight
@@ -419,12 +422,12 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
 
 // The epilogue: one thread per (token, head, dim pair), after every split
 // partial of the step has been written (stream order).
-template <typename T, int D>
+template <typename T, int D, int MB>
 __global__ __launch_bounds__(kFinishThreads) void attn_finish_kernel(AttnArgs a) {
   const int tok = blockIdx.x;
   const int item = blockIdx.y * kFinishThreads + threadIdx.x;
   if (item >= a.heads * (D / 2)) return;
-  finish_item<T, D>(a, tok, item);
+  finish_item<T, D, MB>(a, tok, item);
 }
 
 template <typename T, int D>
@@ -448,7 +451,10 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 fgrid(tokens, (a.heads * (D / 2) + kFinishThreads - 1) / kFinishThreads);
-  hipLaunchKernelGGL((attn_finish_kernel<T, D>), fgrid, dim3(kFinishThreads), 0, st, a);
+  if (NS <= 8)
+    hipLaunchKernelGGL((attn_finish_kernel<T, D, 8>), fgrid, dim3(kFinishThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_finish_kernel<T, D, 16>), fgrid, dim3(kFinishThreads), 0, st, a);
   return hipGetLastError();
 }
 
