@@ -405,11 +405,17 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int DI, int HI, bool PG>
+// KF8: FP8 key cache (E4M3 codes, one fp32 scale per row).  The ring holds
+// the codes; each lane widens its 8 codes per k-step to bf16 (exact: every
+// E4M3 value is a bf16 value) and the row's scale multiplies the head sum, as
+// in the kernel above.
+template <int DI, int HI, bool PG, bool KF8>
 __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_score_gemm_kernel(ScoreArgs a) {
   typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
-  constexpr int ROW = DI * 2;                          // bytes per query / key row
+  constexpr int QROW = DI * 2;                         // bytes per query row
+  constexpr int ROW = KF8 ? DI : DI * 2;               // bytes per key row
   constexpr int KS = DI / 16;                          // 16-dim MFMA k-steps
   constexpr int MT = 2;                                // 32-row M tiles per wave
   constexpr int TPL = 16 / HI;                         // tokens per lane per M tile
@@ -424,6 +430,7 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
   static_assert(NSTEPS >= 2 * NB, "a block spans at least two ring rounds");
 
   __shared__ __attribute__((aligned(1024))) char ring[NB][STEP_BYTES];
+  __shared__ float kscale[KF8 ? kGemmKeys : 1];        // scales of the block's key rows
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -461,14 +468,14 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
   float wv[MT][16];
   uint32_t sbase[MT][TPL];   // byte offset of (token, key l32) in the block's score rows
   int slim[MT][TPL];         // store while key0 + st*32 < slim (visible count - l32; 0: never)
-  const char* qbase = static_cast<const char*>(a.q_idx) + tok0 * HI * ROW;
+  const char* qbase = static_cast<const char*>(a.q_idx) + tok0 * HI * QROW;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int tile_row0 = wave * 64 + mt * 32;
     {
       const int m = l32, i = (m >> 3) * 4 + (m & 3);
       const int row = tile_row0 + ((m >> 2) & 1) * TPL * HI + i;  // token*HI + head, in block rows
-      const char* qp = qbase + (size_t)min(row, SH - 1) * ROW + 16 * half;
+      const char* qp = qbase + (size_t)min(row, SH - 1) * QROW + 16 * half;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qa[mt][ks] = ld16(qp + 32 * ks);
     }
@@ -481,6 +488,21 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
       const int nv = s < S ? min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap) : 0;
       sbase[mt][tt] = (uint32_t)(min(s, S - 1) * a.n_cap + l32) * 4u;
       slim[mt][tt] = nv > a.topk ? nv - l32 : INT32_MIN;   // past the block, or fits Top-K: never
+    }
+  }
+  // FP8: the scales of keys key0 + 4*tid .. +3 (rows past nmax repeat the
+  // last one), loaded before any DMA and published by the first step's barrier
+  float ksv[KF8 ? 4 : 1];
+  if constexpr (KF8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = min(key0 + 4 * (int)threadIdx.x + i, nmax - 1);
+      size_t row = (size_t)b * a.n_cap + j;
+      if constexpr (PG) {
+        const int blk = __shfl(pblk, (j >> a.block_shift) - (key0 >> a.block_shift));
+        row = ((size_t)blk << a.block_shift) + (size_t)(j & ((1 << a.block_shift) - 1));
+      }
+      ksv[i] = a.k_scale[row];
     }
   }
   // scores of this block's tokens, addressed by buffer stores (32-bit offsets)
@@ -542,6 +564,7 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
           const float x = acc[mt][tt * HI + h];
           sum += wv[mt][tt * HI + h] * relu_bits(x);
         }
+        if constexpr (KF8) sum *= kscale[max(st_done, 0) * kGemmStepKeys + l32];
         const uint32_t off = st_done >= 0 && jb < slim[mt][tt] ? sbase[mt][tt] + (uint32_t)jb * 4u : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), srs, off, 0, kNonTemporal);
       }
@@ -557,8 +580,18 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int sl = (2 * ks + half) ^ (r % TL::NPR);
-      const u32x4_t kb = *reinterpret_cast<const u32x4_t*>(src + u * TL::BYTES + r * ROW + 16 * sl);
+      u32x4_t kb;
+      if constexpr (KF8) {  // dims 16*ks + 8*half .. +8: half of piece ks
+        const int sl = ks ^ (r % TL::NPR);
+        const uint2 w = *reinterpret_cast<const uint2*>(src + u * TL::BYTES + r * ROW + 16 * sl + 8 * half);
+        kb = u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true))};
+      } else {
+        const int sl = (2 * ks + half) ^ (r % TL::NPR);
+        kb = *reinterpret_cast<const u32x4_t*>(src + u * TL::BYTES + r * ROW + 16 * sl);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[mt][ks]),
@@ -579,6 +612,10 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
 #pragma unroll
   for (int st = 0; st < NB - 1; ++st) issue_step(st, st);
   wait_vmcnt<(NB - 1) * DPW>();
+  if constexpr (KF8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kscale[4 * threadIdx.x + i] = ksv[i];
+  }
 
   // Step st is in once at most the younger operations are outstanding: the
   // DMA of up to NB - 2 younger steps and the stores of the up to NB - 1
@@ -633,12 +670,12 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
   wait_vmcnt<0>();  // no DMA may still be writing this block's LDS when it exits
 }
 
-template <int DI, bool PG>
+template <int DI, bool PG, bool KF8>
 hipError_t launch_gemm(const ScoreArgs& a, dim3 grid, hipStream_t st) {
   switch (a.idx_heads) {
-    case 4: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 4, PG>), grid, dim3(kGemmThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 8, PG>), grid, dim3(kGemmThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 16, PG>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 4, PG, KF8>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 8, PG, KF8>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((indexer_score_gemm_kernel<DI, 16, PG, KF8>), grid, dim3(kGemmThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -687,12 +724,13 @@ hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
   const int n_bound = std::min(in.n_cap, in.max_len / in.ratio);
   if (n_bound <= in.topk) return hipSuccess;  // every token fits Top-K: nothing to score
   // Prefill chunks (at least two blocks of 256 query rows per request) with
-  // bf16 keys and 4, 8 or 16 heads: the shared-key-step kernel.
+  // bf16 queries, bf16 keys or 128-dim FP8 keys, and 4, 8 or 16 heads: the
+  // shared-key-step kernel.
 #ifndef CSA_SCORE_GEMM_MIN_ROWS
 #define CSA_SCORE_GEMM_MIN_ROWS 512
 #endif
   const long long rows_req = (long long)in.q_per_req * in.idx_heads;
-  if (in.dtype == 1 && !in.k_scale && rows_req >= CSA_SCORE_GEMM_MIN_ROWS &&
+  if (in.dtype == 1 && (!in.k_scale || in.idx_dim == 128) && rows_req >= CSA_SCORE_GEMM_MIN_ROWS &&
       (in.idx_heads == 4 || in.idx_heads == 8 || in.idx_heads == 16)) {
     const int tok_per_block = kGemmRows / in.idx_heads;
     const int row_blocks = (in.q_per_req + tok_per_block - 1) / tok_per_block;
@@ -700,9 +738,11 @@ hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
     if (row_blocks <= 65535 && (long long)tok_per_block * in.n_cap * 4 < 0x7FFFF000LL &&
         (long long)in.n_cap * in.idx_dim * 2 < 0x7FFFF000LL) {
       const dim3 grid((n_bound + kGemmKeys - 1) / kGemmKeys, in.batch, row_blocks);
+      if (in.k_scale)
+        return in.block_table ? launch_gemm<128, true, true>(in, grid, st) : launch_gemm<128, false, true>(in, grid, st);
       if (in.block_table)
-        return in.idx_dim == 128 ? launch_gemm<128, true>(in, grid, st) : launch_gemm<64, true>(in, grid, st);
-      return in.idx_dim == 128 ? launch_gemm<128, false>(in, grid, st) : launch_gemm<64, false>(in, grid, st);
+        return in.idx_dim == 128 ? launch_gemm<128, true, false>(in, grid, st) : launch_gemm<64, true, false>(in, grid, st);
+      return in.idx_dim == 128 ? launch_gemm<128, false, false>(in, grid, st) : launch_gemm<64, false, false>(in, grid, st);
     }
   }
   // Query rows per workgroup: all of a request's when they fit in 64 (decode),

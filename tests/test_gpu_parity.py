@@ -293,12 +293,12 @@ def test_end_to_end_paged(fmt, bs, win):
 # prefill indexer: many query tokens per request (q_per_req = chunk length)
 # --------------------------------------------------------------------------
 
-def prefill_cfg(T, K, Hi, start, B=2, grid=False, Di=128):
+def prefill_cfg(T, K, Hi, start, B=2, grid=False, Di=128, key_format="bf16"):
     max_len = start + T
     cfg = small_cfg(name="prefill", batch=B, q_per_req=T, topk=K, idx_heads=Hi, idx_dim=Di,
                     n_cap=max(256, max_len // 4), win=64, w_cap=64 + T, heads=4,
                     max_len=max_len)
-    inp = I.make_inputs(cfg, start_pos=np.full(B, start, np.int32))
+    inp = I.make_inputs(cfg, start_pos=np.full(B, start, np.int32), key_format=key_format)
     if grid:   # dyadic grid: every partial sum exact on both sides
         g = np.random.default_rng(T + K)
         inp["q_idx"] = I.f32_to_bf16_bits((g.integers(-8, 9, inp["q_idx"].shape) / 4.0).astype(np.float32))
@@ -309,12 +309,14 @@ def prefill_cfg(T, K, Hi, start, B=2, grid=False, Di=128):
     return cfg.shape, inp
 
 
-@pytest.mark.parametrize("T,K,Hi,start", [(512, 64, 8, 0), (1024, 256, 8, 3000), (300, 128, 5, 1000),
-                                          (2048, 1024, 4, 30000)])
-def test_prefill_indexer_topk(T, K, Hi, start):
+@pytest.mark.parametrize("T,K,Hi,start,fmt", [(512, 64, 8, 0, "bf16"), (1024, 256, 8, 3000, "bf16"),
+                                              (300, 128, 5, 1000, "bf16"), (2048, 1024, 4, 30000, "bf16"),
+                                              (1024, 512, 8, 12000, "fp8"), (600, 128, 16, 4000, "fp8")])
+def test_prefill_indexer_topk(T, K, Hi, start, fmt):
     # Each of the T tokens scores its own causally visible rows (widths well
     # past 256) and selects its own Top-K; bypass tokens get bounded indices.
-    sh, inp = prefill_cfg(T, K, Hi, start)
+    # fp8: an FP8 key cache with per-row amax/448 scales (GEMM-shaped kernel).
+    sh, inp = prefill_cfg(T, K, Hi, start, key_format=fmt)
     ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
     got = gpu_step(sh, inp, jobs=("score", "topk"))
     check_scores(sh, inp, got, ref)
@@ -322,50 +324,37 @@ def test_prefill_indexer_topk(T, K, Hi, start):
     bound = U.score_error_bound(sh, inp, rows)
     exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
                                inp["start_pos"])
-    print(f"prefill T={T}: {len(rows)} scored tokens, {len(exempt)} boundary exemptions")
+    print(f"prefill {fmt} T={T}: {len(rows)} scored tokens, {len(exempt)} boundary exemptions")
     assert len(exempt) <= max(1, len(rows) // 32)
     # and the selection alone is bit-exact on the oracle's scores
     got2 = gpu_step(sh, inp, scores=ref["scores"], jobs=("topk",))
     assert np.array_equal(got2["topk_idx"], ref["topk_idx"])
 
 
-@pytest.mark.parametrize("T,K,Hi,start,Di,bs", [
-    (600, 256, 8, 1500, 128, 0),      # partial last row block and key step
-    (333, 100, 4, 5000, 64, 0),
-    (200, 64, 16, 9000, 128, 0),
-    (700, 512, 8, 9300, 128, 0),      # several key blocks of 1024
-    (600, 256, 8, 1500, 128, 16),     # paged indexer cache
-    (333, 100, 4, 5000, 64, 64),
-    (300, 150, 8, 500, 128, 0),       # blocks mixing tokens that fit Top-K with scored ones
+@pytest.mark.parametrize("T,K,Hi,start,Di,bs,scales", [
+    (600, 256, 8, 1500, 128, 0, "pow2"),     # GEMM-shaped kernel, FP8 keys
+    (333, 100, 4, 5000, 64, 16, "pow2"),     # 64 dims: decode-shaped kernel, paged codes and scales
+    (200, 64, 16, 9000, 128, 0, "one"),
+    (300, 150, 5, 500, 64, 0, "pow2"),       # 5 heads: the LDS head-sum path; tokens that fit Top-K
+    (700, 256, 8, 3000, 128, 64, "pow2"),    # GEMM-shaped, paged (64-row blocks)
+    (520, 128, 4, 2000, 128, 16, "pow2"),    # GEMM-shaped, paged (16-row blocks), 4 heads
+    (1100, 512, 8, 12000, 128, 0, "pow2"),   # several key blocks and row blocks
 ])
-def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
-    # Dyadic inputs: every partial sum is exact on both sides, so scores and
-    # lists are bitwise equal.  Chunks of at least 512 query rows per request
-    # with 4, 8 or 16 heads take the shared-key-step score kernel.
-    sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
-    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
-    if bs:
-        inp = I.page_inputs(inp, bs, seed=T + bs, cmp=False)
-    got = gpu_step(sh, inp, jobs=("score", "topk"))
-    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
-    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
-
-
-@pytest.mark.parametrize("T,K,Hi,start,Di,bs", [
-    (600, 256, 8, 1500, 128, 0),
-    (333, 100, 4, 5000, 64, 16),      # paged FP8 codes and scales
-    (200, 64, 16, 9000, 128, 0),
-    (300, 150, 5, 500, 64, 0),        # 5 heads: the LDS head-sum path; tokens that fit Top-K
-])
-def test_prefill_indexer_fp8_exact_grid(T, K, Hi, start, Di, bs):
+def test_prefill_indexer_fp8_exact_grid(T, K, Hi, start, Di, bs, scales):
     # A prefill chunk over an FP8 indexer key cache: the grid keys m/4 are
-    # E4M3 values, so codes with scale 1 hold them exactly and scores and
-    # lists stay bitwise equal (the chunk's token blocks run the FP8 variant
-    # of the decode-shaped score kernel).
+    # E4M3 values, so codes hold them exactly; row scales that are powers of
+    # two keep every product exact, so scores and lists stay bitwise equal.
+    # Chunks with 128-dim keys and 4, 8 or 16 heads run the GEMM-shaped
+    # kernel, the others the decode-shaped one; the scales are drawn per row
+    # so that a scale applied to the wrong key shows.
     sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
     kf = I.bf16_bits_to_f32(inp.pop("k_idx"))
     inp["k_idx8"] = I.f32_to_e4m3_bits(kf)          # poison saturates to 448: never read
-    inp["k_scale"] = np.ones(kf.shape[:2], dtype=np.float32)
+    if scales == "one":
+        inp["k_scale"] = np.ones(kf.shape[:2], dtype=np.float32)
+    else:
+        g = np.random.default_rng(T * 7 + Hi)
+        inp["k_scale"] = np.exp2(g.integers(-2, 3, size=kf.shape[:2])).astype(np.float32)
     ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
     if bs:
         inp = I.page_inputs(inp, bs, seed=T + bs, cmp=False)
