@@ -331,6 +331,28 @@ def test_prefill_indexer_topk(T, K, Hi, start, fmt):
     assert np.array_equal(got2["topk_idx"], ref["topk_idx"])
 
 
+@pytest.mark.parametrize("T,K,Hi,start,Di,bs", [
+    (600, 256, 8, 1500, 128, 0),      # partial last row block and key step
+    (333, 100, 4, 5000, 64, 0),
+    (200, 64, 16, 9000, 128, 0),
+    (700, 512, 8, 9300, 128, 0),      # several key blocks of 1024
+    (600, 256, 8, 1500, 128, 16),     # paged indexer cache
+    (333, 100, 4, 5000, 64, 64),
+    (300, 150, 8, 500, 128, 0),       # blocks mixing tokens that fit Top-K with scored ones
+])
+def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
+    # Dyadic inputs: every partial sum is exact on both sides, so scores and
+    # lists are bitwise equal.  Chunks of at least 512 query rows per request
+    # with 4, 8 or 16 heads take the shared-key-step score kernel.
+    sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    if bs:
+        inp = I.page_inputs(inp, bs, seed=T + bs, cmp=False)
+    got = gpu_step(sh, inp, jobs=("score", "topk"))
+    assert np.array_equal(got["scores"], ref["scores"], equal_nan=True)
+    assert np.array_equal(got["topk_idx"], ref["topk_idx"])
+
+
 @pytest.mark.parametrize("T,K,Hi,start,Di,bs,scales", [
     (600, 256, 8, 1500, 128, 0, "pow2"),     # GEMM-shaped kernel, FP8 keys
     (333, 100, 4, 5000, 64, 16, "pow2"),     # 64 dims: decode-shaped kernel, paged codes and scales
