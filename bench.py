@@ -153,7 +153,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "the step runs on one GPU (no multi-GPU path); run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
