@@ -72,8 +72,9 @@ static double e4m3_val(uint8_t code) {
  * (k_idx8 non-NULL) the row is stored as E4M3 codes plus one fp32 scale per
  * row, and its value is scale * decode(code) (the pages pass an indexer key
  * cache together with its scale, "Fix: complete DeepSeek V4 TP CSA decode",
- * description; the encoding and the per-row granularity are this build's
- * reading).  Otherwise the row is read in the input dtype. */
+ * description; the encoding and the per-row granularity are a reading of
+ * that passage, which names neither).  Otherwise the row is read in the
+ * input dtype. */
 static double key_val(const oracle_shape_t *sh, const void *k_idx, const uint8_t *k_idx8,
                       const float *k_scale, int32_t b, int32_t j, int32_t c) {
   const size_t row = (size_t)b * sh->n_cap + (size_t)j;
