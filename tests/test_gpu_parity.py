@@ -610,8 +610,9 @@ def test_end_to_end_exact_grid(n_cap, topk, S, Hi):
 def random_grid_case(seed, prefill=False):
     """A seeded random shape inside the supported ranges, with dyadic-grid
     indexer inputs (every score exact on both sides) and, for some seeds,
-    every cache paged.  prefill: hundreds of tokens per request with 4, 8 or
-    16 bf16 indexer heads, the shape of the GEMM-shaped score kernel."""
+    an FP8 indexer key cache or every cache paged.  prefill: hundreds of
+    tokens per request with 4, 8 or 16 indexer heads, the shape of the
+    GEMM-shaped score kernel."""
     g = np.random.default_rng([seed, 77, int(prefill)])
     dt = I.F32 if (g.random() < 0.25 and not prefill) else I.BF16
     ratio = int(g.choice([1, 2, 4, 8])) if not prefill else 4
@@ -642,21 +643,23 @@ def random_grid_case(seed, prefill=False):
               else np.float32(I.POISON))
     inp["k_idx"] = np.where(inp["k_idx"] == poison, inp["k_idx"], grid(inp["k_idx"].shape))
     inp["w"] = (g.integers(0, 17, inp["w"].shape) / 16.0).astype(np.float32)
-    if dt == I.BF16 and not prefill and g.random() < 0.3:
+    if dt == I.BF16 and g.random() < (0.5 if prefill else 0.3):
         # FP8 key cache: every grid value m/4 (|m| <= 8) is an E4M3 value, so
-        # codes with scale 1 hold the same keys (poisoned rows: the largest
-        # finite code, 448)
+        # codes hold the same keys (poisoned rows: the largest finite code,
+        # 448); prefill cases scale each row by a random power of two, which
+        # keeps every score exact
         kf = I.bf16_bits_to_f32(inp["k_idx"])
         codes = I.f32_to_e4m3_bits(np.where(kf == np.float32(I.POISON), np.float32(448.0), kf))
         inp["k_idx8"] = codes
-        inp["k_scale"] = np.ones(inp["k_idx"].shape[:2], dtype=np.float32)
+        inp["k_scale"] = (np.exp2(g.integers(-2, 3, size=inp["k_idx"].shape[:2])).astype(np.float32)
+                          if prefill else np.ones(inp["k_idx"].shape[:2], dtype=np.float32))
         del inp["k_idx"]
     if g.random() < 0.3:
         inp = I.page_inputs(inp, int(g.choice([16, 32, 64])), seed=seed, win=True)
     return sh, inp
 
 
-@pytest.mark.parametrize("seed,prefill", [(k, False) for k in range(64)] + [(k, True) for k in range(8)])
+@pytest.mark.parametrize("seed,prefill", [(k, False) for k in range(64)] + [(k, True) for k in range(18)])
 def test_random_shapes_exact_grid(seed, prefill):
     # scores and lists bitwise, attention within tolerance, over random
     # shapes: ratio, batch, tokens per request, K (bypass and not), capacities,
