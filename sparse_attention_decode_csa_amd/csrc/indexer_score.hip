@@ -723,14 +723,20 @@ hipError_t launch_layout(const ScoreArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
   const int n_bound = std::min(in.n_cap, in.max_len / in.ratio);
   if (n_bound <= in.topk) return hipSuccess;  // every token fits Top-K: nothing to score
-  // Prefill chunks (at least two blocks of 256 query rows per request) with
-  // bf16 queries, bf16 keys or 128-dim FP8 keys, and 4, 8 or 16 heads: the
-  // shared-key-step kernel.
+  // Prefill chunks with bf16 queries, bf16 keys or 128-dim FP8 keys, and 4, 8
+  // or 16 heads: the shared-key-step kernel, from the query-row count per
+  // request at which it overtakes the kernel above (measured: about 2048 rows
+  // with bf16 keys, 4096 with FP8 keys, whose widening costs it VALU issue;
+  // below that its few 256-row blocks leave most CUs idle).
 #ifndef CSA_SCORE_GEMM_MIN_ROWS
-#define CSA_SCORE_GEMM_MIN_ROWS 512
+#define CSA_SCORE_GEMM_MIN_ROWS 2048
+#endif
+#ifndef CSA_SCORE_GEMM_MIN_ROWS_FP8
+#define CSA_SCORE_GEMM_MIN_ROWS_FP8 4096
 #endif
   const long long rows_req = (long long)in.q_per_req * in.idx_heads;
-  if (in.dtype == 1 && (!in.k_scale || in.idx_dim == 128) && rows_req >= CSA_SCORE_GEMM_MIN_ROWS &&
+  const long long min_rows = in.k_scale ? CSA_SCORE_GEMM_MIN_ROWS_FP8 : CSA_SCORE_GEMM_MIN_ROWS;
+  if (in.dtype == 1 && (!in.k_scale || in.idx_dim == 128) && rows_req >= min_rows &&
       (in.idx_heads == 4 || in.idx_heads == 8 || in.idx_heads == 16)) {
     const int tok_per_block = kGemmRows / in.idx_heads;
     const int row_blocks = (in.q_per_req + tok_per_block - 1) / tok_per_block;

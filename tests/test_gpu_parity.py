@@ -333,16 +333,16 @@ def test_prefill_indexer_topk(T, K, Hi, start, fmt):
 
 @pytest.mark.parametrize("T,K,Hi,start,Di,bs", [
     (600, 256, 8, 1500, 128, 0),      # partial last row block and key step
-    (333, 100, 4, 5000, 64, 0),
+    (533, 100, 4, 5000, 64, 0),
     (200, 64, 16, 9000, 128, 0),
     (700, 512, 8, 9300, 128, 0),      # several key blocks of 1024
     (600, 256, 8, 1500, 128, 16),     # paged indexer cache
-    (333, 100, 4, 5000, 64, 64),
+    (533, 100, 4, 5000, 64, 64),
     (300, 150, 8, 500, 128, 0),       # blocks mixing tokens that fit Top-K with scored ones
 ])
 def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
     # Dyadic inputs: every partial sum is exact on both sides, so scores and
-    # lists are bitwise equal.  Chunks of at least 512 query rows per request
+    # lists are bitwise equal.  Chunks of at least 2048 query rows per request
     # with 4, 8 or 16 heads take the shared-key-step score kernel.
     sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
     ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
@@ -356,19 +356,20 @@ def test_prefill_indexer_exact_grid(T, K, Hi, start, Di, bs):
 @pytest.mark.parametrize("T,K,Hi,start,Di,bs,scales", [
     (600, 256, 8, 1500, 128, 0, "pow2"),     # GEMM-shaped kernel, FP8 keys
     (333, 100, 4, 5000, 64, 16, "pow2"),     # 64 dims: decode-shaped kernel, paged codes and scales
-    (200, 64, 16, 9000, 128, 0, "one"),
+    (300, 64, 16, 9000, 128, 0, "one"),
     (300, 150, 5, 500, 64, 0, "pow2"),       # 5 heads: the LDS head-sum path; tokens that fit Top-K
     (700, 256, 8, 3000, 128, 64, "pow2"),    # GEMM-shaped, paged (64-row blocks)
-    (520, 128, 4, 2000, 128, 16, "pow2"),    # GEMM-shaped, paged (16-row blocks), 4 heads
+    (1100, 128, 4, 2000, 128, 16, "pow2"),   # GEMM-shaped, paged (16-row blocks), 4 heads
     (1100, 512, 8, 12000, 128, 0, "pow2"),   # several key blocks and row blocks
 ])
 def test_prefill_indexer_fp8_exact_grid(T, K, Hi, start, Di, bs, scales):
     # A prefill chunk over an FP8 indexer key cache: the grid keys m/4 are
     # E4M3 values, so codes hold them exactly; row scales that are powers of
     # two keep every product exact, so scores and lists stay bitwise equal.
-    # Chunks with 128-dim keys and 4, 8 or 16 heads run the GEMM-shaped
-    # kernel, the others the decode-shaped one; the scales are drawn per row
-    # so that a scale applied to the wrong key shows.
+    # Chunks of at least 4096 query rows per request with 128-dim keys and 4,
+    # 8 or 16 heads run the GEMM-shaped kernel, the others the decode-shaped
+    # one; the scales are drawn per row, so that a scale applied to the wrong
+    # key shows.
     sh, inp = prefill_cfg(T, K, Hi, start, grid=True, Di=Di)
     kf = I.bf16_bits_to_f32(inp.pop("k_idx"))
     inp["k_idx8"] = I.f32_to_e4m3_bits(kf)          # poison saturates to 448: never read
