@@ -510,8 +510,12 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
 
   // DMA of step st: instruction i = wave*DPW + d fills tile u = i / NPT, rows
   // k*RPI + lane/NPR (k = i % NPT) with the piece swizzle of the kernel above.
-  // Dense keys: buffer loads against the request's key rows (rows past n_cap
-  // read as zero; rows past nmax are read and never used).  Paged keys: rows
+  // Dense keys: buffer loads against the request's key rows.  The whole byte
+  // offset, step included, goes in the per-lane offset: the range check of a
+  // raw buffer access covers that offset only (the scalar offset is added
+  // unchecked), so rows at or past n_cap read as zero without touching
+  // memory, even for the steps the prologue issues past the last one.  Rows
+  // past nmax but below n_cap are read and never used.  Paged keys: rows
   // clamped to nmax - 1 and mapped through the block table.
   int lrow[DPW];
   uint32_t loff[DPW];
@@ -538,7 +542,8 @@ __global__ __launch_bounds__(kGemmThreads, CSA_GEMM_BLOCKS_PER_CU) void indexer_
         const size_t row = ((size_t)blk << a.block_shift) + (size_t)(j & ((1 << a.block_shift) - 1));
         dma16_global<kNonTemporal>(kreq + row * ROW + (loff[d] - (uint32_t)(lrow[d] * ROW)), lds);
       } else {
-        dma16_buffer<kNonTemporal>(krs, lds, loff[d], (uint32_t)(step0 * ROW));
+        // < 2^32: n_cap * ROW < 2^31 and step0 < n_cap + kGemmKeys
+        dma16_buffer<kNonTemporal>(krs, lds, loff[d] + (uint32_t)step0 * (uint32_t)ROW, 0u);
       }
     }
   };
