@@ -1,16 +1,26 @@
 """Benchmark of one CSA sparse-attention decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--cache flushed|hot]
 
 A step is one pass of the whole path on one batch of seeded synthetic input
 already resident in HBM: indexer scoring, Top-K (with the fits-in-Top-K
 bypass), and two-stream attention with the fused merge / inverse RoPE /
 packing epilogue, issued through the C ABI on one stream.
 
-Prints ONE JSON line: query tokens per second over the timed steps, the
-roofline of the dominant kernel (algorithmic bytes / its HIP-event-timed
-average duration against 8 TB/s), per-stage figures, and the CPU oracle timed
-on the host as a baseline.
+Timing follows the pages' protocol of timed rounds after warm-ups ("Perf:
+skip redundant CSA scoring and fuse gather unpack" and "Perf: fuse HCA merge,
+inverse RoPE, and packing", descriptions): W untimed steps, then K timed
+steps.  With --cache flushed (the default) a 1 GiB scratch buffer is written
+before every timed step, outside the events that bracket the step's calls, so
+that neither the L2s nor the 256 MB Infinity Cache hold anything the step
+reads; the step time is the median (and minimum) of those event intervals.
+A back-to-back pass of exactly K steps between two synchronisations is also
+timed and reported under "hot".
+
+Prints ONE JSON line: query tokens per second, the roofline of the dominant
+kernel (algorithmic bytes / its median HIP-event-timed duration over at least
+64 flushed launches, against 8 TB/s), per-stage figures, and the CPU oracle
+timed on the host as a baseline.
 """
 from __future__ import annotations
 
@@ -18,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -27,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CPU_SHARE = 16                   # host cores a one-GPU job may use on the GPU machine
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "sparse_attention_decode_csa_amd", "csrc")
@@ -53,9 +65,13 @@ def parse():
     ap.add_argument("--query-sets", type=int, default=4,
                     help="query sets cycled over the steps (queries rolled along the batch), so "
                          "consecutive steps select different compressed rows")
-    ap.add_argument("--event-every", type=int, default=8, metavar="E",
-                    help="record the events around the dominant kernel on every E-th timed "
-                         "step (two event records cost about 6 us per step on this path)")
+    ap.add_argument("--cache", choices=("flushed", "hot"), default="flushed",
+                    help="flushed: 1 GiB scratch write before each timed step (outside its "
+                         "events), step time = median event interval; hot: back-to-back steps, "
+                         "step time = wall time of the K steps / K")
+    ap.add_argument("--stage-launches", type=int, default=64,
+                    help="least number of flushed steps timed stage by stage (per-stage events)")
+    ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -205,18 +221,20 @@ def main():
         k_new = dev[kwin].reshape(-1, D_)[wb_slots.long()].contiguous()
         v_new = dev[vwin].reshape(-1, D_)[wb_slots.long()].contiguous()
 
-    # ev: events recorded around the stages, on the launch stream.  "dom" records
-    # only the two around the dominant kernel (the timed region keeps its
-    # event packets to those); "all" records the four stage boundaries.
+    # ev: events recorded on the launch stream.  mode "step" records the two
+    # that bracket the whole step (ev[0] before its first call, ev[4] after its
+    # last); mode "all" also the stage boundaries: ev[1] before scoring, ev[2]
+    # before Top-K, ev[3] before attention.  Each record is a packet of its own
+    # in the stream, so the step timing keeps to the bracketing pair.
     def run_step(ev=None, r=0, mode="all"):
         dev = qsets[r % R]
+        rec = ev is not None
+        rec_all = rec and mode == "all"
+        if rec: ev[0].record(stream)
         if args.writeback:
             C.swa_writeback(sh, k_new, v_new, wb_slots, dev[kwin], dev[vwin], stream)
-        rec_all = ev is not None and mode == "all"
-        rec_score = ev is not None and (mode == "all" or dominant == "indexer_score")
-        rec_attn = ev is not None and (mode == "all" or dominant == "sparse_attn")
+        if rec_all: ev[1].record(stream)
         if not cfg.supplied_topk:
-            if rec_score: ev[0].record(stream)
             if paged:
                 C.indexer_score_paged(sh, dev["q_idx"], dev["w"],
                                       dev["k_idx8_pool"] if fp8 else dev["k_idx_pool"],
@@ -228,13 +246,13 @@ def main():
             else:
                 C.indexer_score(sh, dev["q_idx"], dev["w"], dev["k_idx"], dev["start_pos"],
                                 bufs["scores"], stream)
-            if rec_score: ev[1].record(stream)
+            if rec_all: ev[2].record(stream)
             C.topk(sh, bufs["scores"], dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream)
             ti = bufs["topk_idx"]
         else:
-            if rec_all: ev[0].record(stream); ev[1].record(stream)
+            if rec_all: ev[2].record(stream)
             ti = dev["topk_idx"]
-        if rec_attn: ev[2].record(stream)
+        if rec_all: ev[3].record(stream)
         if not cfg.indexer_only and paged:
             C.sparse_attn_decode_paged(sh, dev["q"], dev[kwin], dev[vwin], dev["k_cmp_pool"],
                                        dev["v_cmp_pool"], dev["cmp_table"], ti, dev["start_pos"],
@@ -244,7 +262,7 @@ def main():
             C.sparse_attn_decode(sh, dev["q"], dev["k_win"], dev["v_win"], dev["k_cmp"], dev["v_cmp"],
                                  ti, dev["start_pos"], dev["rope_cos"], dev["rope_sin"], scale,
                                  bufs["out"], bufs["attn_ws"], stream)
-        if rec_attn: ev[3].record(stream)
+        if rec: ev[4].record(stream)
 
     # the dominant kernel: the larger algorithmic byte count (attention bytes
     # of the first query set decide it; scoring moves far more on the long
@@ -257,39 +275,70 @@ def main():
     dominant = ("indexer_score" if cfg.indexer_only or sb >= attn_bytes(sh, sp, ti0)[0]
                 else "sparse_attn")
 
+    # the 1 GiB scratch written before every flushed step: larger than the
+    # 256 MB Infinity Cache and the L2s together, so nothing the step reads is
+    # still cached when it starts (the write is outside the step's events)
+    scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+
+    def flush(k):
+        scratch.fill_(k & 0x7F)
+
+    def ev_set():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def us(e, a, b):
+        return e[a].elapsed_time(e[b]) * 1e3
+
     for k in range(args.warmup):
+        if args.cache == "flushed":
+            flush(k)
         run_step(r=k)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps; HIP events on the launch stream around the
-    # dominant kernel of every E-th step (each event record is a packet of its
-    # own in the stream: on every step the pair would add a few microseconds
-    # to the step being measured)
-    every = max(1, args.event_every)
-    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-           for k in range(0, args.steps, every)}
+    # timed region: exactly K steps between two synchronisations.  Flushed:
+    # each step after a flush, bracketed by its own pair of events.  Hot: back
+    # to back, wall time.
+    hot_steps = args.steps
+    step_us = []
+    if args.cache == "flushed":
+        sev = [ev_set() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            flush(k)
+            run_step(sev[k], r=k, mode="step")
+        torch.cuda.synchronize()
+        wall_flushed = time.perf_counter() - t0
+        step_us = [us(e, 0, 4) for e in sev]
+    # hot pass (the headline with --cache hot, a labelled extra otherwise)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        run_step(evs.get(k), r=k, mode="dom")
+    for k in range(hot_steps):
+        run_step(r=k)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1000.0 / args.steps
-    if dominant == "indexer_score":
-        t_dom = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()])) * 1e-3
+    hot_ms = (time.perf_counter() - t0) * 1000.0 / hot_steps
+    if args.cache == "flushed":
+        ms_per_step = float(np.median(step_us)) * 1e-3
     else:
-        t_dom = float(np.mean([e[2].elapsed_time(e[3]) for e in evs.values()])) * 1e-3
+        ms_per_step = hot_ms
 
-    # stage breakdown (outside the timed region): events at every stage boundary
-    nb = min(args.steps, 40)
-    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
+    # stage breakdown: at least --stage-launches steps with events at every
+    # stage boundary, flushed as the timed steps are (or back to back when hot)
+    nb = max(args.stage_launches, min(args.steps, 300))
+    gev = [ev_set() for _ in range(nb)]
     for k in range(nb):
-        run_step(sevs[k], r=k, mode="all")
+        if args.cache == "flushed":
+            flush(k)
+        run_step(gev[k], r=k, mode="all")
     torch.cuda.synchronize()
-    t_score = float(np.mean([e[0].elapsed_time(e[1]) for e in sevs])) * 1e-3
-    t_topk = float(np.mean([e[1].elapsed_time(e[2]) for e in sevs])) * 1e-3
-    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in sevs])) * 1e-3
-    t_event_step = float(np.mean([e[0].elapsed_time(e[3]) for e in sevs])) * 1e-3
+    st_us = {"indexer_score": [us(e, 1, 2) for e in gev], "topk": [us(e, 2, 3) for e in gev],
+             "sparse_attn": [us(e, 3, 4) for e in gev]}
+    t_score = float(np.median(st_us["indexer_score"])) * 1e-6
+    t_topk = float(np.median(st_us["topk"])) * 1e-6
+    t_attn = float(np.median(st_us["sparse_attn"])) * 1e-6
+    t_dom = float(np.median(st_us[dominant])) * 1e-6
+    dom_min = float(np.min(st_us[dominant])) * 1e-6
+    t_event_step = float(np.median([us(e, 0, 4) for e in gev])) * 1e-6
 
     tb = topk_bytes(sh, sp)
     # attention bytes depend on the selection: mean over the query sets
@@ -304,25 +353,29 @@ def main():
     ab, rows_att = (float(np.mean(abs_)), int(np.mean(rows_))) if abs_ else (0.0, 0)
     T = sh.batch * sh.q_per_req
 
-    def stage(bytes_, t):
+    def stage(name, bytes_, t):
         gbs = bytes_ / t / 1e9 if t > 0 else 0.0
-        return {"us": round(t * 1e6, 2), "alg_bytes": int(bytes_), "GB_s": round(gbs, 1),
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        return {"us": round(t * 1e6, 2), "us_min": round(float(np.min(st_us[name])), 2),
+                "alg_bytes": int(bytes_), "GB_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
-    stages = {"indexer_score": stage(sb, t_score), "topk": stage(tb, t_topk),
-              "sparse_attn": stage(ab, t_attn)}
+    stages = {"indexer_score": stage("indexer_score", sb, t_score), "topk": stage("topk", tb, t_topk),
+              "sparse_attn": stage("sparse_attn", ab, t_attn)}
     stages["indexer_score"]["TFLOP_s"] = round(sf / t_score / 1e12, 2) if t_score else 0.0
     stages["sparse_attn"]["rows_attended"] = rows_att
 
     dom_bytes = sb if dominant == "indexer_score" else ab
     achieved = dom_bytes / t_dom / 1e9
+    timing = {"kernel_us": round(t_dom * 1e6, 2), "kernel_us_min": round(dom_min * 1e6, 2),
+              "kernel_launches_timed": nb, "kernel_time": "median of per-launch HIP events"}
     if cfg.indexer_only:
         # a prefill chunk re-reads each request's few MB of keys from L2 for
         # every block of query rows: the contraction, not HBM, bounds it
-        roofline = {"bound": "mfma", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
-                    "achieved": round(sf / t_dom / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(sf / t_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "kernel_launches_timed": len(evs)}
+        roofline = dict({"bound": "mfma", "kernel": dominant}, **timing,
+                        achieved=round(sf / t_dom / 1e12, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(sf / t_dom / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+    else:
+        roofline = dict({"bound": "hbm", "kernel": dominant}, **timing, achieved=round(achieved, 1),
+                        peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4))
     traffic = None
     kf = ("_fp8" if fp8 and dominant == "indexer_score" else "") + ("_paged" if paged else "")
     tfile = os.path.join(PROFILES, f"traffic_{dominant}{kf}_config{args.config}.json")
@@ -331,11 +384,19 @@ def main():
         src = "indexer_score.hip" if dominant == "indexer_score" else "sparse_attn.hip"
         if tj.get("kernel_source_hash") == kernel_source_hash(src, whole=cfg.indexer_only):
             traffic = tj.get("hbm_bytes_per_launch")
+    roofline["traffic"] = traffic
 
-    # CPU baseline: the oracle as it stands, whole step, on the host's cores
+    # CPU baseline: the oracle as it stands, whole step, on the host cores this
+    # job may use.  A one-GPU job's share of the host is 16 cores, whatever
+    # the affinity mask shows; the counts are reported beside it.
     cpu = None
     if not args.no_cpu_baseline:
-        nthreads = max(1, min(16, len(os.sched_getaffinity(0))))
+        affinity = len(os.sched_getaffinity(0))
+        nthreads = max(1, min(CPU_SHARE, affinity))
+        try:
+            nproc = int(subprocess.run(["nproc"], capture_output=True, text=True).stdout.strip())
+        except (OSError, ValueError):
+            nproc = None
         times = []
         if cfg.indexer_only:   # scoring + Top-K of the chunk's first 1024 tokens
             jobs, n_tok, what = oracle.JOB_SCORE | oracle.JOB_TOPK, min(T, 1024), "scoring + Top-K"
@@ -354,7 +415,22 @@ def main():
         cpu = {"value": round(n_tok / tc, 2), "unit": "query-tokens/s", "cores": nthreads,
                "kind": "oracle",
                "sample": f"{what} of {n_tok} of this workload's {T} query tokens, median of "
-                         f"{len(times)} runs ({sum(times):.1f} s in all), {tc:.2f} s each, fp64 oracle"}
+                         f"{len(times)} runs ({sum(times):.1f} s in all), {tc:.2f} s each, fp64 oracle",
+               "nproc": nproc, "affinity_cpus": affinity,
+               "hardware_concurrency": os.sysconf("SC_NPROCESSORS_ONLN"),
+               "cpu_share": CPU_SHARE}
+        # the long-context configuration's whole step on one thread (median of 3)
+        inp3 = inp if args.config == 3 else I.make_inputs(3)
+        t1 = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.run(I.CONFIGS[3].shape, inp3, nthreads=1)
+            t1.append(time.perf_counter() - t0)
+        del inp3
+        T3 = I.CONFIGS[3].shape.batch * I.CONFIGS[3].shape.q_per_req
+        cpu["long_context_1thread"] = {"s": round(float(np.median(t1)), 4),
+                                       "query_tokens_per_s": round(T3 / float(np.median(t1)), 1),
+                                       "sample": f"the full step of all {T3} tokens, median of 3"}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -375,6 +451,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if sh.dtype == 1 else "f32",
         "data": "synthetic (seeded N(0,1) caches and queries, structure per configuration)",
+        "cache": args.cache,
+        "step_time": ("median of per-step HIP events bracketing the calls; 1 GiB scratch written "
+                      "before each step, outside the events" if args.cache == "flushed"
+                      else "wall time of K back-to-back steps / K"),
         "config": {"workload": f"{cfg.name}: B={sh.batch} S={sh.q_per_req} context->"
                                f"{sh.n_cap} compressed rows (ratio {sh.ratio}) K={sh.topk} "
                                f"WIN={sh.win} H={sh.heads} D={sh.head_dim} Dr={sh.rope_dim} "
@@ -386,17 +466,21 @@ def main():
                    "paged_caches": (["indexer keys", "compressed K/V", "window rings"]
                                     if paged else None),
                    "parallelism": "single GPU"},
-        "roofline": dict(roofline, traffic=traffic) if cfg.indexer_only else
-                    {"bound": "hbm", "kernel": dominant, "kernel_us": round(t_dom * 1e6, 2),
-                     "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel_launches_timed": len(evs)},
+        "roofline": roofline,
         "stages": stages,
-        "stages_note": "per-stage HIP events from a separate 40-step pass after the timed region; "
-                       "their packets add gaps, so they sum above ms_per_step",
+        "stages_note": f"median (and minimum) of {nb} per-stage HIP event intervals, "
+                       f"{args.cache} as the timed steps; their extra event packets add gaps, so "
+                       "the stages sum above ms_per_step",
         "event_step_us": round(t_event_step * 1e6, 2),
+        "hot": {"cache": "hot", "ms_per_step": round(hot_ms, 4),
+                "value": round(T / (hot_ms * 1e-3), 1),
+                "step_time": f"wall time of {hot_steps} back-to-back steps / {hot_steps}"},
         "cpu_baseline": cpu,
     }
+    if step_us:
+        line["step_us_min"] = round(float(np.min(step_us)), 2)
+        line["step_us_median"] = round(float(np.median(step_us)), 2)
+        line["flushed_wall_ms_per_step"] = round(wall_flushed * 1000.0 / args.steps, 4)
     print(json.dumps(line), flush=True)
 
 

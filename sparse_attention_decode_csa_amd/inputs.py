@@ -35,7 +35,7 @@ F32 = 0
 BF16 = 1
 
 # tensor ids of the child streams (fixed order; never renumber)
-_T_START, _T_Q, _T_KWIN, _T_VWIN, _T_KCMP, _T_VCMP, _T_QIDX, _T_W, _T_KIDX, _T_STRUCT = range(10)
+_T_START, _T_Q, _T_KWIN, _T_VWIN, _T_KCMP, _T_VCMP, _T_QIDX, _T_W, _T_KIDX, _T_STRUCT, _T_TIE = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,7 +68,7 @@ class Config:
     shape: Shape
     seed: int
     lengths: str          # how start_pos is drawn (documentation + dispatch key)
-    structure: str        # extra structure planted into the indexer keys
+    structure: str        # extra structure planted into the indexer keys ("+"-separated parts)
     supplied_topk: bool   # True: the harness supplies topk_idx (attention only)
     indexer_only: bool = False  # True: a prefill chunk measured for scoring + Top-K
 
@@ -107,7 +107,11 @@ CONFIGS: Dict[int, Config] = {
         shape=_shape(batch=64, q_per_req=2, ratio=4, n_cap=32768, topk=1024, win=256, w_cap=512,
                      heads=16, head_dim=128, rope_dim=64, idx_heads=8, idx_dim=128,
                      out_groups=1, max_len=131072, dtype=BF16),
-        seed=4, lengths="fixed:131072", structure="dup:0.01", supplied_topk=False),
+        # 1% duplicated key rows, and the row that token (0, 0) ranks K-th (row
+        # 13692, found by the oracle on the inputs without the tie:
+        # tests/golden/config4_boundary_tie.py) copied to 2 rows below and 2
+        # above it, so that equal scores straddle the selection boundary
+        seed=4, lengths="fixed:131072", structure="dup:0.01+tie:0:13692:2:2", supplied_topk=False),
     # A prefill chunk: the last 4096 tokens of a 32768-token context, each
     # scoring its own causally visible compressed rows (7168 .. 8192).
     5: Config(
@@ -251,6 +255,55 @@ def visible_rows(p: np.ndarray, ratio: int) -> np.ndarray:
     return (np.asarray(p, dtype=np.int64) + 1) // ratio
 
 
+def _plant(part: str, g: np.random.Generator, g_tie: np.random.Generator, k_idx: np.ndarray,
+           q_idx: np.ndarray, w: np.ndarray, last_vis: np.ndarray, sh: Shape) -> None:
+    """Apply one structure part to the float32 indexer keys k_idx [B, N_cap, Di] in place."""
+    B, Di, dt = sh.batch, sh.idx_dim, sh.dtype
+    kind, _, arg = part.partition(":")
+    if kind == "planted":
+        # Rows aligned with the request's weighted indexer query score far above
+        # the N(0,1) rows, so they must win Top-K wherever they sit.
+        n_plant = int(arg)
+        qi = as_float(_store(q_idx, dt), dt).astype(np.float64)
+        for b in range(B):
+            nv = int(last_vis[b])
+            if nv <= sh.topk:
+                continue
+            m = min(n_plant, nv)
+            pos = g.choice(nv, size=m, replace=False)
+            u = np.einsum("h,hc->c", w[b, 0].astype(np.float64), qi[b, 0])
+            u /= np.linalg.norm(u)
+            alpha = g.uniform(1.0, 2.0, size=m)
+            k_idx[b, pos] = (alpha[:, None] * np.sqrt(Di) * u[None, :]).astype(np.float32)
+    elif kind == "dup":
+        # A fraction of rows copy another row's indexer key, so exact score ties
+        # occur on both sides of every comparison.
+        frac = float(arg)
+        for b in range(B):
+            nv = int(last_vis[b])
+            nd = int(round(frac * nv))
+            if nd == 0 or nv < 2:
+                continue
+            dst = g.choice(nv, size=nd, replace=False)
+            src = g.integers(0, nv, size=nd)
+            k_idx[b, dst] = k_idx[b, src]
+    elif kind == "tie":
+        # tie:b:row:below:above -- key row `row` of request b is copied to
+        # `below` seeded random rows under it and `above` rows over it (among
+        # the rows its last token sees), so equal scores sit on both sides of
+        # that row's index.  Which row to copy is chosen by the caller: the
+        # wide Top-K configuration names the row its first token ranks K-th,
+        # so the tie straddles the selection boundary and the index decides.
+        b, row, below, above = (int(x) for x in arg.split(":"))
+        nv = int(last_vis[b])
+        assert 0 <= row < nv and below <= row and above <= nv - 1 - row
+        lo = g_tie.choice(row, size=below, replace=False) if below else np.zeros(0, np.int64)
+        hi = row + 1 + g_tie.choice(nv - 1 - row, size=above, replace=False) if above else np.zeros(0, np.int64)
+        k_idx[b, np.concatenate([lo, hi])] = k_idx[b, row]
+    elif kind != "none":
+        raise ValueError(part)
+
+
 def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
                 shape: Optional[Shape] = None, start_pos: Optional[np.ndarray] = None,
                 structure: Optional[str] = None, key_format: str = "bf16") -> Dict[str, np.ndarray]:
@@ -293,36 +346,8 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
 
     g = _rng(seed, _T_STRUCT)
     last_vis = np.minimum(visible_rows(sp + S - 1, sh.ratio), Nc)   # rows visible to the last token
-    kind, _, arg = structure.partition(":")
-    if kind == "planted":
-        # Rows aligned with the request's weighted indexer query score far above
-        # the N(0,1) rows, so they must win Top-K wherever they sit.
-        n_plant = int(arg)
-        qi = as_float(_store(q_idx, dt), dt).astype(np.float64)
-        for b in range(B):
-            nv = int(last_vis[b])
-            if nv <= sh.topk:
-                continue
-            m = min(n_plant, nv)
-            pos = g.choice(nv, size=m, replace=False)
-            u = np.einsum("h,hc->c", w[b, 0].astype(np.float64), qi[b, 0])
-            u /= np.linalg.norm(u)
-            alpha = g.uniform(1.0, 2.0, size=m)
-            k_idx[b, pos] = (alpha[:, None] * np.sqrt(Di) * u[None, :]).astype(np.float32)
-    elif kind == "dup":
-        # A fraction of rows copy another row's indexer key, so exact score ties
-        # occur on both sides of every comparison.
-        frac = float(arg)
-        for b in range(B):
-            nv = int(last_vis[b])
-            nd = int(round(frac * nv))
-            if nd == 0 or nv < 2:
-                continue
-            dst = g.choice(nv, size=nd, replace=False)
-            src = g.integers(0, nv, size=nd)
-            k_idx[b, dst] = k_idx[b, src]
-    elif kind != "none":
-        raise ValueError(structure)
+    for part in structure.split("+"):
+        _plant(part, g, _rng(seed, _T_TIE), k_idx, q_idx, w, last_vis, sh)
 
     if poison:
         for b in range(B):

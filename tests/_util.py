@@ -5,9 +5,24 @@ mathematics); GPU results are only ever compared, never fed to the oracle.
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 from sparse_attention_decode_csa_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+RECORD = os.path.join(ROOT, "gpurun_out", "parity_record.jsonl")
+
+
+def record(test: str, **data):
+    """Append one JSON line (test name + figures such as boundary-exemption
+    counts) to gpurun_out/parity_record.jsonl, next to the run's logs, so the
+    figures of a passing run stay visible."""
+    os.makedirs(os.path.dirname(RECORD), exist_ok=True)
+    with open(RECORD, "a") as f:
+        f.write(json.dumps(dict(test=test, **data), default=int) + "\n")
 
 # max-abs tolerance for bf16 outputs with fp32 accumulation
 BF16_ATOL = 2e-2
@@ -100,31 +115,65 @@ def compare_outputs(shape, got: np.ndarray, ref: np.ndarray, tokens=None):
     return worst
 
 
-def topk_exemptions(shape, gpu_idx, ref_idx, ref_scores, bound, start_pos):
+def topk_exemptions(shape, gpu_idx, ref_idx, ref_scores, bound, start_pos, tokens=None):
     """Compare end-to-end Top-K lists; return the (b, s) tokens that differ.
 
     A difference is allowed only at the selection boundary: every row in the
     symmetric difference must have an oracle score within the score error
-    bound (on both sides) of the oracle's K-th largest score.
+    bound (on both sides) of the oracle's K-th largest score.  `tokens`
+    restricts the comparison to those (b, s) pairs.
     """
     exempt = []
     K = shape.topk
-    for b in range(shape.batch):
-        for s in range(shape.q_per_req):
-            gi, ri = gpu_idx[b, s], ref_idx[b, s]
-            if np.array_equal(gi, ri):
-                continue
-            p = int(start_pos[b]) + s
-            n = min((p + 1) // shape.ratio, shape.n_cap)
-            assert n > K, f"bypass token {(b, s)} differs"
-            assert len(set(gi.tolist())) == K and (gi >= 0).all() and (gi < n).all()
-            assert np.all(np.diff(gi) > 0), "GPU list not ascending"
-            sc = ref_scores[b, s, :n].astype(np.float64)
-            kth = np.sort(sc)[::-1][K - 1]
-            bd = bound[(b, s)]
-            diff = set(gi.tolist()) ^ set(ri.tolist())
-            for j in diff:
-                assert abs(sc[j] - kth) <= bd[j] + bd.max(), (
-                    f"token {(b, s)} row {j}: score {sc[j]} far from boundary {kth}")
-            exempt.append((b, s, len(diff)))
+    pairs = tokens if tokens is not None else [(b, s) for b in range(shape.batch)
+                                               for s in range(shape.q_per_req)]
+    for (b, s) in pairs:
+        gi, ri = gpu_idx[b, s], ref_idx[b, s]
+        if np.array_equal(gi, ri):
+            continue
+        p = int(start_pos[b]) + s
+        n = min((p + 1) // shape.ratio, shape.n_cap)
+        assert n > K, f"bypass token {(b, s)} differs"
+        assert len(set(gi.tolist())) == K and (gi >= 0).all() and (gi < n).all()
+        assert np.all(np.diff(gi) > 0), "GPU list not ascending"
+        sc = ref_scores[b, s, :n].astype(np.float64)
+        kth = np.sort(sc)[::-1][K - 1]
+        bd = bound[(b, s)]
+        diff = set(gi.tolist()) ^ set(ri.tolist())
+        for j in diff:
+            assert abs(sc[j] - kth) <= bd[j] + bd.max(), (
+                f"token {(b, s)} row {j}: score {sc[j]} far from boundary {kth}")
+        exempt.append((b, s, len(diff)))
     return exempt
+
+
+def selection_mask(scores, n_vis, K):
+    """Boolean [T, N] mask of the exact selection of each score row: the K
+    largest of its first n_vis entries, lower index first among equal values
+    (rows with n_vis <= K keep all of them).  numpy's partition gives each
+    row's K-th largest value; the rest is counting.  A check that holds at any
+    size: it compares a list with the exact selection of the scores it was
+    chosen from."""
+    T, N = scores.shape
+    n_vis = np.asarray(n_vis)
+    col = np.arange(N)[None, :]
+    valid = col < n_vis[:, None]
+    sc = np.where(valid, scores, -np.inf).astype(np.float32)
+    kth = -np.partition(-sc, K - 1, axis=1)[:, K - 1]                 # K-th largest per row
+    gt = valid & (sc > kth[:, None])
+    eq = valid & (sc == kth[:, None])
+    need = K - gt.sum(axis=1)
+    take_eq = eq & (np.cumsum(eq, axis=1) <= need[:, None])
+    sel = gt | take_eq
+    fits = n_vis <= K
+    sel[fits] = valid[fits]
+    return sel
+
+
+def list_mask(idx, N):
+    """Boolean [T, N] mask of the entries >= 0 of Top-K lists idx [T, K]."""
+    T, K = idx.shape
+    m = np.zeros((T, N), dtype=bool)
+    r, c = np.nonzero(idx >= 0)
+    m[r, idx[r, c]] = True
+    return m

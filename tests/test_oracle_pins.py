@@ -147,6 +147,51 @@ def test_signed_zero_ties():
     assert oracle.select_row(row, 3).tolist() == [0, 1, 5]
 
 
+@pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero"])
+def test_selection_mask_vs_lexsort(kind):
+    # The GPU tests check every prefill-chunk list against this mask of the
+    # exact selection; pin it to a library sort first.
+    from tests import _util as U
+    n_cap, K = 700, 64
+    sc = I.random_scores(5, 3, 8, n_cap, kind).reshape(24, n_cap)
+    nv = np.array([1, 63, 64, 65, 700] + list(range(100, 700, 32)))[:24]
+    want = np.zeros_like(sc, dtype=bool)
+    for t in range(24):
+        sel = lexsort_topk(sc[t, :nv[t]], K)
+        want[t, sel[sel >= 0]] = True
+    assert np.array_equal(U.selection_mask(sc, nv, K), want)
+    idx = np.full((24, K), -1, np.int32)
+    for t in range(24):
+        idx[t] = lexsort_topk(sc[t, :nv[t]], K)
+    assert np.array_equal(U.list_mask(idx, n_cap), want)
+
+
+def test_wide_topk_boundary_tie():
+    # The wide Top-K configuration copies the key row that token (0, 0) ranks
+    # K-th (found by the oracle on the inputs without the tie) to two rows
+    # below and two above it.  Re-derive that row, then check on the planted
+    # inputs that five rows share the boundary score, that the oracle keeps
+    # only some of them, the lowest-indexed ones, and that its list equals a
+    # library sort of its own scores.
+    from tests.golden.config4_boundary_tie import BASE_STRUCTURE, rank_k_row
+    cfg = I.CONFIGS[4]
+    sh = cfg.shape
+    parts = dict(p.split(":", 1) for p in cfg.structure.split("+"))
+    b, row, below, above = (int(x) for x in parts["tie"].split(":"))
+    assert (b, below, above) == (0, 2, 2)
+    assert rank_k_row(I.make_inputs(cfg, structure=BASE_STRUCTURE), sh) == row
+    inp = I.make_inputs(cfg)
+    ref = oracle.run(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK, tokens=(0, 1), nthreads=8)
+    n = oracle.n_vis(int(inp["start_pos"][0]), sh.ratio)
+    sc = ref["scores"][0, 0, :n]
+    tied = np.flatnonzero(sc == sc[row])
+    assert tied.size >= 5 and (tied < row).sum() >= 2 and (tied > row).sum() >= 2
+    kept = np.intersect1d(tied, ref["topk_idx"][0, 0])
+    assert 0 < kept.size < tied.size
+    assert kept.tolist() == tied[:kept.size].tolist()      # lower indices win the tie
+    assert ref["topk_idx"][0, 0].tolist() == lexsort_topk(sc, sh.topk).tolist()
+
+
 # --------------------------------------------------------------------------
 # indexer scores
 # --------------------------------------------------------------------------
