@@ -253,6 +253,33 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* shape, const void* q, con
                                     int32_t rope_rows, float softmax_scale, void* out, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/* csa_sparse_attn_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, checks and result as csa_sparse_attn_decode,
+ * without the workspace: the split partials live in a static device array of
+ * the library (csa_sparse_attn_noalloc_max_workspace_bytes() bytes, 32 MiB;
+ * each GPU the library runs on holds its own copy until the process ends).
+ * The call allocates nothing and frees nothing.
+ *   - A shape whose workspace (csa_sparse_attn_workspace_bytes) exceeds that
+ *     size is refused with CSA_ERR_WORKSPACE before anything is enqueued.
+ *   - The first call on a GPU looks up that GPU's copy of the array (the
+ *     GPU that runs `stream`); CSA_ERR_LAUNCH if the lookup fails.
+ *   - Every call on one GPU shares that GPU's array and leaves the last
+ *     call's partials in it: calls that overlap in time on one GPU (other
+ *     streams, other threads) race and give undefined results.  Calls
+ *     ordered on one stream are safe.
+ */
+csa_status_t csa_sparse_attn_decode_noalloc(const csa_shape_t* shape, const void* q,
+                                            const void* k_win, const void* v_win,
+                                            const void* k_cmp, const void* v_cmp,
+                                            const int32_t* topk_idx, const int32_t* start_pos,
+                                            const float* rope_cos, const float* rope_sin,
+                                            int32_t rope_rows, float softmax_scale, void* out,
+                                            void* stream);
+
+/* Size of the static array behind csa_sparse_attn_decode_noalloc (bytes). */
+size_t csa_sparse_attn_noalloc_max_workspace_bytes(void);
+
 /* Window-cache writeback of the step's new tokens, by slot mapping.
  *
  * Copies the K and V rows of every new token t = b*S + s to row

@@ -7,8 +7,8 @@ library, a CPU tensor or a non-contiguous tensor is an error.
 
 Names match the C ABI: indexer_score, indexer_score_fp8,
 indexer_score_paged, topk, sparse_attn_decode, sparse_attn_decode_paged,
-swa_writeback, plus the workspace queries and step(), which issues the three
-calls in order on one stream.
+sparse_attn_decode_noalloc, swa_writeback, plus the workspace queries and
+step(), which issues the three calls in order on one stream.
 """
 from __future__ import annotations
 
@@ -36,8 +36,9 @@ ABI_VERSION = 2
 
 EXPORTS = ("csa_indexer_score", "csa_indexer_score_fp8", "csa_indexer_score_paged",
            "csa_topk_workspace_bytes", "csa_topk", "csa_sparse_attn_workspace_bytes",
-           "csa_sparse_attn_decode", "csa_sparse_attn_decode_paged", "csa_swa_writeback",
-           "csa_status_string", "csa_abi_version")
+           "csa_sparse_attn_decode", "csa_sparse_attn_decode_paged",
+           "csa_sparse_attn_decode_noalloc", "csa_sparse_attn_noalloc_max_workspace_bytes",
+           "csa_swa_writeback", "csa_status_string", "csa_abi_version")
 
 
 class CShape(ctypes.Structure):
@@ -93,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.csa_sparse_attn_decode.restype = i32
         L.csa_sparse_attn_decode.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp,
                                              vp, sz, vp]
+        L.csa_sparse_attn_decode_noalloc.restype = i32
+        L.csa_sparse_attn_decode_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                     f32, vp, vp]
+        L.csa_sparse_attn_noalloc_max_workspace_bytes.restype = sz
+        L.csa_sparse_attn_noalloc_max_workspace_bytes.argtypes = []
         L.csa_swa_writeback.restype = i32
         L.csa_swa_writeback.argtypes = [sp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         L.csa_status_string.restype = ctypes.c_char_p
@@ -257,6 +263,22 @@ def sparse_attn_decode(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos
         _dev(v_cmp, "v_cmp", n["cmp"], dt), c["topk_idx"], c["start_pos"], c["rope_cos"],
         c["rope_sin"], c["rope_rows"], float(softmax_scale), c["out"], _dev(ws, "ws"), nbytes,
         _stream(stream)))
+
+
+def sparse_attn_decode_noalloc(shape, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos,
+                               rope_cos, rope_sin, softmax_scale, out, stream=None) -> None:
+    """sparse_attn_decode without a workspace: the split partials live in the
+    library's static device array (see csa_sparse_attn_noalloc_max_workspace_bytes)."""
+    cs, n, dt = CShape.of(shape), _sizes(shape), torch_dtype(shape)
+    c = _attn_common(shape, q, k_win, v_win, topk_idx, start_pos, rope_cos, rope_sin, out)
+    _check("csa_sparse_attn_decode_noalloc", lib().csa_sparse_attn_decode_noalloc(
+        ctypes.byref(cs), c["q"], c["k_win"], c["v_win"], _dev(k_cmp, "k_cmp", n["cmp"], dt),
+        _dev(v_cmp, "v_cmp", n["cmp"], dt), c["topk_idx"], c["start_pos"], c["rope_cos"],
+        c["rope_sin"], c["rope_rows"], float(softmax_scale), c["out"], _stream(stream)))
+
+
+def sparse_attn_noalloc_max_workspace_bytes() -> int:
+    return int(lib().csa_sparse_attn_noalloc_max_workspace_bytes())
 
 
 def sparse_attn_decode_paged(shape, q, k_win, v_win, k_pool, v_pool, block_table, topk_idx,

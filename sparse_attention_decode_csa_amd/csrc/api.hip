@@ -4,6 +4,7 @@
 // GPU, so they behave the same on a machine without one.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/csa.h"
 #include "kernels.h"
@@ -54,6 +55,41 @@ csa_status_t check_pages(const csa_shape_t* sh, const csa_pages_t* pg, int64_t r
   if ((reinterpret_cast<uintptr_t>(pg->block_table) & 15u) != 0) return CSA_ERR_ALIGNMENT;
   *shift = __builtin_ctz((unsigned)bs);
   return CSA_OK;
+}
+
+// Split partials of csa_sparse_attn_decode_noalloc: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address of each GPU's copy is looked up once with
+// hipGetSymbolAddress, with that GPU current, and kept per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU that runs `stream` (NULL on failure).
+void* scratch_address(hipStream_t stream) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -134,7 +170,8 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
                                 const float* rope_cos, const float* rope_sin, int32_t rope_rows,
                                 float softmax_scale, void* out, void* ws, size_t ws_bytes,
                                 void* stream, const csa_pages_t* pages, int block_shift,
-                                const csa_pages_t* win_pages, int win_shift) {
+                                const csa_pages_t* win_pages, int win_shift,
+                                bool use_scratch = false) {
   bool empty = false;
   csa_status_t st = check_common(sh, &empty);
   if (st != CSA_OK || empty) return st;
@@ -155,11 +192,16 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
   }
   const csa::AttnPlan pl =
       csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk, sh->dtype);
-  if (!ws || ws_bytes < pl.ws_bytes) return CSA_ERR_WORKSPACE;
+  if (use_scratch ? pl.ws_bytes > kScratchBytes : (!ws || ws_bytes < pl.ws_bytes)) return CSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_win) || !aligned16(v_win) || !aligned16(k_cmp) ||
       !aligned16(v_cmp) || !aligned16(topk_idx) || !aligned16(start_pos) || !aligned16(out) ||
-      !aligned16(ws) || (rope_cos && !aligned16(rope_cos)) || (rope_sin && !aligned16(rope_sin)))
+      (!use_scratch && !aligned16(ws)) || (rope_cos && !aligned16(rope_cos)) ||
+      (rope_sin && !aligned16(rope_sin)))
     return CSA_ERR_ALIGNMENT;
+  if (use_scratch) {  // every check has passed: only now touch the device
+    ws = scratch_address(static_cast<hipStream_t>(stream));
+    if (!ws) return CSA_ERR_LAUNCH;
+  }
   char* wsb = static_cast<char*>(ws);
   csa::AttnArgs a{};
   a.q = q;
@@ -215,6 +257,20 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* sh, const void* q, const 
   return attn_decode(sh, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos, rope_cos, rope_sin,
                      rope_rows, softmax_scale, out, ws, ws_bytes, stream, nullptr, 0, nullptr, 0);
 }
+
+csa_status_t csa_sparse_attn_decode_noalloc(const csa_shape_t* sh, const void* q,
+                                            const void* k_win, const void* v_win,
+                                            const void* k_cmp, const void* v_cmp,
+                                            const int32_t* topk_idx, const int32_t* start_pos,
+                                            const float* rope_cos, const float* rope_sin,
+                                            int32_t rope_rows, float softmax_scale, void* out,
+                                            void* stream) {
+  return attn_decode(sh, q, k_win, v_win, k_cmp, v_cmp, topk_idx, start_pos, rope_cos, rope_sin,
+                     rope_rows, softmax_scale, out, nullptr, 0, stream, nullptr, 0, nullptr, 0,
+                     /*use_scratch=*/true);
+}
+
+size_t csa_sparse_attn_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
 
 csa_status_t csa_swa_writeback(const csa_shape_t* sh, const void* k_new, const void* v_new,
                                const int32_t* slot_mapping, void* k_cache, void* v_cache,

@@ -183,6 +183,36 @@ def test_attn_capacity_workspace_alignment():
     assert call_attn(shape(rope_dim=0), [FAKE] * 7 + [None, None, FAKE], ws_bytes=0) == 6
 
 
+def call_attn_noalloc(sh, ptrs=None, rope_rows=1 << 20, scale=0.1):
+    p = ptrs or [FAKE] * 10
+    return C.lib().csa_sparse_attn_decode_noalloc(ctypes.byref(C.CShape.of(sh)), *p[:9], rope_rows,
+                                                  scale, p[9], None)
+
+
+def test_attn_noalloc_refusals():
+    # Every check runs before the static array is looked up on the device, so
+    # these refusals need no GPU.
+    cap = C.sparse_attn_noalloc_max_workspace_bytes()
+    assert cap == 32 << 20
+    sh = shape()
+    assert C.sparse_attn_workspace_bytes(sh) <= cap
+    assert call_attn_noalloc(sh, rope_rows=1000) == 4
+    assert call_attn_noalloc(shape(w_cap=127)) == 4
+    assert call_attn_noalloc(shape(heads=17)) == 8
+    assert call_attn_noalloc(sh, scale=float("inf")) == 2
+    p = [FAKE] * 10
+    p[9] = MISALIGNED
+    assert call_attn_noalloc(sh, p) == 5
+    p = [FAKE] * 10
+    p[4] = None
+    assert call_attn_noalloc(sh, p) == 1
+    # a shape whose split partials exceed the static array
+    big = shape(batch=4096, topk=4096, win=4096, w_cap=4096, max_len=1024)
+    assert C.sparse_attn_workspace_bytes(big) > cap
+    assert call_attn_noalloc(big) == 6
+    assert call_attn_noalloc(shape(batch=0)) == 0
+
+
 def test_empty_problem_is_ok_without_gpu_work():
     sh = shape(batch=0)
     assert call_score(sh) == 0 and call_topk(sh) == 0 and call_attn(sh) == 0
