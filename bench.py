@@ -11,9 +11,10 @@ Timing follows the pages' protocol of timed rounds after warm-ups ("Perf:
 skip redundant CSA scoring and fuse gather unpack" and "Perf: fuse HCA merge,
 inverse RoPE, and packing", descriptions): W untimed steps, then K timed
 steps.  With --cache flushed (the default) a 1 GiB scratch buffer is written
-before every timed step, outside the events that bracket the step's calls, so
-that neither the L2s nor the 256 MB Infinity Cache hold anything the step
-reads; the step time is the median (and minimum) of those event intervals.
+and a 512 MB one read before every timed step, outside the events that
+bracket the step's calls, so that neither the L2s nor the 256 MB Infinity
+Cache hold anything the step reads (nor dirty lines of the flush); the step
+time is the median (and minimum) of those event intervals.
 A back-to-back pass of exactly K steps between two synchronisations is also
 timed and reported under "hot".
 
@@ -66,9 +67,9 @@ def parse():
                     help="query sets cycled over the steps (queries rolled along the batch), so "
                          "consecutive steps select different compressed rows")
     ap.add_argument("--cache", choices=("flushed", "hot"), default="flushed",
-                    help="flushed: 1 GiB scratch write before each timed step (outside its "
-                         "events), step time = median event interval; hot: back-to-back steps, "
-                         "step time = wall time of the K steps / K")
+                    help="flushed: 1 GiB scratch write and 512 MB clean read before each timed "
+                         "step (outside its events), step time = median event interval; hot: "
+                         "back-to-back steps, step time = wall time of the K steps / K")
     ap.add_argument("--stage-launches", type=int, default=64,
                     help="least number of flushed steps timed stage by stage (per-stage events)")
     ap.add_argument("--flush-mib", type=int, default=1024)
@@ -275,13 +276,19 @@ def main():
     dominant = ("indexer_score" if cfg.indexer_only or sb >= attn_bytes(sh, sp, ti0)[0]
                 else "sparse_attn")
 
-    # the 1 GiB scratch written before every flushed step: larger than the
-    # 256 MB Infinity Cache and the L2s together, so nothing the step reads is
-    # still cached when it starts (the write is outside the step's events)
+    # Before every flushed step (outside its events): 1 GiB of scratch written,
+    # more than the 256 MB Infinity Cache and the L2s together, so nothing the
+    # step reads is still cached; then 512 MB of another buffer read, so that
+    # the caches hold clean lines rather than the write's dirty ones, whose
+    # write-back would otherwise run inside the measured kernels (measured: a
+    # sequential 84 MB read takes 35 us after the write alone, 17.6 us after
+    # write + read, 16.3 us with hot caches).
     scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device="cuda")
+    clean = torch.ones((args.flush_mib << 20) // 8, dtype=torch.float32, device="cuda")
 
     def flush(k):
         scratch.fill_(k & 0x7F)
+        clean.sum()
 
     def ev_set():
         return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -452,8 +459,9 @@ def main():
         "dtype": "bf16" if sh.dtype == 1 else "f32",
         "data": "synthetic (seeded N(0,1) caches and queries, structure per configuration)",
         "cache": args.cache,
-        "step_time": ("median of per-step HIP events bracketing the calls; 1 GiB scratch written "
-                      "before each step, outside the events" if args.cache == "flushed"
+        "step_time": ("median of per-step HIP events bracketing the calls; before each step, "
+                      "outside the events, 1 GiB of scratch written and 512 MB of another "
+                      "buffer read" if args.cache == "flushed"
                       else "wall time of K back-to-back steps / K"),
         "config": {"workload": f"{cfg.name}: B={sh.batch} S={sh.q_per_req} context->"
                                f"{sh.n_cap} compressed rows (ratio {sh.ratio}) K={sh.topk} "

@@ -25,8 +25,10 @@
  * --------------------------------
  * - Every tensor pointer is a DEVICE pointer to a contiguous, row-major,
  *   16-byte aligned buffer owned by the caller.  The shape pointer is HOST
- *   memory.  The library allocates nothing, keeps no pointer after a call
- *   returns and holds no state: calls are reentrant.
+ *   memory.  The library allocates nothing and keeps no pointer after a call
+ *   returns; its only state is the static device array behind
+ *   csa_sparse_attn_decode_noalloc.  Calls are reentrant (calls that share a
+ *   workspace, or that array, must not overlap in time).
  * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *   Calls only enqueue work; ordering is the stream order.
  * - Element type of q, k_win, v_win, k_cmp, v_cmp, q_idx, k_idx and out is
