@@ -187,7 +187,11 @@ csa_status_t csa_indexer_score_paged(const csa_shape_t* shape, const void* q_idx
                                      const csa_pages_t* pages, const int32_t* start_pos,
                                      float* scores, void* stream);
 
-/* Workspace bytes csa_topk needs for this shape (0 means none). */
+/* Workspace bytes csa_topk needs for this shape (0 means none).  Launches of
+ * fewer than 2048 query tokens over rows of at least 4096 visible entries
+ * (K <= 1024, at most a quarter of the row) split each row over several
+ * workgroups and merge their candidates; their candidates and counts live in
+ * the workspace (contents need no initialisation). */
 size_t csa_topk_workspace_bytes(const csa_shape_t* shape);
 
 /* Causal Top-K selection, with the fits-in-Top-K bypass.
@@ -205,7 +209,8 @@ size_t csa_topk_workspace_bytes(const csa_shape_t* shape);
  *
  *   scores   [B][S][n_cap] float32 (read only at j < n_vis of non-fitting tokens)
  *   topk_idx [B][S][K]     int32 output
- * ws may be NULL when csa_topk_workspace_bytes() returns 0.
+ * ws: at least csa_topk_workspace_bytes() bytes, 16-byte aligned (may be NULL
+ * when that is 0; CSA_ERR_WORKSPACE when missing or smaller).
  * Requires n_cap >= floor(max_len / R).
  */
 csa_status_t csa_topk(const csa_shape_t* shape, const float* scores, const int32_t* start_pos,

@@ -344,18 +344,23 @@ def to_device(inp: dict, shape, device="cuda") -> dict:
     return out
 
 
+def alloc_topk_workspace(shape, device="cuda") -> Optional[torch.Tensor]:
+    """The workspace csa_topk needs for this shape (None when it needs none)."""
+    n = topk_workspace_bytes(shape)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def alloc_outputs(shape, device="cuda", scores_fill=float("nan")) -> dict:
     """Output and workspace buffers of one step."""
     B, S, Nc, K = shape.batch, shape.q_per_req, shape.n_cap, shape.topk
     G, H, D = shape.out_groups, shape.heads, shape.head_dim
     dt = torch_dtype(shape)
-    tw = topk_workspace_bytes(shape)
     aw = sparse_attn_workspace_bytes(shape)
     return dict(
         scores=torch.full((B, S, Nc), scores_fill, dtype=torch.float32, device=device),
         topk_idx=torch.full((B, S, K), -7, dtype=torch.int32, device=device),
         out=torch.empty((G, B * S, (H // G) * D), dtype=dt, device=device),
-        topk_ws=torch.empty(max(tw, 1), dtype=torch.uint8, device=device) if tw else None,
+        topk_ws=alloc_topk_workspace(shape, device),
         attn_ws=torch.empty(max(aw, 16), dtype=torch.uint8, device=device),
     )
 

@@ -138,22 +138,33 @@ csa_status_t csa_indexer_score_fp8(const csa_shape_t* sh, const void* q_idx, con
 }
 
 size_t csa_topk_workspace_bytes(const csa_shape_t* sh) {
-  (void)sh;
-  return 0;  // the selection keeps its state in LDS / registers
+  bool empty = false;
+  if (check_common(sh, &empty) != CSA_OK || empty || check_selection(sh) != CSA_OK) return 0;
+  return csa::topk_plan(sh->batch, sh->q_per_req, sh->n_cap, sh->topk, sh->ratio, sh->max_len).ws_bytes;
 }
 
 csa_status_t csa_topk(const csa_shape_t* sh, const float* scores, const int32_t* start_pos,
                       int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   bool empty = false;
   csa_status_t st = check_common(sh, &empty);
   if (st != CSA_OK || empty) return st;
   if (!scores || !start_pos || !topk_idx) return CSA_ERR_NULL_PTR;
   if ((st = check_selection(sh)) != CSA_OK) return st;
-  if (!aligned16(scores) || !aligned16(start_pos) || !aligned16(topk_idx)) return CSA_ERR_ALIGNMENT;
+  const csa::TopkPlan pl =
+      csa::topk_plan(sh->batch, sh->q_per_req, sh->n_cap, sh->topk, sh->ratio, sh->max_len);
+  if (pl.ws_bytes && (!ws || ws_bytes < pl.ws_bytes)) return CSA_ERR_WORKSPACE;
+  if (!aligned16(scores) || !aligned16(start_pos) || !aligned16(topk_idx) || (pl.ws_bytes && !aligned16(ws)))
+    return CSA_ERR_ALIGNMENT;
   csa::TopkArgs a{scores, start_pos, topk_idx, sh->batch, sh->q_per_req, sh->n_cap, sh->topk,
-                  sh->ratio, sh->max_len};
+                  sh->ratio, sh->max_len, nullptr, nullptr, 0, 0, 0};
+  if (pl.two_pass) {
+    char* w = static_cast<char*>(ws);
+    a.cand = reinterpret_cast<uint2*>(w);
+    a.cand_count = reinterpret_cast<int32_t*>(w + pl.cand_bytes);
+    a.chunk_keys = pl.chunk_keys;
+    a.n_chunks = pl.n_chunks;
+    a.chunk_cap = pl.chunk_cap;
+  }
   (void)hipGetLastError();
   return to_status(csa::launch_topk(a, static_cast<hipStream_t>(stream)));
 }

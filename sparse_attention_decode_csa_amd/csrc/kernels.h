@@ -31,7 +31,24 @@ struct TopkArgs {
   const int32_t* start_pos; // [B]
   int32_t* topk_idx;        // [B][S][K]
   int batch, q_per_req, n_cap, topk, ratio, max_len;
+  // two-pass selection (workspace): candidates of chunk c of token t at
+  // cand[(t * n_chunks + c) * chunk_cap ..], their count at
+  // cand_count[t * n_chunks + c] (-1: more than chunk_cap)
+  uint2* cand;
+  int32_t* cand_count;
+  int chunk_keys, n_chunks, chunk_cap;
 };
+
+// Plan of the Top-K launch; a function of the shape only, so the workspace
+// query and the launch always agree.
+struct TopkPlan {
+  bool two_pass;        // rows split over several workgroups, then merged
+  int chunk_keys;       // keys per chunk workgroup (256 threads x keys per thread)
+  int n_chunks, chunk_cap;
+  size_t cand_bytes, count_bytes, ws_bytes;
+};
+
+TopkPlan topk_plan(int batch, int q_per_req, int n_cap, int topk, int ratio, int max_len);
 
 struct AttnArgs {
   const void* q;            // [B][S][H][D]

@@ -25,14 +25,22 @@
 //   3. Emit in ascending index order: each thread counts its keys above and
 //      equal to T, one block scan turns the counts into output offsets and
 //      tie ranks, and each thread writes its slice.
-//   Longer rows (more than 32768 candidates) use the same selection with the
-//   keys re-read from global memory in every pass.
+//   Longer rows (more than 32768 candidates) are split over several
+//   workgroups in a decode-sized launch (two passes: per-chunk candidates
+//   above a sampled threshold, then an exact merge, below), and otherwise use
+//   the same selection with the keys re-read from global memory in every
+//   pass.
 // The selection never depends on a floating-point operation, so it is exact
 // and identical from run to run.  The pages' own design is a blocked sort with
 // merge stages that quadruple the block length and must reach 1024 past width
 // 256 ("Fix: port the DeepSeek-V4 MoE, hc_pre and prefill fixes to DSpark",
 // description); with ascending-index output no sorted order is needed at all,
 // so selection replaces the sort and has no width-dependent stage to miss.
+// (A bitonic sort of the sampled candidates in registers and LDS, 2048 wide,
+// in place of their radix select, was measured slower: decode Top-K 30.1
+// against 18.8 us on 128 rows of 32768, 24.6 against 13.9 us on 16 rows of
+// 8-16k, its 66 dependent exchange stages each a cross-lane or LDS round
+// trip.)
 #include "device_common.h"
 #include "kernels.h"
 
@@ -40,6 +48,10 @@ namespace csa {
 namespace {
 
 constexpr int kTopkThreads = 1024;
+// launches of at least this many tokens (prefill chunks) select in 4-wave
+// blocks, several per CU; fewer tokens (decode) take 16-wave blocks, or the
+// two-pass selection for rows past 32768 keys
+#define CSA_TOPK_SMALL_BLOCK_TOKENS_DEFAULT 2048
 constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kHistWords = kTopkWaves * 256;
 constexpr int kMiscWords = 64;
@@ -52,28 +64,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Rows longer than the register-resident kernel holds: same selection, keys
-// re-read from global memory (L2) in every pass.
-__global__ __launch_bounds__(kTopkThreads) void topk_global_kernel(TopkArgs a) {
-  __shared__ uint32_t smem[kHistWords + 256 + kMiscWords];
+constexpr int kGlobalSmemWords = kHistWords + 256 + kMiscWords;
+
+// Exact selection of the K largest of row[0 .. n) (n > K) by one workgroup of
+// kTopkThreads, with the keys re-read from global memory (L2) in every pass,
+// written to out[0 .. K) in ascending index order.  smem: kGlobalSmemWords.
+__device__ void select_row_global(const float* row, int n, int K, int32_t* out, uint32_t* smem) {
   uint32_t* hist = smem;                      // [16 waves][256 bins]
   uint32_t* cnt = smem + kHistWords;          // [256]
   int* misc = reinterpret_cast<int*>(cnt + 256);
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok = blockIdx.x;
-  const int S = a.q_per_req, b = tok / S, s = tok % S;
-  const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
-  const int n = min(n_visible(p, a.ratio), a.n_cap);
-  const int K = a.topk;
-  int32_t* out = a.topk_idx + (size_t)tok * K;
 
-  if (n <= K) {  // fits: every visible row, no scoring needed
-    for (int i = tid; i < K; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
-
-  const float* row = a.scores + (size_t)tok * a.n_cap;
   auto key_at = [&](int i) -> uint32_t { return order_key(row[i]); };
 
   // ---- exact K-th largest key by MSB-first radix select
@@ -167,6 +168,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_global_kernel(TopkArgs a) {
     out_pos += __popcll(msel);
     eq_before += __popcll(meq);
   }
+}
+
+// Rows longer than the register-resident kernel holds: the same selection,
+// keys re-read from global memory (L2) in every pass.
+__global__ __launch_bounds__(kTopkThreads) void topk_global_kernel(TopkArgs a) {
+  __shared__ uint32_t smem[kGlobalSmemWords];
+  const int tid = threadIdx.x;
+  const int tok = blockIdx.x;
+  const int S = a.q_per_req, b = tok / S, s = tok % S;
+  const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
+  const int n = min(n_visible(p, a.ratio), a.n_cap);
+  const int K = a.topk;
+  int32_t* out = a.topk_idx + (size_t)tok * K;
+  if (n <= K) {  // fits: every visible row, no scoring needed
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  select_row_global(a.scores + (size_t)tok * a.n_cap, n, K, out, smem);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: four
@@ -624,18 +643,262 @@ bool launch_reg_sized(const TopkArgs& a, int n_bound, bool vec4, hipStream_t st)
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Decode-sized launches: a few hundred long rows or fewer.  One workgroup per
+// row would leave most CUs idle while it reads its row and runs its chain of
+// barriers, so each row is split over several workgroups and merged:
+//   pass 1 (topk_chunk_kernel), one 256-thread workgroup per (token, chunk of
+//     256 * KPT keys): the chunk's keys in registers; a sample of the whole
+//     row (256 groups of 4 consecutive keys, at positions that depend on the
+//     row length only, so every chunk of the row draws the same 1024 keys)
+//     gives the same threshold tau in every chunk's workgroup: the sample key
+//     of the rank expected at row rank K plus four standard deviations, so
+//     that at least K keys of the row clear it with near certainty.  The
+//     chunk's keys >= tau are compacted, in row order, into the chunk's slot
+//     of the workspace (with their count; a slot holds a whole chunk, -1
+//     marks a chunk past its slot's capacity should a plan ever make slots
+//     smaller).
+//   pass 2 (topk_merge_kernel), one 1024-thread workgroup per token: the
+//     token's candidates, chunk by chunk (so in row order), at most 4 per
+//     thread; the exact selection over them (every key >= the K-th largest
+//     candidate is a candidate, since all keys >= tau are), then the
+//     ascending-index emission of the candidate path above.  When the sample
+//     misleads (fewer than K candidates, a chunk past its capacity, or more
+//     candidates than the merge holds) the merge selects over the whole row
+//     from global memory instead: only the speed depends on the data.
+constexpr int kChunkThreads = 256;
+constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kSampleGroups = kChunkThreads;           // one group of 4 keys per thread
+constexpr int kSamples = 4 * kSampleGroups;
+constexpr int kMergePerThread = 8;
+constexpr int kMergeCap = kTopkThreads * kMergePerThread;
+
+// First key of sample group g in a row of n >= 4 keys: spread over the row,
+// a multiple of 4, and g's group ends inside the row.
+__device__ __forceinline__ int sample_group_start(int g, int n) {
+  return (int)(((long long)g * (n - 4)) / (kSampleGroups - 1)) & ~3;
+}
+
+template <int KPT, bool VEC4>
+__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(TopkArgs a) {
+  __shared__ SelectSmem<kChunkWaves> sm;
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x, tok = blockIdx.y;
+  const int S = a.q_per_req, b = tok / S, s = tok % S;
+  const float* row = a.scores + (size_t)tok * a.n_cap;
+  const int i0 = chunk * (kChunkThreads * KPT) + tid * KPT;
+  // the chunk's loads first: they do not depend on the position (a token
+  // that fits Top-K discards them); nothing past n_cap is read
+  const bool vec_slice = VEC4 && i0 + KPT <= a.n_cap;
+  float4 raw[VEC4 ? KPT / 4 : 1];
+  if (vec_slice) {
+#pragma unroll
+    for (int j = 0; j < KPT; j += 4) raw[j / 4] = *reinterpret_cast<const float4*>(row + i0 + j);
+  }
+  const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
+  const int n = min(n_visible(p, a.ratio), a.n_cap);
+  const int K = a.topk;
+  int32_t* cnt_out = a.cand_count + (size_t)tok * a.n_chunks + chunk;
+  if (n <= K) return;  // fits: the merge emits every visible row and reads nothing here
+  if (chunk * (kChunkThreads * KPT) >= n) {
+    if (tid == 0) *cnt_out = 0;
+    return;
+  }
+  // sample group of this thread: 4 keys inside the row (a row shorter than 4
+  // keys repeats its last one)
+  uint32_t sk[4];
+  {
+    const int q = n >= 4 ? sample_group_start(tid, n) : 0;
+    if (VEC4 && n >= 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + q);
+      sk[0] = order_key(v.x);
+      sk[1] = order_key(v.y);
+      sk[2] = order_key(v.z);
+      sk[3] = order_key(v.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sk[e] = order_key(row[min(q + e, n - 1)]);
+    }
+  }
+  uint32_t key[KPT];
+  if (vec_slice) {
+#pragma unroll
+    for (int j = 0; j < KPT; j += 4) {
+      const float4 v = raw[j / 4];
+      key[j] = order_key(v.x);
+      key[j + 1] = order_key(v.y);
+      key[j + 2] = order_key(v.z);
+      key[j + 3] = order_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = order_key(row[min(i0 + j, n - 1)]);
+  }
+  auto valid = [&](int j) { return i0 + j < n; };
+
+  // tau: the sample key of rank ks (exact: the select runs to the end)
+  const int ks0 = (int)(((long long)K * kSamples + n - 1) / n);
+  const int ks = min(kSamples, ks0 + 4 * (int)sqrtf((float)ks0) + 4);
+  uint32_t tau;
+  int unused;
+  block_radix_select<kChunkWaves, false, 4, true>([&](int r) { return sk[r]; }, [&](int) { return true; }, ks,
+                                                  0u, 0xFFFFFFFFu, sm, tau, unused);
+  // the chunk's keys >= tau, compacted in row order
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) mine += (valid(j) && key[j] >= tau) ? 1 : 0;
+  int total;
+  int pos = block_exclusive_scan<kChunkWaves>(mine, sm.red, total);
+  if (total > a.chunk_cap) {  // block-uniform
+    if (tid == 0) *cnt_out = -1;
+    return;
+  }
+  uint2* cand = a.cand + ((size_t)tok * a.n_chunks + chunk) * a.chunk_cap;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool hit = valid(j) && key[j] >= tau;
+    if (hit) cand[pos] = make_uint2(key[j], (uint32_t)(i0 + j));
+    pos += hit ? 1 : 0;
+  }
+  if (tid == 0) *cnt_out = total;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(TopkArgs a) {
+  __shared__ SelectSmem<kTopkWaves> sm;
+  __shared__ uint32_t gsm[kGlobalSmemWords];   // the whole-row fallback
+  __shared__ int first[65];                    // first candidate of each chunk
+  __shared__ int status[2];                    // (total candidates, any chunk past its capacity)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tok = blockIdx.x;
+  const int S = a.q_per_req, b = tok / S, s = tok % S;
+  const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
+  const int n = min(n_visible(p, a.ratio), a.n_cap);
+  const int K = a.topk;
+  int32_t* out = a.topk_idx + (size_t)tok * K;
+  if (n <= K) {  // fits: every visible row, no scoring needed
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  // candidates per chunk (the chunks holding visible keys: at most 64)
+  const int nch = (n + a.chunk_keys - 1) / a.chunk_keys;
+  if (wave == 0) {
+    const int c = lane < nch ? a.cand_count[(size_t)tok * a.n_chunks + lane] : 0;
+    const uint64_t over = __ballot(c < 0);
+    const int inc = wave_inclusive_scan(max(c, 0));
+    first[lane + 1] = inc;
+    if (lane == 0) first[0] = 0;
+    if (lane == kWave - 1) {
+      status[0] = inc;
+      status[1] = over != 0 ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  const int total = status[0];
+  if (status[1] || total < K || total > kMergeCap) {  // block-uniform
+    select_row_global(a.scores + (size_t)tok * a.n_cap, n, K, out, gsm);
+    return;
+  }
+  // thread t holds candidates [4t, 4t + 4): row order
+  uint2 cv[kMergePerThread];
+  const int c0 = tid * kMergePerThread;
+  const int cnt = max(0, min(kMergePerThread, total - c0));
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kMergePerThread; ++j) {
+    const int i = min(c0 + j, total - 1);
+    int c = 0;  // chunk of candidate i: first[c] <= i < first[c + 1]
+    for (int step = 32; step > 0; step >>= 1)
+      if (c + step <= nch - 1 && first[c + step] <= i) c += step;
+    cv[j] = a.cand[((size_t)tok * a.n_chunks + c) * a.chunk_cap + (i - first[c])];
+    kmax = max(kmax, cv[j].x);
+  }
+  // every candidate lies in [smallest candidate, row max] (the range only
+  // decides how many radix passes run)
+  uint32_t cmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < kMergePerThread; ++j) cmin = j < cnt ? min(cmin, cv[j].x) : cmin;
+  uint32_t lo, row_max;
+  block_min_max<kTopkWaves>(cmin, kmax, sm.red, lo, row_max);
+  uint32_t T;
+  int keq;
+  block_radix_select<kTopkWaves, false, kMergePerThread, true>(
+      [&](int r) { return cv[r].x; }, [&](int r) { return r < cnt; }, K, lo, row_max, sm, T, keq);
+  emit_selection<kTopkWaves, kMergePerThread>([&](int j) { return cv[j]; }, cnt, T, keq, out, K, sm.red);
+}
+
+template <int KPT>
+void launch_two_pass(const TopkArgs& a, bool vec4, hipStream_t st) {
+  const dim3 grid(a.n_chunks, a.batch * a.q_per_req);
+  if (vec4)
+    hipLaunchKernelGGL((topk_chunk_kernel<KPT, true>), grid, dim3(kChunkThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((topk_chunk_kernel<KPT, false>), grid, dim3(kChunkThreads), 0, st, a);
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(a.batch * a.q_per_req), dim3(kTopkThreads), 0, st, a);
+}
+
 }  // namespace
+
+TopkPlan topk_plan(int batch, int q_per_req, int n_cap, int topk, int ratio, int max_len) {
+  TopkPlan pl{};
+  const long long tokens = (long long)batch * q_per_req;
+  const int n_bound = std::min(n_cap, max_len / ratio);
+  // Two passes for decode-sized launches of rows longer than one workgroup's
+  // registers hold (32768 keys; there the one-workgroup selection re-reads
+  // the row from L2 in every pass), with K small enough that the merge's
+  // 8192 candidates hold the sampled threshold's expected count (about 2.9 K
+  // at K = 1024 of 131072) with a wide margin.
+#ifndef CSA_TOPK_TWO_PASS_MIN_ROW
+#define CSA_TOPK_TWO_PASS_MIN_ROW 32769
+#endif
+#ifndef CSA_TOPK_TWO_PASS
+#define CSA_TOPK_TWO_PASS 1
+#endif
+  if (CSA_TOPK_TWO_PASS && tokens < CSA_TOPK_SMALL_BLOCK_TOKENS_DEFAULT && n_bound >= CSA_TOPK_TWO_PASS_MIN_ROW &&
+      topk <= 1024 && n_bound >= 4 * topk) {
+    // the largest chunk (1024 .. 8192 keys) that still gives every CU a
+    // workgroup, within the 64 chunks per row the merge reads
+    int kpt = 0;
+    for (int k : {32, 16, 8, 4}) {
+      const long long chunks = (n_bound + kChunkThreads * k - 1) / (kChunkThreads * k);
+      if (chunks > 64) break;
+      kpt = k;
+      if (tokens * chunks >= 256) break;
+    }
+    const int chunks = kpt ? (n_bound + kChunkThreads * kpt - 1) / (kChunkThreads * kpt) : 0;
+    if (chunks < 2) return pl;  // rows too long for 64 chunks, or too short to split
+    pl.two_pass = true;
+    pl.chunk_keys = kChunkThreads * kpt;
+    pl.n_chunks = (n_bound + pl.chunk_keys - 1) / pl.chunk_keys;
+    // a slot holds a whole chunk: however the winners cluster in the row, no
+    // chunk overflows (the number of candidates is a property of the row)
+    pl.chunk_cap = pl.chunk_keys;
+    pl.cand_bytes = ((size_t)tokens * pl.n_chunks * pl.chunk_cap * 8 + 255) / 256 * 256;
+    pl.count_bytes = ((size_t)tokens * pl.n_chunks * 4 + 255) / 256 * 256;
+    pl.ws_bytes = pl.cand_bytes + pl.count_bytes;
+  }
+  return pl;
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   const int n_bound = std::min(a.n_cap, a.max_len / a.ratio);
   const long long tokens = (long long)a.batch * a.q_per_req;
   // rows start 16-byte aligned when n_cap is a multiple of 4 floats
   const bool vec4 = (a.n_cap & 3) == 0;
+  if (a.cand) {  // the two-pass plan (the caller sized the workspace by topk_plan)
+    switch (a.chunk_keys / kChunkThreads) {
+      case 4: launch_two_pass<4>(a, vec4, st); break;
+      case 8: launch_two_pass<8>(a, vec4, st); break;
+      case 16: launch_two_pass<16>(a, vec4, st); break;
+      case 32: launch_two_pass<32>(a, vec4, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // A decode step has few tokens: one 16-wave block per token, for latency.
   // A prefill chunk has thousands: 4-wave blocks (several per CU) when every
   // row fits in their registers.
 #ifndef CSA_TOPK_SMALL_BLOCK_TOKENS
-#define CSA_TOPK_SMALL_BLOCK_TOKENS 2048
+#define CSA_TOPK_SMALL_BLOCK_TOKENS CSA_TOPK_SMALL_BLOCK_TOKENS_DEFAULT
 #endif
 #ifndef CSA_TOPK_SMALL_BLOCK_WAVES
 #define CSA_TOPK_SMALL_BLOCK_WAVES 4

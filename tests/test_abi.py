@@ -152,6 +152,19 @@ def test_topk_null():
     assert call_topk(shape(), [FAKE, None, FAKE]) == 1
 
 
+def test_topk_workspace_refusals():
+    # rows past 32768 keys are split over several workgroups, whose
+    # candidates need the workspace
+    sh = I.CONFIGS[3].shape.replace(n_cap=65536, max_len=4 * 65536)
+    need = C.topk_workspace_bytes(sh)
+    assert need > 0
+    lib = C.lib()
+    cs = ctypes.byref(C.CShape.of(sh))
+    assert lib.csa_topk(cs, FAKE, FAKE, FAKE, None, 0, None) == 6
+    assert lib.csa_topk(cs, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 6
+    assert lib.csa_topk(cs, FAKE, FAKE, FAKE, MISALIGNED, need, None) == 5
+
+
 @pytest.mark.parametrize("case,code", [
     (dict(head_dim=96, rope_dim=32), 8),
     (dict(heads=32), 8),
@@ -222,10 +235,15 @@ def test_empty_problem_is_ok_without_gpu_work():
 def test_workspace_queries():
     for cid, cfg in I.CONFIGS.items():
         sh = cfg.shape
-        assert C.topk_workspace_bytes(sh) == 0
+        # rows of at most 32768 keys: one workgroup per row, no workspace
+        assert C.topk_workspace_bytes(sh) == 0, cid
         ws = C.sparse_attn_workspace_bytes(sh)
         T = sh.batch * sh.q_per_req
         assert ws >= T * 2 * sh.heads * (sh.head_dim + 2) * 4     # at least one split per stream
+    # decode launches over longer rows select in two passes: a candidate slot
+    # of a whole chunk per (token, chunk), and counts
+    long = I.CONFIGS[4].shape.replace(n_cap=131072, max_len=4 * 131072)
+    assert C.topk_workspace_bytes(long) >= long.batch * long.q_per_req * 131072 * 8
 
 
 def test_binding_refuses_cpu_tensors():

@@ -496,7 +496,8 @@ def test_topk_exact_on_oracle_scores(cid, config_inputs):
 @pytest.mark.parametrize("kind", ["normal", "coarse", "signed_zero", "spiked16", "spiked32"])
 @pytest.mark.parametrize("n_cap,topk", [(300, 64), (4096, 256), (4096, 257), (9000, 1024),
                                         (16384, 512), (32768, 1024), (32768, 4096), (40000, 2048),
-                                        (1000, 999), (20000, 4000), (4100, 1024), (12292, 2048)])
+                                        (1000, 999), (20000, 4000), (4100, 1024), (12292, 2048),
+                                        (65536, 1024), (131072, 512), (131072, 64)])
 def test_topk_exact_synthetic(kind, n_cap, topk):
     # "spiked" rows put their largest values exactly where the selection's
     # strided sample looks, so the sampled threshold keeps too few rows and
@@ -504,7 +505,9 @@ def test_topk_exact_synthetic(kind, n_cap, topk):
     # rows of several visible lengths, including n_vis == K and K + 1.
     # 4100 and 12292 are multiples of 4 but not of the per-thread slice length
     # (8 and 16), so a thread's slice would straddle n_cap: the selection must
-    # take its per-element load path there.
+    # take its per-element load path there.  Rows past 32768 keys take the
+    # two-pass selection (chunks, then a merge), short rows of the same launch
+    # included.
     B, S = 3, 2
     sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=16, heads=1,
                  head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1,
@@ -517,7 +520,7 @@ def test_topk_exact_synthetic(kind, n_cap, topk):
     d_scores = torch.from_numpy(scores).cuda()
     d_sp = torch.from_numpy(sp).cuda()
     out = torch.full((B, S, topk), -7, dtype=torch.int32, device="cuda")
-    C.topk(sh, d_scores, d_sp, out)
+    C.topk(sh, d_scores, d_sp, out, C.alloc_topk_workspace(sh))
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
 
@@ -540,7 +543,8 @@ def test_topk_many_tokens(kind, n_cap, topk):
     scores = I.random_scores(n_cap * 7 + topk, B, S, n_cap, kind)
     ref = oracle.run(sh, dict(start_pos=sp), jobs=oracle.JOB_TOPK, scores=scores, nthreads=NTHREADS)
     out = torch.full((B, S, topk), -7, dtype=torch.int32, device="cuda")
-    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out)
+    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out,
+           C.alloc_topk_workspace(sh))
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
 
@@ -558,7 +562,8 @@ def test_topk_winners_past_256(topk):
     sp = np.array([4 * n_cap - 1], np.int32)
     ref = oracle.run(sh, dict(start_pos=sp), jobs=oracle.JOB_TOPK, scores=scores)
     out = torch.empty((1, 1, topk), dtype=torch.int32, device="cuda")
-    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out)
+    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out,
+           C.alloc_topk_workspace(sh))
     got = out.cpu().numpy()
     assert set(planted.tolist()) <= set(got[0, 0].tolist())
     assert np.array_equal(got, ref["topk_idx"])
