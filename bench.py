@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--stage-launches", type=int, default=64,
                     help="least number of flushed steps timed stage by stage (per-stage events)")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--no-hot", action="store_true",
+                    help="skip the back-to-back pass (profiler runs of flushed launches only)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -318,12 +320,14 @@ def main():
         wall_flushed = time.perf_counter() - t0
         step_us = [us(e, 0, 4) for e in sev]
     # hot pass (the headline with --cache hot, a labelled extra otherwise)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(hot_steps):
-        run_step(r=k)
-    torch.cuda.synchronize()
-    hot_ms = (time.perf_counter() - t0) * 1000.0 / hot_steps
+    hot_ms = None
+    if args.cache == "hot" or not args.no_hot:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(hot_steps):
+            run_step(r=k)
+        torch.cuda.synchronize()
+        hot_ms = (time.perf_counter() - t0) * 1000.0 / hot_steps
     if args.cache == "flushed":
         ms_per_step = float(np.median(step_us)) * 1e-3
     else:
@@ -480,8 +484,8 @@ def main():
                        f"{args.cache} as the timed steps; their extra event packets add gaps, so "
                        "the stages sum above ms_per_step",
         "event_step_us": round(t_event_step * 1e6, 2),
-        "hot": {"cache": "hot", "ms_per_step": round(hot_ms, 4),
-                "value": round(T / (hot_ms * 1e-3), 1),
+        "hot": None if hot_ms is None else
+               {"cache": "hot", "ms_per_step": round(hot_ms, 4), "value": round(T / (hot_ms * 1e-3), 1),
                 "step_time": f"wall time of {hot_steps} back-to-back steps / {hot_steps}"},
         "cpu_baseline": cpu,
     }

@@ -188,7 +188,7 @@ csa_status_t csa_indexer_score_paged(const csa_shape_t* shape, const void* q_idx
                                      float* scores, void* stream);
 
 /* Workspace bytes csa_topk needs for this shape (0 means none).  Launches of
- * fewer than 2048 query tokens over rows of at least 4096 visible entries
+ * fewer than 2048 query tokens whose rows can exceed 32768 visible entries
  * (K <= 1024, at most a quarter of the row) split each row over several
  * workgroups and merge their candidates; their candidates and counts live in
  * the workspace (contents need no initialisation). */

@@ -24,6 +24,7 @@ struct ScoreArgs {
   const int32_t* block_table;
   int blocks_per_req, block_shift;
   int64_t n_blocks;
+  int gemm_key_blocks, gemm_row_blocks;  // GEMM-shaped prefill grid (set by the launcher)
 };
 
 struct TopkArgs {
