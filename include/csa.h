@@ -217,8 +217,11 @@ csa_status_t csa_topk(const csa_shape_t* shape, const float* scores, const int32
                       int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes csa_sparse_attn_decode needs for this shape (split
- * partials).  Its contents need no initialisation; calls that overlap in time
- * must not share a workspace. */
+ * partials).  0 for shapes that a single workgroup per token finishes by
+ * itself: window and Top-K rows within 12 waves of at most 64 rows each
+ * (fp32 rows of 128 dims: 16 rows), at most 4096 tokens, and at least 1024
+ * such waves in all.  Its contents need no initialisation; calls that overlap
+ * in time must not share a workspace. */
 size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* shape);
 
 /* Two-stream sparse attention of every query token, merged, RoPE undone, packed.
@@ -248,7 +251,8 @@ size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* shape);
  *   topk_idx [B][S][K]           int32 (ascending or not; duplicates count twice)
  *   rope_cos, rope_sin [rope_rows][Dr/2] float32, rope_rows >= max_len
  *   out      [G][B*S][(H/G)*D]   dtype output
- *   ws       at least csa_sparse_attn_workspace_bytes(shape) bytes
+ *   ws       at least csa_sparse_attn_workspace_bytes(shape) bytes, 16-byte
+ *            aligned (may be NULL when that is 0)
  * Requires w_cap >= win + S - 1.  One request's slice of a K or V cache
  * (n_cap or w_cap rows) must stay below 2^31 - 4096 bytes, else
  * CSA_ERR_UNSUPPORTED.
@@ -269,6 +273,7 @@ csa_status_t csa_sparse_attn_decode(const csa_shape_t* shape, const void* q, con
  * The call allocates nothing and frees nothing.
  *   - A shape whose workspace (csa_sparse_attn_workspace_bytes) exceeds that
  *     size is refused with CSA_ERR_WORKSPACE before anything is enqueued.
+ *     A shape whose workspace is 0 does not touch the array.
  *   - The first call on a GPU looks up that GPU's copy of the array (the
  *     GPU that runs `stream`); CSA_ERR_LAUNCH if the lookup fails.
  *   - Every call on one GPU shares that GPU's array and leaves the last

@@ -203,13 +203,14 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
   }
   const csa::AttnPlan pl =
       csa::attn_plan(sh->batch, sh->q_per_req, sh->heads, sh->head_dim, sh->win, sh->topk, sh->dtype);
-  if (use_scratch ? pl.ws_bytes > kScratchBytes : (!ws || ws_bytes < pl.ws_bytes)) return CSA_ERR_WORKSPACE;
+  if (use_scratch ? pl.ws_bytes > kScratchBytes : (pl.ws_bytes && (!ws || ws_bytes < pl.ws_bytes)))
+    return CSA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_win) || !aligned16(v_win) || !aligned16(k_cmp) ||
       !aligned16(v_cmp) || !aligned16(topk_idx) || !aligned16(start_pos) || !aligned16(out) ||
-      (!use_scratch && !aligned16(ws)) || (rope_cos && !aligned16(rope_cos)) ||
+      (!use_scratch && pl.ws_bytes && !aligned16(ws)) || (rope_cos && !aligned16(rope_cos)) ||
       (rope_sin && !aligned16(rope_sin)))
     return CSA_ERR_ALIGNMENT;
-  if (use_scratch) {  // every check has passed: only now touch the device
+  if (use_scratch && pl.ws_bytes) {  // every check has passed: only now touch the device
     ws = scratch_address(static_cast<hipStream_t>(stream));
     if (!ws) return CSA_ERR_LAUNCH;
   }
@@ -243,6 +244,8 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
   a.chunks_per_wave = pl.chunks_per_wave;
   a.n_split_win = pl.n_split_win;
   a.n_split_cmp = pl.n_split_cmp;
+  a.waves_win = pl.waves_win;
+  a.waves_cmp = pl.waves_cmp;
   if (pages) {
     a.block_table = pages->block_table;
     a.blocks_per_req = pages->blocks_per_req;

@@ -68,6 +68,9 @@ struct AttnArgs {
       max_len, dtype;
   float scale_log2;         // softmax_scale * log2(e)
   int chunks_per_wave, n_split_win, n_split_cmp;
+  // one workgroup per token (waves_win + waves_cmp > 0): that many waves walk
+  // the window and the Top-K list; no split partials
+  int waves_win, waves_cmp;
   // paged compressed K/V (block_table non-null): k_cmp / v_cmp are pools, as
   // for ScoreArgs
   const int32_t* block_table;
@@ -94,7 +97,10 @@ struct WritebackArgs {
 // Split plan of the attention kernel; a function of the shape only, so the
 // workspace query and the launch always agree.
 struct AttnPlan {
-  int chunks_per_wave;  // 16-row chunks per wave (4 waves per workgroup)
+  int chunks_per_wave;  // 16-row chunks per wave
+  // one workgroup per token: waves per stream (0, 0 for the split kernels)
+  int waves_win, waves_cmp;
+  // split kernels: 4 waves per workgroup
   int rows_per_split;   // 64 * chunks_per_wave
   int n_split_win, n_split_cmp;
   size_t ws_o_floats, ws_ml_floats;

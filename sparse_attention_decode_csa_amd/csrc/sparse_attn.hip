@@ -48,6 +48,7 @@ namespace {
 
 constexpr int kChunk = 16;  // rows per MFMA chunk
 constexpr int kWaves = 4;
+constexpr int kTokenMaxWaves = 12;  // waves of the one-workgroup-per-token kernel
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any valid range
 
 template <typename T, int D>
@@ -159,6 +160,136 @@ __device__ __forceinline__ void compute_chunk(const Chunk<T, D>& ch, const u32x4
   }
 }
 
+// Output dims (d, d+1) of head h of token tok, already normalised: the
+// inverse RoPE rotation of the pair by the position's angle (cs, sn) when it
+// lies in the rotary dims, one rounding, the packed group layout.
+template <typename T, int D>
+__device__ __forceinline__ void store_pair(const AttnArgs& a, int tok, int h, int d, float x, float y, float cs,
+                                           float sn) {
+  const int Hg = a.heads / a.out_groups;
+  if (d >= D - a.rope_dim) {  // inverse RoPE: turn the pair back by the position's angle
+    const float xr = x * cs + y * sn;
+    const float yr = y * cs - x * sn;
+    x = xr;
+    y = yr;
+  }
+  const int grp = h / Hg, hl = h - grp * Hg;
+  const size_t o = ((size_t)grp * a.batch * a.q_per_req + tok) * Hg * D + (size_t)hl * D + d;
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t packed = float_to_bf16_bits(x) | (float_to_bf16_bits(y) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o) = packed;
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(x, y);
+  }
+}
+
+// B operand of logits^T: q^T of token tok, column = head n16 (zero for
+// padded heads).  Depends on nothing else, so it is issued first.
+template <typename T, int D>
+__device__ __forceinline__ void load_query(const AttnArgs& a, int tok, int n16, int g,
+                                           u32x4_t (&qf)[AttnGeo<T, D>::CH]) {
+  using G = AttnGeo<T, D>;
+  const char* qp = static_cast<const char*>(a.q) + ((size_t)tok * a.heads + min(n16, a.heads - 1)) * G::ROW + g * 16;
+#pragma unroll
+  for (int c = 0; c < G::CH; ++c) {
+    const u32x4_t v = ld16(qp + c * 64);
+    qf[c] = n16 < a.heads ? v : u32x4_t{0, 0, 0, 0};
+  }
+}
+
+// One wave's pass over entries [e_lo, e_lo + 16 * CPW) of one stream of token
+// (b, s): its online-softmax state, with lane (n16, g) holding O[head n16][d]
+// for d = g*D/4 + (D/16)*i + t in acc[t][i], the head's running max in m_run
+// and the head's sum over the wave's rows in l_tot (same in the 4 lanes of a
+// head).
+template <typename T, int D, int CPW>
+__device__ __forceinline__ void wave_pass(const AttnArgs& a, bool win, int b, int s, int e_lo, int lane,
+                                          const u32x4_t (&qf)[AttnGeo<T, D>::CH], f32x4_t (&acc)[AttnGeo<T, D>::DT],
+                                          float& m_run, float& l_tot) {
+  using G = AttnGeo<T, D>;
+  constexpr int RPW = kChunk * CPW;  // rows per wave
+  static_assert(RPW <= 64, "one row number per lane");
+  const int n16 = lane & 15, g = lane >> 4;
+  const int tok = b * a.q_per_req + s;
+
+  // The byte offset of the row behind entry e_lo + lane (kOutOfRange for
+  // padding or past the end).
+  int e_hi;
+  uint32_t rowoff;
+  if (win) {
+    const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
+    const int nrows = min(a.win, p + 1);
+    const int first_pos = p - nrows + 1;
+    e_hi = min(nrows, e_lo + RPW);
+    const int e = e_lo + lane;
+    const int slot = (first_pos + e) % a.w_cap;
+    const bool ok = lane < RPW && e < e_hi;
+    if (a.win_table) {  // paged ring: pool row through the window's table (clamped into the pool)
+      const int blk = a.win_table[(size_t)b * a.win_blocks_per_req + (ok ? (slot >> a.win_shift) : 0)];
+      const int64_t pb = min((int64_t)max(blk, 0), a.win_n_blocks - 1);
+      const int64_t prow = (pb << a.win_shift) + (slot & ((1 << a.win_shift) - 1));
+      rowoff = ok ? (uint32_t)(prow * G::ROW) : kOutOfRange;
+    } else {
+      rowoff = ok ? (uint32_t)slot * G::ROW : kOutOfRange;
+    }
+  } else {
+    e_hi = min(a.topk, e_lo + RPW);
+    const int e = e_lo + lane;
+    const int j = (lane < RPW && e < e_hi) ? a.topk_idx[(size_t)tok * a.topk + e] : -1;
+    const bool ok = j >= 0 && j < a.n_cap;
+    if (a.block_table) {  // paged: pool row through the block table (clamped into the pool)
+      const int blk = a.block_table[(size_t)b * a.blocks_per_req + (ok ? (j >> a.block_shift) : 0)];
+      const int64_t pb = min((int64_t)max(blk, 0), a.n_blocks - 1);
+      const int64_t prow = (pb << a.block_shift) + (j & ((1 << a.block_shift) - 1));
+      rowoff = ok ? (uint32_t)(prow * G::ROW) : kOutOfRange;
+    } else {
+      rowoff = ok ? (uint32_t)j * G::ROW : kOutOfRange;
+    }
+  }
+  const int nrows_wave = e_hi - e_lo;  // may be <= 0
+
+  // the request's slice of its cache, or for a paged cache the whole pool;
+  // the host keeps either below 2^31 bytes
+  const bool pooled = win ? a.win_table != nullptr : a.block_table != nullptr;
+  const size_t rows_req = win ? (size_t)a.w_cap : (size_t)a.n_cap;
+  const size_t base_row = pooled ? 0 : (size_t)b * rows_req;
+  const size_t pool_rows = win ? (size_t)(a.win_n_blocks << a.win_shift) : (size_t)(a.n_blocks << a.block_shift);
+  const size_t range_rows = pooled ? pool_rows : rows_req;
+  const char* kreq = static_cast<const char*>(win ? a.k_win : a.k_cmp) + base_row * G::ROW;
+  const char* vreq = static_cast<const char*>(win ? a.v_win : a.v_cmp) + base_row * G::ROW;
+  const int range = (int)(range_rows * G::ROW);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kreq, range);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vreq, range);
+
+#pragma unroll
+  for (int t = 0; t < G::DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  m_run = -INFINITY;
+  float l_run = 0.0f;
+
+  // Chunks, one ahead: chunk c + 1 is in flight while chunk c is computed.
+  // The loads are issued unconditionally (rows past the end cost no memory
+  // traffic), so the compiler can count them exactly and wait for chunk c
+  // alone; a load under a runtime branch would make it wait for everything.
+  // A scheduling barrier after each chunk keeps later loads from being
+  // hoisted above it, which would only raise register pressure.  A chunk
+  // whose rows are all padding is skipped (it would leave the state as is).
+  Chunk<T, D> buf[2];
+  load_chunk<T, D>(buf[0], krs, vrs, rowoff, 0, n16, g);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    if (c + 1 < CPW) load_chunk<T, D>(buf[(c + 1) & 1], krs, vrs, rowoff, c + 1, n16, g);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kChunk * c < nrows_wave && __builtin_amdgcn_ballot_w64(buf[c & 1].valid != 0) != 0)  // wave-uniform
+      compute_chunk<T, D>(buf[c & 1], qf, acc, m_run, l_run, a.scale_log2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // per-head sum over the 4 lanes that share a head column
+  l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+}
+
 // Split partials of a token, merged in ascending split order into the state
 // of their stream (window splits first, then compressed).  Loads of up to MB
 // splits (one batch) are issued before any of them is used, so a token with
@@ -219,8 +350,6 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int b0, const Sp
 // depends on it: the two reads overlap instead of adding up.
 template <typename T, int D, int MB>
 __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int item) {
-  const int H = a.heads, G = a.out_groups, Hg = H / G;
-  const int T_ = a.batch * a.q_per_req;
   const int r0 = D - a.rope_dim;
   const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
   const int NS = a.n_split_win + a.n_split_cmp;
@@ -245,22 +374,7 @@ __device__ __forceinline__ void finish_item(const AttnArgs& a, int tok, int item
   const float fw = w.l > 0.0f ? exp2f(w.m - M) : 0.0f;
   const float fc = c.l > 0.0f ? exp2f(c.m - M) : 0.0f;
   const float inv = 1.0f / (fw * w.l + fc * c.l);
-  float x = (fw * w.o0 + fc * c.o0) * inv;
-  float y = (fw * w.o1 + fc * c.o1) * inv;
-  if (d >= r0) {  // inverse RoPE: turn the pair back by the position's angle
-    const float xr = x * cs + y * sn;
-    const float yr = y * cs - x * sn;
-    x = xr;
-    y = yr;
-  }
-  const int grp = h / Hg, hl = h - grp * Hg;
-  const size_t o = ((size_t)grp * T_ + tok) * Hg * D + (size_t)hl * D + d;
-  if constexpr (sizeof(T) == 2) {
-    const uint32_t packed = float_to_bf16_bits(x) | (float_to_bf16_bits(y) << 16);
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + o) = packed;
-  } else {
-    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + o) = make_float2(x, y);
-  }
+  store_pair<T, D>(a, tok, h, d, (fw * w.o0 + fc * c.o0) * inv, (fw * w.o1 + fc * c.o1) * inv, cs, sn);
 }
 
 constexpr int kFinishThreads = 256;
@@ -291,95 +405,12 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
   float* ml_out = a.ws_ml + ((size_t)tok * NS + split) * H * 2;
   float* o_out = a.ws_o + ((size_t)tok * NS + split) * H * D;
 
-  // B operand of logits^T: q^T, column = head n16 (zero for padded heads);
-  // issued first, it does not depend on the position.
   u32x4_t qf[G::CH];
-  {
-    const char* qp = static_cast<const char*>(a.q) + ((size_t)tok * H + min(n16, H - 1)) * G::ROW + g * 16;
-#pragma unroll
-    for (int c = 0; c < G::CH; ++c) {
-      const u32x4_t v = ld16(qp + c * 64);
-      qf[c] = n16 < H ? v : u32x4_t{0, 0, 0, 0};
-    }
-  }
-
-  // This wave's entries [e_lo, e_hi) of the stream, and the byte offset of the
-  // row behind entry e_lo + lane (kOutOfRange for padding or past the end).
-  int e_lo, e_hi;
-  uint32_t rowoff;
-  if (win) {
-    const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
-    const int nrows = min(a.win, p + 1);
-    const int first_pos = p - nrows + 1;
-    e_lo = split * RPS + wave * RPW;
-    e_hi = min(nrows, e_lo + RPW);
-    const int e = e_lo + lane;
-    const int slot = (first_pos + e) % a.w_cap;
-    const bool ok = lane < RPW && e < e_hi;
-    if (a.win_table) {  // paged ring: pool row through the window's table (clamped into the pool)
-      const int blk = a.win_table[(size_t)b * a.win_blocks_per_req + (ok ? (slot >> a.win_shift) : 0)];
-      const int64_t pb = min((int64_t)max(blk, 0), a.win_n_blocks - 1);
-      const int64_t prow = (pb << a.win_shift) + (slot & ((1 << a.win_shift) - 1));
-      rowoff = ok ? (uint32_t)(prow * G::ROW) : kOutOfRange;
-    } else {
-      rowoff = ok ? (uint32_t)slot * G::ROW : kOutOfRange;
-    }
-  } else {
-    e_lo = (split - NSW) * RPS + wave * RPW;
-    e_hi = min(a.topk, e_lo + RPW);
-    const int e = e_lo + lane;
-    const int j = (lane < RPW && e < e_hi) ? a.topk_idx[(size_t)tok * a.topk + e] : -1;
-    const bool ok = j >= 0 && j < a.n_cap;
-    if (a.block_table) {  // paged: pool row through the block table (clamped into the pool)
-      const int blk = a.block_table[(size_t)b * a.blocks_per_req + (ok ? (j >> a.block_shift) : 0)];
-      const int64_t pb = min((int64_t)max(blk, 0), a.n_blocks - 1);
-      const int64_t prow = (pb << a.block_shift) + (j & ((1 << a.block_shift) - 1));
-      rowoff = ok ? (uint32_t)(prow * G::ROW) : kOutOfRange;
-    } else {
-      rowoff = ok ? (uint32_t)j * G::ROW : kOutOfRange;
-    }
-  }
-  const int nrows_wave = e_hi - e_lo;  // may be <= 0
-
-  // the request's slice of its cache, or for a paged cache the whole pool;
-  // the host keeps either below 2^31 bytes
-  const bool pooled = win ? a.win_table != nullptr : a.block_table != nullptr;
-  const size_t rows_req = win ? (size_t)a.w_cap : (size_t)a.n_cap;
-  const size_t base_row = pooled ? 0 : (size_t)b * rows_req;
-  const size_t pool_rows = win ? (size_t)(a.win_n_blocks << a.win_shift) : (size_t)(a.n_blocks << a.block_shift);
-  const size_t range_rows = pooled ? pool_rows : rows_req;
-  const char* kreq = static_cast<const char*>(win ? a.k_win : a.k_cmp) + base_row * G::ROW;
-  const char* vreq = static_cast<const char*>(win ? a.v_win : a.v_cmp) + base_row * G::ROW;
-  const int range = (int)(range_rows * G::ROW);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kreq, range);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vreq, range);
-
+  load_query<T, D>(a, tok, n16, g, qf);
   f32x4_t acc[G::DT];
-#pragma unroll
-  for (int t = 0; t < G::DT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  // Chunks, one ahead: chunk c + 1 is in flight while chunk c is computed.
-  // The loads are issued unconditionally (rows past the end cost no memory
-  // traffic), so the compiler can count them exactly and wait for chunk c
-  // alone; a load under a runtime branch would make it wait for everything.
-  // A scheduling barrier after each chunk keeps later loads from being
-  // hoisted above it, which would only raise register pressure.
-  Chunk<T, D> buf[2];
-  load_chunk<T, D>(buf[0], krs, vrs, rowoff, 0, n16, g);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    if (c + 1 < CPW) load_chunk<T, D>(buf[(c + 1) & 1], krs, vrs, rowoff, c + 1, n16, g);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kChunk * c < nrows_wave)  // wave-uniform
-      compute_chunk<T, D>(buf[c & 1], qf, acc, m_run, l_run, a.scale_log2);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // per-head sum over the 4 lanes that share a head column
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  float m_run, l_tot;
+  const int e_lo = (win ? split : split - NSW) * RPS + wave * RPW;
+  wave_pass<T, D, CPW>(a, win, b, s, e_lo, lane, qf, acc, m_run, l_tot);
 
   // ---- the 4 waves' partials, merged in fixed wave order.  Lane (n16, g)
   // holds O[head n16][d] for d = g*D/4 + (D/16)*i + t in acc[t][i].
@@ -430,12 +461,122 @@ __global__ __launch_bounds__(kFinishThreads) void attn_finish_kernel(AttnArgs a)
   finish_item<T, D, MB>(a, tok, item);
 }
 
+// LDS DMA of 4 bytes per lane to lds + 4 * lane (wave 0 of the workgroup).
+__device__ __forceinline__ void dma4_global(const float* src, float* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// The whole step of one token in one workgroup, for shapes whose window and
+// Top-K rows fit 12 waves of at most 4 chunks: waves [0, WW) walk the window,
+// waves [WW, WW + WC) the Top-K list, each as one split wave does.  Their
+// states meet in LDS and the workgroup finishes the token itself: per head,
+// each stream's max and sum over its waves in fixed wave order, the stream
+// merge, then per output pair the factor-weighted sum over the waves in fixed
+// order, the inverse RoPE, one rounding and the packed store.  No partials
+// leave the workgroup and there is no second launch.
+template <typename T, int D, int CPW>
+__global__ __launch_bounds__(kTokenMaxWaves * 64) void attn_token_kernel(AttnArgs a) {
+  using G = AttnGeo<T, D>;
+  constexpr int RPW = kChunk * CPW;
+  __shared__ __attribute__((aligned(16))) float mo[kTokenMaxWaves * 16 * G::MO_STRIDE];  // [wave][head][d]
+  __shared__ float wml[kTokenMaxWaves][16][2];  // per-wave (max, sum) per head
+  __shared__ float wfac[kTokenMaxWaves][16];    // per-wave output factor per head
+  __shared__ float rope_cs[D / 2], rope_sn[D / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = a.waves_win + a.waves_cmp;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int S = a.q_per_req, H = a.heads, WW = a.waves_win;
+  // neighbouring tokens (the S tokens of a request read the same window rows)
+  // land on the same XCD
+  const int tok = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int b = tok / S, s = tok - b * S;
+  const bool win = wave < WW;
+
+  u32x4_t qf[G::CH];
+  load_query<T, D>(a, tok, n16, g, qf);
+  // the position's RoPE row, copied straight into LDS (no registers held
+  // across the gather); the barrier before the merge waits for it
+  const int half = a.rope_dim >> 1;
+  if (tid < half) {
+    const int p = clamp_pos(a.start_pos[b] + s, a.max_len);
+    dma4_global(a.rope_cos + (size_t)p * half + tid, rope_cs);
+    dma4_global(a.rope_sin + (size_t)p * half + tid, rope_sn);
+  }
+  f32x4_t acc[G::DT];
+  float m_run, l_tot;
+  wave_pass<T, D, CPW>(a, win, b, s, (win ? wave : wave - WW) * RPW, lane, qf, acc, m_run, l_tot);
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < G::DT; ++t)
+      mo[(wave * 16 + n16) * G::MO_STRIDE + g * (D / 4) + (D / 16) * i + t] = acc[t][i];
+  if (g == 0) {
+    wml[wave][n16][0] = m_run;
+    wml[wave][n16][1] = l_tot;
+  }
+  __syncthreads();  // also waits for every wave's outstanding loads, the RoPE copy included
+  if (tid < nw * 16) {  // output factor of wave v for head h
+    const int v = tid >> 4, h = tid & 15;
+    float Mw = -INFINITY, Mc = -INFINITY;
+    for (int u = 0; u < nw; ++u) {
+      if (u < WW) Mw = fmaxf(Mw, wml[u][h][0]);
+      else Mc = fmaxf(Mc, wml[u][h][0]);
+    }
+    float Lw = 0.0f, Lc = 0.0f;
+    for (int u = 0; u < nw; ++u) {
+      const float l = wml[u][h][1];
+      if (!(l > 0.0f)) continue;  // a wave that saw no row carries no weight
+      if (u < WW) Lw += exp2f(wml[u][h][0] - Mw) * l;
+      else Lc += exp2f(wml[u][h][0] - Mc) * l;
+    }
+    // stream merge: an empty stream (sum 0) carries no weight
+    const float M = fmaxf(Mw, Mc);
+    const float fw = Lw > 0.0f ? exp2f(Mw - M) : 0.0f;
+    const float fc = Lc > 0.0f ? exp2f(Mc - M) : 0.0f;
+    const float inv = 1.0f / (fw * Lw + fc * Lc);
+    const float l = wml[v][h][1];
+    wfac[v][h] = l > 0.0f ? exp2f(wml[v][h][0] - (v < WW ? Mw : Mc)) * (v < WW ? fw : fc) * inv : 0.0f;
+  }
+  __syncthreads();
+  const int r0 = D - a.rope_dim;
+  for (int item = tid; item < H * (D / 2); item += nw * 64) {
+    const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
+    float x = 0.0f, y = 0.0f;
+    for (int v = 0; v < nw; ++v) {
+      const float f = wfac[v][h];
+      const float2 o = *reinterpret_cast<const float2*>(&mo[(v * 16 + h) * G::MO_STRIDE + d]);
+      x += f * o.x;
+      y += f * o.y;
+    }
+    const int i = (d - r0) >> 1;
+    store_pair<T, D>(a, tok, h, d, x, y, d >= r0 ? rope_cs[i] : 1.0f, d >= r0 ? rope_sn[i] : 0.0f);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   const int tokens = a.batch * a.q_per_req;
+  constexpr bool kWideRows = sizeof(T) == 4 && D == 128;  // one chunk per wave only
+  if (a.waves_win + a.waves_cmp > 0) {  // one workgroup per token
+    const dim3 tgrid(tokens), tblock(64 * (a.waves_win + a.waves_cmp));
+    switch (a.chunks_per_wave) {
+      case 1: hipLaunchKernelGGL((attn_token_kernel<T, D, 1>), tgrid, tblock, 0, st, a); break;
+      case 2:
+        if constexpr (kWideRows) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((attn_token_kernel<T, D, 2>), tgrid, tblock, 0, st, a);
+        break;
+      case 4:
+        if constexpr (kWideRows) return hipErrorInvalidValue;
+        else hipLaunchKernelGGL((attn_token_kernel<T, D, 4>), tgrid, tblock, 0, st, a);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int NS = a.n_split_win + a.n_split_cmp;
   const dim3 grid(tokens * NS);
-  constexpr bool kWideRows = sizeof(T) == 4 && D == 128;  // one chunk per wave only
   switch (a.chunks_per_wave) {
     case 1: hipLaunchKernelGGL((attn_split_kernel<T, D, 1>), grid, dim3(kWaves * 64), 0, st, a); break;
     case 2:
@@ -478,6 +619,33 @@ AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, i
     const long long n = tokens * ((win + rps - 1) / rps + (topk + rps - 1) / rps);
     if (n >= CSA_ATTN_MIN_SPLITS) {
       cpw = c;
+      break;
+    }
+  }
+  // One workgroup per token (no split partials, no second launch) when the
+  // window and Top-K rows fit kTokenMaxWaves waves with the fewest chunks per
+  // wave (4 at most), the step has at most CSA_ATTN_TOKEN_MAX_TOKENS tokens,
+  // and its waves number at least CSA_ATTN_TOKEN_MIN_WAVES (4 per CU).  On a
+  // smaller step the split kernels, with a single chunk per wave and many
+  // more workgroups, have more loads in flight and finish sooner from cold
+  // caches, the second launch included.
+#ifndef CSA_ATTN_TOKEN_MAX_TOKENS
+#define CSA_ATTN_TOKEN_MAX_TOKENS 4096
+#endif
+#ifndef CSA_ATTN_TOKEN_MIN_WAVES
+#define CSA_ATTN_TOKEN_MIN_WAVES 1024
+#endif
+  if (tokens <= CSA_ATTN_TOKEN_MAX_TOKENS) {
+    for (int c : {1, 2, 4}) {
+      if (wide_rows && c > 1) break;
+      const int ww = (win + kChunk * c - 1) / (kChunk * c), wc = (topk + kChunk * c - 1) / (kChunk * c);
+      if (ww + wc > kTokenMaxWaves) continue;
+      if (tokens * (ww + wc) >= CSA_ATTN_TOKEN_MIN_WAVES) {
+        pl.chunks_per_wave = c;
+        pl.waves_win = ww;
+        pl.waves_cmp = wc;
+        return pl;  // no workspace
+      }
       break;
     }
   }

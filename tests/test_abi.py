@@ -178,10 +178,17 @@ def test_attn_refusals(case, code):
     assert call_attn(shape(**case)) == code
 
 
+def split_shape(**kw):
+    """A shape whose window and Top-K rows do not fit one workgroup per token:
+    the split kernels and their workspace."""
+    return shape(topk=1024, **kw)
+
+
 def test_attn_capacity_workspace_alignment():
     sh = shape()
     assert call_attn(sh, rope_rows=1000) == 4            # max_len = 1024 rows needed
-    assert call_attn(sh, ws_bytes=C.sparse_attn_workspace_bytes(sh) - 1) == 6
+    sp = split_shape()
+    assert call_attn(sp, ws_bytes=C.sparse_attn_workspace_bytes(sp) - 1) == 6
     assert call_attn(sh, scale=float("nan")) == 2
     p = [FAKE] * 10
     p[2] = MISALIGNED
@@ -193,7 +200,7 @@ def test_attn_capacity_workspace_alignment():
     p[7] = None                                          # rope table with rope_dim > 0
     assert call_attn(sh, p) == 1
     # no RoPE: NULL tables pass the pointer checks (refused later, for the workspace)
-    assert call_attn(shape(rope_dim=0), [FAKE] * 7 + [None, None, FAKE], ws_bytes=0) == 6
+    assert call_attn(split_shape(rope_dim=0), [FAKE] * 7 + [None, None, FAKE], ws_bytes=0) == 6
 
 
 def call_attn_noalloc(sh, ptrs=None, rope_rows=1 << 20, scale=0.1):
@@ -239,7 +246,11 @@ def test_workspace_queries():
         assert C.topk_workspace_bytes(sh) == 0, cid
         ws = C.sparse_attn_workspace_bytes(sh)
         T = sh.batch * sh.q_per_req
-        assert ws >= T * 2 * sh.heads * (sh.head_dim + 2) * 4     # at least one split per stream
+        if cid == 2:
+            # 128 tokens of 12 waves, one workgroup per token: no partials
+            assert ws == 0, cid
+        else:
+            assert ws >= T * 2 * sh.heads * (sh.head_dim + 2) * 4, cid  # a split per stream at least
     # decode launches over longer rows select in two passes: a candidate slot
     # of a whole chunk per (token, chunk), and counts
     long = I.CONFIGS[4].shape.replace(n_cap=131072, max_len=4 * 131072)
@@ -346,8 +357,9 @@ def test_attn_paged_window_tables_that_fit():
     sh = shape()
     # a window table covering exactly w_cap rows passes the page checks (the
     # call then stops at the missing workspace, before any launch)
-    assert call_attn_paged(sh, pages(), ws_bytes=0, win_pg=pages(bpr=8, bs=16)) == 6
-    assert call_attn_paged(sh, pages(), ws_bytes=0, win_pg=pages(bpr=1, bs=128)) == 6
+    sp = split_shape()
+    assert call_attn_paged(sp, pages(), ws_bytes=0, win_pg=pages(bpr=8, bs=16)) == 6
+    assert call_attn_paged(sp, pages(), ws_bytes=0, win_pg=pages(bpr=1, bs=128)) == 6
 
 
 def test_paged_null_dtype_alignment_workspace():
@@ -366,7 +378,7 @@ def test_paged_null_dtype_alignment_workspace():
     p = [FAKE] * 10
     p[4] = MISALIGNED                                            # v_pool
     assert call_attn_paged(shape(), pages(), p) == 5
-    sh = shape()
+    sh = split_shape()
     assert call_attn_paged(sh, pages(), ws_bytes=C.sparse_attn_workspace_bytes(sh) - 1) == 6
     # the largest pool the 32-bit offsets allow passes the page checks
     assert call_attn_paged(sh, pages(n_blocks=(0x7FFFF000 // (16 * 256))), ws_bytes=0) == 6

@@ -100,6 +100,58 @@ def test_attention_matches_oracle(cid, config_inputs):
     print(f"config {cid}: worst error {worst:.3g}")
 
 
+# Shapes on either side of the one-workgroup-per-token kernel: window and
+# Top-K rows within 12 waves of at most 4 chunks of 16 rows, at most 4096
+# tokens and at least 1024 waves in all take it (no workspace); the rest take
+# the split kernels (4, 2 or 1 chunks per wave).  Random lists of visible rows with duplicates, padding and
+# out-of-range entries; the output must match the oracle and repeat bit for
+# bit.
+ATTN_PATHS = [
+    # split kernels
+    (dict(batch=2, q_per_req=1, win=64, w_cap=64, topk=1024), True),                       # 1 chunk/wave
+    (dict(batch=16, q_per_req=4, win=128, w_cap=131, topk=1024, heads=8, out_groups=2), True),  # 2
+    (dict(batch=32, q_per_req=4, win=256, w_cap=259, topk=800, head_dim=64, rope_dim=32,
+          out_groups=4), True),                                                          # 4
+    (dict(batch=8, q_per_req=8, win=96, w_cap=103, topk=1024, heads=4, head_dim=64, rope_dim=0,
+          dtype=I.F32, idx_dim=64), True),
+    (dict(batch=3, q_per_req=1, win=100, w_cap=100, topk=200, rope_dim=2, dtype=I.F32), True),
+    (dict(batch=4100, q_per_req=1, n_cap=64, max_len=256, win=16, w_cap=16, topk=16, heads=2,
+          head_dim=64, rope_dim=64, idx_heads=1, idx_dim=64), True),                       # tokens
+    (dict(batch=4, q_per_req=2, win=128, w_cap=129, topk=512), True),   # 4 chunks, 80 waves
+    (dict(batch=3, q_per_req=3, win=32, w_cap=34, topk=100, heads=5, head_dim=64), True),  # 81 waves
+    # one workgroup per token
+    (dict(batch=128, q_per_req=2, win=128, w_cap=129, topk=512), False),                   # 4 chunks
+    (dict(batch=256, q_per_req=1, win=64, w_cap=64, topk=256, out_groups=2), False),       # 2
+    (dict(batch=40, q_per_req=3, win=32, w_cap=34, topk=100, heads=5, head_dim=64), False),  # 1
+    (dict(batch=48, q_per_req=2, win=64, w_cap=65, topk=100, rope_dim=32, out_groups=4,
+          dtype=I.F32), False),
+    (dict(batch=64, q_per_req=4, win=200, w_cap=203, topk=300, heads=3, head_dim=64, rope_dim=16,
+          out_groups=3, dtype=I.F32, idx_dim=64), False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ATTN_PATHS)))
+def test_attention_split_and_token_paths(case):
+    kw, split = ATTN_PATHS[case]
+    cfg = small_cfg(name="paths", seed=40 + case, **kw)
+    sh = cfg.shape
+    assert (C.sparse_attn_workspace_bytes(sh) > 0) == split
+    inp = I.make_inputs(cfg)
+    g = np.random.default_rng(400 + case)
+    B, S, K = sh.batch, sh.q_per_req, sh.topk
+    p = inp["start_pos"].astype(np.int64)[:, None] + np.arange(S)[None, :]
+    nv = np.minimum((p + 1) // sh.ratio, sh.n_cap)[..., None]
+    ti = (g.random((B, S, K)) * nv).astype(np.int32)            # visible rows, repeats allowed
+    pad = (g.random((B, S, K)) < 0.1) | (nv == 0)
+    ti = np.where(pad, g.choice(np.int32([-3, -1, sh.n_cap, sh.n_cap + 2]), size=(B, S, K)), ti)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=ti)
+    got = gpu_step(sh, inp, topk_idx=ti, jobs=("attn",))
+    worst = U.compare_outputs(sh, got["out"], ref["out"])
+    again = gpu_step(sh, inp, topk_idx=ti, jobs=("attn",))
+    assert np.array_equal(got["out"], again["out"])
+    print(f"case {case} ({'split' if split else 'token'}): worst error {worst:.3g}")
+
+
 # --------------------------------------------------------------------------
 # indexer scores
 # --------------------------------------------------------------------------
@@ -844,8 +896,11 @@ def test_binding_refuses_short_or_mistyped_tensors():
 
 
 def test_refused_call_leaves_outputs_untouched():
-    cfg = small_cfg(batch=2, q_per_req=1)
+    # K = 1024 rows do not fit one workgroup per token: the split kernels and
+    # their workspace
+    cfg = small_cfg(batch=2, q_per_req=1, topk=1024)
     sh = cfg.shape
+    assert C.sparse_attn_workspace_bytes(sh) > 16
     inp = I.make_inputs(cfg)
     d = C.to_device(inp, sh)
     bufs = C.alloc_outputs(sh)

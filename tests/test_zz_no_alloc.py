@@ -2,9 +2,10 @@
 
 csa_sparse_attn_decode_noalloc keeps its split partials in the library's
 static device array instead of a caller workspace; it runs the same kernels,
-so its output must equal csa_sparse_attn_decode's bit for bit.  Two calls in a
-row, the second on a smaller input (the array keeps the first call's
-partials), then the first shape again.
+so its output must equal csa_sparse_attn_decode's bit for bit.  Calls in a
+row: the second on a smaller input (the array keeps the first call's
+partials), a third on a shape that needs no partials, then the first shape
+again.
 """
 import numpy as np
 import pytest
@@ -18,9 +19,10 @@ from tests import _util as U
 pytestmark = pytest.mark.gpu
 
 
-def _case(cid):
+def _case(cid, **kw):
     cfg = I.CONFIGS[cid]
-    sh, inp = cfg.shape, I.make_inputs(cid)
+    sh = cfg.shape.replace(**kw)
+    inp = I.make_inputs(cid, shape=sh)
     jobs = oracle.JOB_ATTN if cfg.supplied_topk else oracle.JOB_SCORE | oracle.JOB_TOPK | oracle.JOB_ATTN
     ref = oracle.run(sh, inp, jobs=jobs, nthreads=8)
     d = C.to_device(inp, sh)
@@ -42,10 +44,12 @@ def _both(sh, d):
 
 def test_noalloc_equals_workspace_entry_point():
     assert torch.cuda.is_available()
-    big = _case(4)      # 128 tokens, 5 splits each
-    small = _case(3)    # 16 tokens, 10 splits each
-    assert C.sparse_attn_workspace_bytes(big[0]) > C.sparse_attn_workspace_bytes(small[0])
-    for sh, d, ref in (big, small, big):
+    big = _case(4)              # 128 tokens, 5 splits each
+    small = _case(4, batch=8)   # 16 tokens, 20 splits each (one chunk per wave)
+    token = _case(2)            # one workgroup per token: no partials at all
+    assert C.sparse_attn_workspace_bytes(big[0]) > C.sparse_attn_workspace_bytes(small[0]) > 0
+    assert C.sparse_attn_workspace_bytes(token[0]) == 0
+    for sh, d, ref in (big, small, token, big):
         want, got = _both(sh, d)
         assert np.array_equal(got, want), "no-alloc output differs from the workspace entry point"
         U.compare_outputs(sh, got, ref["out"])
