@@ -219,7 +219,7 @@ csa_status_t csa_topk(const csa_shape_t* shape, const float* scores, const int32
 /* Workspace bytes csa_sparse_attn_decode needs for this shape (split
  * partials).  0 for shapes that a single workgroup per token finishes by
  * itself: window and Top-K rows within 12 waves of at most 64 rows each
- * (fp32 rows of 128 dims: 16 rows), at most 4096 tokens, and at least 1024
+ * (fp32 rows of 128 dims: 16 rows), at most 4096 tokens, and at least 384
  * such waves in all.  Its contents need no initialisation; calls that overlap
  * in time must not share a workspace. */
 size_t csa_sparse_attn_workspace_bytes(const csa_shape_t* shape);

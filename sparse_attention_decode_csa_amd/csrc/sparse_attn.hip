@@ -461,6 +461,30 @@ __global__ __launch_bounds__(kFinishThreads) void attn_finish_kernel(AttnArgs a)
   finish_item<T, D, MB>(a, tok, item);
 }
 
+// Maximum and sum over each 16-lane row of the wave with DPP moves (quad
+// swaps, then half-row and row mirrors); every lane of the row ends with the
+// same bits.
+__device__ __forceinline__ float dpp_f(float x, int ctrl) {
+  switch (ctrl) {  // the control must be a constant
+    case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
+    case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));
+    case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));
+  }
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f(x, 0x141));  // row_half_mirror
+  return fmaxf(x, dpp_f(x, 0x140));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f(x, 0xB1);
+  x += dpp_f(x, 0x4E);
+  x += dpp_f(x, 0x141);
+  return x + dpp_f(x, 0x140);
+}
+
 // LDS DMA of 4 bytes per lane to lds + 4 * lane (wave 0 of the workgroup).
 __device__ __forceinline__ void dma4_global(const float* src, float* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
@@ -517,41 +541,45 @@ __global__ __launch_bounds__(kTokenMaxWaves * 64) void attn_token_kernel(AttnArg
     wml[wave][n16][1] = l_tot;
   }
   __syncthreads();  // also waits for every wave's outstanding loads, the RoPE copy included
-  if (tid < nw * 16) {  // output factor of wave v for head h
-    const int v = tid >> 4, h = tid & 15;
-    float Mw = -INFINITY, Mc = -INFINITY;
-    for (int u = 0; u < nw; ++u) {
-      if (u < WW) Mw = fmaxf(Mw, wml[u][h][0]);
-      else Mc = fmaxf(Mc, wml[u][h][0]);
-    }
-    float Lw = 0.0f, Lc = 0.0f;
-    for (int u = 0; u < nw; ++u) {
-      const float l = wml[u][h][1];
-      if (!(l > 0.0f)) continue;  // a wave that saw no row carries no weight
-      if (u < WW) Lw += exp2f(wml[u][h][0] - Mw) * l;
-      else Lc += exp2f(wml[u][h][0] - Mc) * l;
-    }
+  // Output factor of wave u for head h.  Lanes 16j .. 16j+15 of a wave hold
+  // waves 0 .. 15 of head 4*hg + j, so each stream's max and sum over its
+  // waves are 16-lane reductions in registers (fixed pattern: every lane of
+  // the row gets the same bits).
+  for (int hg = wave; hg < 4; hg += nw) {  // wave-uniform
+    const int h = 4 * hg + (lane >> 4), u = lane & 15;
+    const bool live = u < nw, uw = u < WW;
+    const float m = live ? wml[u][h][0] : -INFINITY;
+    const float l = live ? wml[u][h][1] : 0.0f;
+    const float Mw = row16_max(uw ? m : -INFINITY);
+    const float Mc = row16_max(uw ? -INFINITY : m);
+    const float f = l > 0.0f ? exp2f(m - (uw ? Mw : Mc)) : 0.0f;  // a wave that saw no row weighs nothing
+    const float Lw = row16_sum(uw ? f * l : 0.0f);
+    const float Lc = row16_sum(uw ? 0.0f : f * l);
     // stream merge: an empty stream (sum 0) carries no weight
     const float M = fmaxf(Mw, Mc);
     const float fw = Lw > 0.0f ? exp2f(Mw - M) : 0.0f;
     const float fc = Lc > 0.0f ? exp2f(Mc - M) : 0.0f;
     const float inv = 1.0f / (fw * Lw + fc * Lc);
-    const float l = wml[v][h][1];
-    wfac[v][h] = l > 0.0f ? exp2f(wml[v][h][0] - (v < WW ? Mw : Mc)) * (v < WW ? fw : fc) * inv : 0.0f;
+    if (live) wfac[u][h] = f * (uw ? fw : fc) * inv;
   }
   __syncthreads();
   const int r0 = D - a.rope_dim;
-  for (int item = tid; item < H * (D / 2); item += nw * 64) {
-    const int h = item / (D / 2), d = 2 * (item - h * (D / 2));
-    float x = 0.0f, y = 0.0f;
-    for (int v = 0; v < nw; ++v) {
+  for (int item = tid; item < H * (D / 4); item += nw * 64) {  // 4 dims per item
+    const int h = item / (D / 4), d = 4 * (item - h * (D / 4));
+    f32x4_t o4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // every slot read at once (slots past nw hold no wave and are skipped)
+#pragma unroll
+    for (int v = 0; v < kTokenMaxWaves; ++v) {
       const float f = wfac[v][h];
-      const float2 o = *reinterpret_cast<const float2*>(&mo[(v * 16 + h) * G::MO_STRIDE + d]);
-      x += f * o.x;
-      y += f * o.y;
+      const f32x4_t o = *reinterpret_cast<const f32x4_t*>(&mo[(v * 16 + h) * G::MO_STRIDE + d]);
+      if (v < nw) o4 += f * o;
     }
-    const int i = (d - r0) >> 1;
-    store_pair<T, D>(a, tok, h, d, x, y, d >= r0 ? rope_cs[i] : 1.0f, d >= r0 ? rope_sn[i] : 0.0f);
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const int i = (d + e - r0) >> 1;
+      const bool rot = d + e >= r0;
+      store_pair<T, D>(a, tok, h, d + e, o4[e], o4[e + 1], rot ? rope_cs[i] : 1.0f, rot ? rope_sn[i] : 0.0f);
+    }
   }
 }
 
@@ -625,7 +653,7 @@ AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, i
   // One workgroup per token (no split partials, no second launch) when the
   // window and Top-K rows fit kTokenMaxWaves waves with the fewest chunks per
   // wave (4 at most), the step has at most CSA_ATTN_TOKEN_MAX_TOKENS tokens,
-  // and its waves number at least CSA_ATTN_TOKEN_MIN_WAVES (4 per CU).  On a
+  // and its waves number at least CSA_ATTN_TOKEN_MIN_WAVES (1.5 per CU).  On a
   // smaller step the split kernels, with a single chunk per wave and many
   // more workgroups, have more loads in flight and finish sooner from cold
   // caches, the second launch included.
@@ -633,7 +661,7 @@ AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, i
 #define CSA_ATTN_TOKEN_MAX_TOKENS 4096
 #endif
 #ifndef CSA_ATTN_TOKEN_MIN_WAVES
-#define CSA_ATTN_TOKEN_MIN_WAVES 1024
+#define CSA_ATTN_TOKEN_MIN_WAVES 384
 #endif
   if (tokens <= CSA_ATTN_TOKEN_MAX_TOKENS) {
     for (int c : {1, 2, 4}) {

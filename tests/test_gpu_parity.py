@@ -102,7 +102,7 @@ def test_attention_matches_oracle(cid, config_inputs):
 
 # Shapes on either side of the one-workgroup-per-token kernel: window and
 # Top-K rows within 12 waves of at most 4 chunks of 16 rows, at most 4096
-# tokens and at least 1024 waves in all take it (no workspace); the rest take
+# tokens and at least 384 waves in all take it (no workspace); the rest take
 # the split kernels (4, 2 or 1 chunks per wave).  Random lists of visible rows with duplicates, padding and
 # out-of-range entries; the output must match the oracle and repeat bit for
 # bit.
