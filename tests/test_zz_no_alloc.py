@@ -45,7 +45,7 @@ def _both(sh, d):
 def test_noalloc_equals_workspace_entry_point():
     assert torch.cuda.is_available()
     big = _case(4)              # 128 tokens, 5 splits each
-    small = _case(4, batch=8)   # 16 tokens, 20 splits each (one chunk per wave)
+    small = _case(4, batch=8)   # 16 tokens, 5 splits each
     token = _case(2)            # one workgroup per token: no partials at all
     assert C.sparse_attn_workspace_bytes(big[0]) > C.sparse_attn_workspace_bytes(small[0]) > 0
     assert C.sparse_attn_workspace_bytes(token[0]) == 0
