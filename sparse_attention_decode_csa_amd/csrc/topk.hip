@@ -518,16 +518,15 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
       key[j + 3] = order_key(v.w);
     }
     if (i0 + KPT > n) {  // the one thread straddling n
-      const uint32_t last = i0 < n ? key[0] : order_key(row[n - 1]);
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) key[j] = i0 + j < n ? key[j] : last;
+      for (int j = 0; j < KPT; ++j) key[j] = i0 + j < n ? key[j] : 0u;
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = order_key(row[min(i0 + j, n - 1)]);
+    for (int j = 0; j < KPT; ++j) key[j] = i0 + j < n ? order_key(row[i0 + j]) : 0u;
   }
   auto valid = [&](int j) { return i0 + j < n; };
-  uint32_t kmax = key[0];  // slots past n copy a valid key, so they never raise it
+  uint32_t kmax = key[0];  // slots past n hold key 0, below every float's key: they never raise it
 #pragma unroll
   for (int j = 1; j < KPT; ++j) kmax = max(kmax, key[j]);
 
@@ -576,9 +575,12 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
                                              ks, 0u, 0xFFFFFFFFu, sm, tau, unused, 2);
     // ---- rows at or above the threshold, compacted in row order; the same
     // barriers give the row maximum
+    // slots past n hold key 0, and no float has key 0: against a threshold of
+    // at least 1 they need no separate test
+    tau = max(tau, 1u);
     int mine = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) mine += (valid(j) && key[j] >= tau) ? 1 : 0;
+    for (int j = 0; j < KPT; ++j) mine += key[j] >= tau ? 1 : 0;
     int c;
     uint32_t row_max;
     int pos = block_exclusive_scan_max<NW>(mine, kmax, sm.red, c, row_max);
@@ -587,7 +589,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
       // every slot with the misses sent to a spare slot)
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        const bool hit = valid(j) && key[j] >= tau;
+        const bool hit = key[j] >= tau;
         if (hit) cand[pos] = make_uint2(key[j], (uint32_t)(i0 + j));
         pos += hit ? 1 : 0;
       }
@@ -608,9 +610,9 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
     }
   }
   // ---- whole-row selection and emission
-  uint32_t kmin = key[0];
+  uint32_t kmin = 0xFFFFFFFFu;
 #pragma unroll
-  for (int j = 1; j < KPT; ++j) kmin = min(kmin, key[j]);
+  for (int j = 0; j < KPT; ++j) kmin = min(kmin, valid(j) ? key[j] : 0xFFFFFFFFu);
   uint32_t row_min, row_max;
   block_min_max<NW>(kmin, kmax, sm.red, row_min, row_max);
   uint32_t T;
