@@ -7,22 +7,28 @@ from __future__ import annotations
 
 import json
 import os
+import warnings
 
 import numpy as np
 
 from sparse_attention_decode_csa_amd import inputs as I
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-RECORD = os.path.join(ROOT, "gpurun_out", "parity_record.jsonl")
+
+class ParityRecord(UserWarning):
+    """Figures of a passing parity test (boundary-exemption counts and the
+    like), shown in pytest's warnings summary even in a quiet run."""
 
 
 def record(test: str, **data):
-    """Append one JSON line (test name + figures such as boundary-exemption
-    counts) to gpurun_out/parity_record.jsonl, next to the run's logs, so the
-    figures of a passing run stay visible."""
-    os.makedirs(os.path.dirname(RECORD), exist_ok=True)
-    with open(RECORD, "a") as f:
-        f.write(json.dumps(dict(test=test, **data), default=int) + "\n")
+    """Report one test's figures: as a ParityRecord warning, and appended as
+    one JSON line to the file named by CSA_PARITY_RECORD when that is set."""
+    line = json.dumps(dict(test=test, **data), default=int)
+    warnings.warn(line, ParityRecord, stacklevel=2)
+    path = os.environ.get("CSA_PARITY_RECORD")
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(line + "\n")
 
 # max-abs tolerance for bf16 outputs with fp32 accumulation
 BF16_ATOL = 2e-2
