@@ -494,10 +494,11 @@ __device__ __forceinline__ void dma4_global(const float* src, float* lds) {
 // Top-K rows fit 12 waves of at most 4 chunks: waves [0, WW) walk the window,
 // waves [WW, WW + WC) the Top-K list, each as one split wave does.  Their
 // states meet in LDS and the workgroup finishes the token itself: per head,
-// each stream's max and sum over its waves in fixed wave order, the stream
-// merge, then per output pair the factor-weighted sum over the waves in fixed
-// order, the inverse RoPE, one rounding and the packed store.  No partials
-// leave the workgroup and there is no second launch.
+// each stream's max and sum over its waves (register reductions of a fixed
+// pattern), the stream merge and each wave's output factor; then per 4 output
+// dims the factor-weighted sum over the waves in fixed order, the inverse
+// RoPE, one rounding and the packed store.  No partials leave the workgroup
+// and there is no second launch.
 template <typename T, int D, int CPW>
 __global__ __launch_bounds__(kTokenMaxWaves * 64) void attn_token_kernel(AttnArgs a) {
   using G = AttnGeo<T, D>;
@@ -576,8 +577,8 @@ __global__ __launch_bounds__(kTokenMaxWaves * 64) void attn_token_kernel(AttnArg
     }
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
-      const int i = (d + e - r0) >> 1;
       const bool rot = d + e >= r0;
+      const int i = rot ? (d + e - r0) >> 1 : 0;
       store_pair<T, D>(a, tok, h, d + e, o4[e], o4[e + 1], rot ? rope_cs[i] : 1.0f, rot ? rope_sn[i] : 0.0f);
     }
   }
