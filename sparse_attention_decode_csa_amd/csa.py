@@ -13,6 +13,7 @@ step(), which issues the three calls in order on one stream.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -47,7 +48,16 @@ class CShape(ctypes.Structure):
 
     @classmethod
     def of(cls, shape) -> "CShape":
+        """The C struct of a shape (for a Shape, one struct per distinct shape,
+        reused across calls: the library only reads it)."""
+        if isinstance(shape, Shape):
+            return _cshape_cached(shape)
         return cls(*[int(getattr(shape, f)) for f in _FIELDS])
+
+
+@functools.lru_cache(maxsize=256)
+def _cshape_cached(shape: Shape) -> CShape:
+    return CShape(*[int(getattr(shape, f)) for f in _FIELDS])
 
 
 class CPages(ctypes.Structure):
@@ -151,7 +161,12 @@ def _dev(t: Optional[torch.Tensor], name: str, numel: Optional[int] = None,
 
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        # the current stream's raw handle without building a Stream object
+        # (several microseconds per call otherwise)
+        try:
+            return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
+        except AttributeError:
+            stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -169,6 +184,17 @@ def sparse_attn_workspace_bytes(shape) -> int:
 
 def _sizes(shape) -> dict:
     """Element counts the shape implies for each tensor of the step."""
+    if isinstance(shape, Shape):
+        return _sizes_cached(shape)
+    return _sizes_of(shape)
+
+
+@functools.lru_cache(maxsize=256)
+def _sizes_cached(shape: Shape) -> dict:
+    return _sizes_of(shape)
+
+
+def _sizes_of(shape) -> dict:
     B, S, Hi, Di = shape.batch, shape.q_per_req, shape.idx_heads, shape.idx_dim
     return dict(q_idx=B * S * Hi * Di, w=B * S * Hi, k_idx=B * shape.n_cap * Di, start_pos=B,
                 scores=B * S * shape.n_cap, topk_idx=B * S * shape.topk,
