@@ -76,7 +76,7 @@ typedef enum {
 typedef enum { CSA_DTYPE_F32 = 0, CSA_DTYPE_BF16 = 1 } csa_dtype_t;
 
 /* Sizes of one decode step.  Supported ranges (CSA_ERR_UNSUPPORTED outside):
- *   head_dim, idx_dim in {64, 128}; 1 <= heads <= 16; 1 <= idx_heads <= 64;
+ *   head_dim, idx_dim in {64, 128}; 1 <= heads <= 64; 1 <= idx_heads <= 64;
  *   1 <= topk <= 4096; win >= 1.  Scoring and Top-K take any q_per_req: a
  *   prefill chunk of T tokens per request is q_per_req = T (the prefill
  *   indexer of "Fix: port the DeepSeek-V4 MoE, hc_pre and prefill fixes to

@@ -193,7 +193,7 @@ static csa_status_t attn_decode(const csa_shape_t* sh, const void* q, const void
     return CSA_ERR_BAD_SHAPE;
   if (!std::isfinite(softmax_scale)) return CSA_ERR_BAD_SHAPE;
   if (sh->head_dim != 64 && sh->head_dim != 128) return CSA_ERR_UNSUPPORTED;
-  if (sh->heads > 16) return CSA_ERR_UNSUPPORTED;
+  if (sh->heads > 64) return CSA_ERR_UNSUPPORTED;
   if ((int64_t)sh->w_cap < (int64_t)sh->win + sh->q_per_req - 1) return CSA_ERR_CAPACITY;
   if (sh->rope_dim > 0 && rope_rows < sh->max_len) return CSA_ERR_CAPACITY;
   {  // one request's cache slice is addressed with 32-bit byte offsets

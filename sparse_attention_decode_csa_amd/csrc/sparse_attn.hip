@@ -183,17 +183,18 @@ __device__ __forceinline__ void store_pair(const AttnArgs& a, int tok, int h, in
   }
 }
 
-// B operand of logits^T: q^T of token tok, column = head n16 (zero for
-// padded heads).  Depends on nothing else, so it is issued first.
+// B operand of logits^T: q^T of token tok, column n16 = head h0 + n16 (zero
+// for padded heads).  Depends on nothing else, so it is issued first.
 template <typename T, int D>
-__device__ __forceinline__ void load_query(const AttnArgs& a, int tok, int n16, int g,
+__device__ __forceinline__ void load_query(const AttnArgs& a, int tok, int h0, int n16, int g,
                                            u32x4_t (&qf)[AttnGeo<T, D>::CH]) {
   using G = AttnGeo<T, D>;
-  const char* qp = static_cast<const char*>(a.q) + ((size_t)tok * a.heads + min(n16, a.heads - 1)) * G::ROW + g * 16;
+  const int h = h0 + n16;  // this lane's head of the group of 16 starting at h0
+  const char* qp = static_cast<const char*>(a.q) + ((size_t)tok * a.heads + min(h, a.heads - 1)) * G::ROW + g * 16;
 #pragma unroll
   for (int c = 0; c < G::CH; ++c) {
     const u32x4_t v = ld16(qp + c * 64);
-    qf[c] = n16 < a.heads ? v : u32x4_t{0, 0, 0, 0};
+    qf[c] = h < a.heads ? v : u32x4_t{0, 0, 0, 0};
   }
 }
 
@@ -393,20 +394,24 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
   const int n16 = lane & 15, g = lane >> 4;
   const int S = a.q_per_req, H = a.heads;
   const int NSW = a.n_split_win, NS = a.n_split_win + a.n_split_cmp;
+  const int NHG = (H + 15) >> 4;  // groups of 16 heads
 
-  // logical block order (b, split, s): the S tokens of a request that read the
-  // same window rows are neighbours, hence on the same XCD and its L2.
+  // logical block order (b, split, s, head group): the head groups of one
+  // (token, split) read the same rows and the S tokens of a request the same
+  // window rows; neighbours share an XCD and its L2.
   const int logical = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int s = logical % S;
-  const int split = (logical / S) % NS;
-  const int b = logical / (S * NS);
+  const int hg = logical % NHG;
+  const int s = (logical / NHG) % S;
+  const int split = (logical / (NHG * S)) % NS;
+  const int b = logical / (NHG * S * NS);
   const int tok = b * S + s;
   const bool win = split < NSW;
-  float* ml_out = a.ws_ml + ((size_t)tok * NS + split) * H * 2;
-  float* o_out = a.ws_o + ((size_t)tok * NS + split) * H * D;
+  const int h0 = hg * 16, HL = min(16, H - h0);  // this group's heads
+  float* ml_out = a.ws_ml + (((size_t)tok * NS + split) * H + h0) * 2;
+  float* o_out = a.ws_o + (((size_t)tok * NS + split) * H + h0) * D;
 
   u32x4_t qf[G::CH];
-  load_query<T, D>(a, tok, n16, g, qf);
+  load_query<T, D>(a, tok, h0, n16, g, qf);
   f32x4_t acc[G::DT];
   float m_run, l_tot;
   const int e_lo = (win ? split : split - NSW) * RPS + wave * RPW;
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) M = fmaxf(M, wml[v][h][0]);
     wfac[w][h] = wml[w][h][1] > 0.0f ? exp2f(wml[w][h][0] - M) : 0.0f;
-    if (w == 0 && h < H) {
+    if (w == 0 && h < HL) {
       float Lsum = 0.0f;
 #pragma unroll
       for (int v = 0; v < kWaves; ++v) {
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void attn_split_kernel(AttnArgs a) 
     }
   }
   __syncthreads();
-  for (int item = tid; item < H * D; item += kWaves * 64) {
+  for (int item = tid; item < HL * D; item += kWaves * 64) {
     const int h = item / D, d = item - h * D;
     float o = 0.0f;
 #pragma unroll
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(kTokenMaxWaves * 64) void attn_token_kernel(AttnArg
   const bool win = wave < WW;
 
   u32x4_t qf[G::CH];
-  load_query<T, D>(a, tok, n16, g, qf);
+  load_query<T, D>(a, tok, 0, n16, g, qf);  // at most 16 heads
   // the position's RoPE row, copied straight into LDS (no registers held
   // across the gather); the barrier before the merge waits for it
   const int half = a.rope_dim >> 1;
@@ -605,7 +610,7 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const int NS = a.n_split_win + a.n_split_cmp;
-  const dim3 grid(tokens * NS);
+  const dim3 grid(tokens * NS * ((a.heads + 15) / 16));
   switch (a.chunks_per_wave) {
     case 1: hipLaunchKernelGGL((attn_split_kernel<T, D, 1>), grid, dim3(kWaves * 64), 0, st, a); break;
     case 2:
@@ -668,7 +673,7 @@ AttnPlan attn_plan(int batch, int q_per_req, int heads, int head_dim, int win, i
 #ifndef CSA_ATTN_TOKEN_MIN_WAVES
 #define CSA_ATTN_TOKEN_MIN_WAVES 384
 #endif
-  if (tokens <= CSA_ATTN_TOKEN_MAX_TOKENS) {
+  if (tokens <= CSA_ATTN_TOKEN_MAX_TOKENS && heads <= 16) {
     for (int c : {1, 2, 4}) {
       if (wide_rows && c > 1) break;
       const int ww = (win + kChunk * c - 1) / (kChunk * c), wc = (topk + kChunk * c - 1) / (kChunk * c);

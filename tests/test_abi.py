@@ -167,7 +167,7 @@ def test_topk_workspace_refusals():
 
 @pytest.mark.parametrize("case,code", [
     (dict(head_dim=96, rope_dim=32), 8),
-    (dict(heads=32), 8),
+    (dict(heads=65), 8),
     (dict(rope_dim=63), 2),
     (dict(rope_dim=256), 2),
     (dict(heads=16, out_groups=3), 2),
@@ -218,7 +218,7 @@ def test_attn_noalloc_refusals():
     assert C.sparse_attn_workspace_bytes(sh) <= cap
     assert call_attn_noalloc(sh, rope_rows=1000) == 4
     assert call_attn_noalloc(shape(w_cap=127)) == 4
-    assert call_attn_noalloc(shape(heads=17)) == 8
+    assert call_attn_noalloc(shape(heads=65)) == 8
     assert call_attn_noalloc(sh, scale=float("inf")) == 2
     p = [FAKE] * 10
     p[9] = MISALIGNED

@@ -117,6 +117,14 @@ ATTN_PATHS = [
     (dict(batch=3, q_per_req=1, win=100, w_cap=100, topk=200, rope_dim=2, dtype=I.F32), True),
     (dict(batch=4100, q_per_req=1, n_cap=64, max_len=256, win=16, w_cap=16, topk=16, heads=2,
           head_dim=64, rope_dim=64, idx_heads=1, idx_dim=64), True),                       # tokens
+    # more than 16 query heads: one split workgroup per group of 16 heads
+    (dict(batch=4, q_per_req=2, heads=64, out_groups=4, win=64, w_cap=65, topk=256), True),
+    (dict(batch=3, q_per_req=1, heads=20, out_groups=5, head_dim=64, rope_dim=32, win=100,
+          w_cap=100, topk=300), True),
+    (dict(batch=2, q_per_req=3, heads=48, out_groups=3, dtype=I.F32, win=40, w_cap=42, topk=128),
+     True),
+    (dict(batch=2, q_per_req=2, heads=32, head_dim=64, rope_dim=0, dtype=I.F32, win=64, w_cap=65,
+          topk=64, idx_dim=64), True),
     (dict(batch=4, q_per_req=2, win=128, w_cap=129, topk=512), True),   # 4 chunks, 80 waves
     (dict(batch=3, q_per_req=3, win=32, w_cap=34, topk=100, heads=5, head_dim=64), True),  # 81 waves
     # one workgroup per token
@@ -336,6 +344,28 @@ def test_end_to_end_paged(fmt, bs, win):
                                inp["start_pos"])
     print(f"paged {fmt} block {bs}: {len(exempt)} boundary exemptions {exempt}")
     assert len(exempt) <= max(1, sh.batch * sh.q_per_req // 32)
+    ex = {b * sh.q_per_req + s for (b, s, _) in exempt}
+    keep = [t for t in range(sh.batch * sh.q_per_req) if t not in ex]
+    U.compare_outputs(sh, got["out"], ref["out"], tokens=keep)
+
+
+@pytest.mark.parametrize("heads,groups,bs", [(64, 4, 32), (32, 1, 16)])
+def test_end_to_end_paged_many_heads(heads, groups, bs):
+    # the whole step with 32 or 64 query heads (split workgroups per group of
+    # 16 heads) over paged caches, against the oracle over the gathered caches
+    cfg = small_cfg(name="heads", seed=31 + heads, batch=4, q_per_req=2, heads=heads,
+                    out_groups=groups, n_cap=512, max_len=2048, topk=128, win=64, w_cap=80,
+                    lengths="start_uniform:800:2046")
+    sh = cfg.shape
+    dense = I.make_inputs(cfg)
+    inp = I.page_inputs(dense, bs, seed=heads, win=True)
+    ref = oracle.run_paged(sh, inp, nthreads=NTHREADS)
+    got = gpu_step(sh, inp)
+    rows = U.token_rows(sh, inp["start_pos"])
+    bound = U.score_error_bound(sh, dense, rows)
+    exempt = U.topk_exemptions(sh, got["topk_idx"], ref["topk_idx"], ref["scores"], bound,
+                               inp["start_pos"])
+    assert len(exempt) <= 1, exempt
     ex = {b * sh.q_per_req + s for (b, s, _) in exempt}
     keep = [t for t in range(sh.batch * sh.q_per_req) if t not in ex]
     U.compare_outputs(sh, got["out"], ref["out"], tokens=keep)
