@@ -3,7 +3,9 @@
     python -m sparse_attention_decode_csa_amd.build
 
 Each .hip source is compiled to an object in parallel, then linked into
-sparse_attention_decode_csa_amd/libcsa.so next to this file.
+sparse_attention_decode_csa_amd/libcsa.so next to this file.  The memory
+ceiling probes (csrc/ceilings.hip, include/csa_ceilings.h) are linked into a
+library of their own, libcsa_ceilings.so, which the decode path never loads.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcsa.so")
+CEILINGS_LIB = os.path.join(PKG, "libcsa_ceilings.so")
+CEILINGS_SOURCES = ["ceilings.hip"]
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "indexer_score.hip", "topk.hip", "sparse_attn.hip", "swa_writeback.hip"]
 
@@ -40,11 +44,19 @@ def _compile(src: str, obj_dir: str = OBJ_DIR, defines=()) -> str:
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile and link; `defines` override tuning constants (e.g. for sweeps)."""
+    """Compile and link; `defines` override tuning constants (e.g. for sweeps).
+    The default build also links the ceiling probes' library."""
     obj_dir = OBJ_DIR if out == LIB else out + ".objs"
     os.makedirs(obj_dir, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, obj_dir, defines), SOURCES))
+    _link(SOURCES, out, obj_dir, defines, verbose)
+    if out == LIB:
+        _link(CEILINGS_SOURCES, CEILINGS_LIB, obj_dir, (), verbose)
+    return out
+
+
+def _link(sources, out: str, obj_dir: str, defines, verbose: bool) -> None:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, defines), sources))
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,7 +73,6 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     os.replace(tmp, out)
     if verbose:
         print(f"built {out}")
-    return out
 
 
 if __name__ == "__main__":
