@@ -1,25 +1,27 @@
 """Memory-system ceilings beside the decode step's kernels, on one MI355X.
 
-    python bench_ceilings.py [--reps 40] [--flush-mib 1024]
+    python bench_ceilings.py [--config 4|3] [--reps 40] [--flush-mib 1024]
 
-On the wide Top-K workload (64 requests x 2 query tokens, 32768 compressed
-rows of 256 bytes per request, K = 1024, window 256), this times, flushed
+On the wide Top-K workload (config 4, the default: 64 requests x 2 query
+tokens, 32768 compressed rows of 256 bytes per request, K = 1024, window 256)
+or the long-context one (config 3: 16 requests x 1 token, 8192-16384 visible
+rows, K = 512, window 128), this times, flushed
 (1 GiB written and 512 MiB read before every launch, outside its events) and
 hot (no flush; a GPU spin that touches no memory runs before each launch, so
 that the host's launch overhead stays outside the events):
 
-- the library's indexer score kernel, and probes that read the same 512 MiB
-  key stream and compute nothing: the score kernel's own LDS-DMA stream in
-  address order and with 16 KiB pages in a random order, and plain 16-byte
-  vector loads, one contiguous range per workgroup;
+- the library's indexer score kernel, and probes that read the key pages it
+  reads (the visible rows) and compute nothing: the score kernel's own LDS-DMA
+  stream in address order and with the pages in a random order, and plain
+  16-byte vector loads of as many bytes, one contiguous range per workgroup;
 - the paged score kernel over a pool of 64-row blocks in a seeded random
-  order, and the LDS-DMA stream reading that pool through the same table;
+  order, and the LDS-DMA stream reading the same pages through the same table;
 - the library's Top-K kernel right after the score kernel (untimed) wrote its
-  rows, and probes that only read those rows, one or 8 workgroups per row;
-- the library's attention (split kernel + finish kernel, as the decode step
-  launches it), and a probe that gathers exactly its K and V rows (the step's
-  own Top-K lists plus the window rows) 4 rows per wave and computes nothing,
-  next to a sequential read of as many bytes.
+  rows, and probes that only read those rows (whole rows), one or 8
+  workgroups per row;
+- the library's attention call, and a probe that gathers exactly its K and V
+  rows (the step's own Top-K lists plus the window rows) 4 rows per wave and
+  computes nothing, next to a sequential read of as many bytes.
 
 The probes live in libcsa_ceilings.so (csrc/ceilings.hip); the decode path
 never loads that library.  Prints one JSON line per measurement and a last
@@ -42,7 +44,7 @@ CEILINGS_LIB = os.path.join(ROOT, "sparse_attention_decode_csa_amd", "libcsa_cei
 DMA_WG_BYTES = 131072
 DMA_PAGE_BYTES = 16384
 ROW_BYTES = 256
-WORKLOAD = 4  # the wide Top-K configuration
+WORKLOADS = (4, 3)  # wide Top-K (the default), long context
 SPIN_CYCLES = 400_000  # a GPU spin of about 0.2 ms before each hot launch
 PAGE_ROWS = 64         # rows per block of the paged key pool (16 KiB of bf16 keys)
 
@@ -64,6 +66,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=40, help="timed launches per measurement and cache state")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--config", type=int, choices=WORKLOADS, default=WORKLOADS[0])
     args = ap.parse_args()
 
     import torch
@@ -75,9 +78,9 @@ def main():
         sys.exit(3)
     C.lib()
     P = load_ceilings()
-    cfg = I.CONFIGS[WORKLOAD]
+    cfg = I.CONFIGS[args.config]
     sh = cfg.shape
-    inp = I.make_inputs(WORKLOAD)
+    inp = I.make_inputs(args.config)
     dev = C.to_device(inp, sh)
     bufs = C.alloc_outputs(sh)
     scale = I.softmax_scale(sh)
@@ -134,38 +137,63 @@ def main():
         if code != 0:
             raise RuntimeError(f"{what} refused or failed ({code})")
 
-    # ---- the key stream ---------------------------------------------------
+    # ---- the key stream: the 16 KiB pages holding the rows the score kernel
+    # reads (each request's visible rows, up to the most any of its tokens
+    # that do not fit Top-K sees), padded to whole probe workgroups
     keys = dev["k_idx"]
-    kbytes = keys.numel() * keys.element_size()
-    assert kbytes % DMA_WG_BYTES == 0
-    n_pages = kbytes // DMA_PAGE_BYTES
-    order = torch.from_numpy(np.random.default_rng(5).permutation(n_pages).astype(np.int32)).cuda()
+    B, S = sh.batch, sh.q_per_req
+    rows_per_page = DMA_PAGE_BYTES // (sh.idx_dim * keys.element_size())
+    assert sh.n_cap % rows_per_page == 0
+    bpr = sh.n_cap // rows_per_page
+    sp = inp["start_pos"].astype(np.int64)
+    vis, score_rows = [], 0
+    for b in range(B):
+        nmax = 0
+        for s in range(S):
+            p = min(max(int(sp[b]) + s, 0), sh.max_len - 1)
+            nv = min((p + 1) // sh.ratio, sh.n_cap)
+            if nv > sh.topk:
+                nmax = max(nmax, nv)
+                score_rows += nv
+        vis.extend(b * bpr + i for i in range(-(-nmax // rows_per_page)))
+    per_wg = DMA_WG_BYTES // DMA_PAGE_BYTES
+    vis += [vis[-1]] * (-len(vis) % per_wg)
+    vis = np.asarray(vis, dtype=np.int32)
+    kbytes = vis.size * DMA_PAGE_BYTES
+    d_vis = torch.from_numpy(vis).cuda()
+    d_rand = torch.from_numpy(np.random.default_rng(5).permutation(vis)).cuda()
+    n_pages = B * bpr
+    snote = (f"bytes: the visible key pages only (the kernel also writes {score_rows * 4 / 1e6:.1f} MB "
+             "of scores)")
     timed("indexer_score kernel", kbytes,
           lambda: C.indexer_score(sh, dev["q_idx"], dev["w"], keys, dev["start_pos"], bufs["scores"], stream),
-          note="bytes: the key stream only (the kernel also writes 16.8 MB of scores)")
+          note=snote)
     timed("probe: LDS-DMA stream, address order", kbytes,
-          lambda: ok(P.csa_ceiling_stream_dma(keys.data_ptr(), kbytes, None, 0, sink.data_ptr(), sptr), "dma"))
+          lambda: ok(P.csa_ceiling_stream_dma(keys.data_ptr(), kbytes, d_vis.data_ptr(), n_pages,
+                                              sink.data_ptr(), sptr), "dma"))
     timed("probe: LDS-DMA stream, random 16 KiB pages", kbytes,
-          lambda: ok(P.csa_ceiling_stream_dma(keys.data_ptr(), kbytes, order.data_ptr(), n_pages,
-                                              sink.data_ptr(), sptr), "dma paged"))
+          lambda: ok(P.csa_ceiling_stream_dma(keys.data_ptr(), kbytes, d_rand.data_ptr(), n_pages,
+                                              sink.data_ptr(), sptr), "dma random"))
     timed("probe: vector-load stream, 128 KiB per workgroup", kbytes,
-          lambda: ok(P.csa_ceiling_stream_vec(keys.data_ptr(), kbytes, 131072, sink.data_ptr(), sptr), "vec"))
+          lambda: ok(P.csa_ceiling_stream_vec(keys.data_ptr(), kbytes, DMA_WG_BYTES, sink.data_ptr(), sptr),
+                     "vec"), note="as many bytes, contiguous from the start of the key cache")
 
     # the same keys in a pool of 64-row (16 KiB) blocks in a seeded random
-    # order: the paged score kernel, and the DMA stream reading the pool
-    # through the same block table
+    # order: the paged score kernel, and the DMA stream reading the same
+    # visible pages through the same block table
     pin = I.page_inputs({"k_idx": inp["k_idx"]}, PAGE_ROWS, seed=11, cmp=False)
+    assert PAGE_ROWS == rows_per_page
     pool = torch.from_numpy(pin["k_idx_pool"].view(np.int16)).view(torch.bfloat16).cuda()
-    table = torch.from_numpy(np.ascontiguousarray(pin["idx_table"], dtype=np.int32)).cuda()
+    tab = np.ascontiguousarray(pin["idx_table"], dtype=np.int32)
+    table = torch.from_numpy(tab).cuda()
     pool_pages = pool.numel() * pool.element_size() // DMA_PAGE_BYTES
-    assert table.numel() == n_pages and PAGE_ROWS * sh.idx_dim * 2 == DMA_PAGE_BYTES
-    assert int(table.min()) >= 0 and int(table.max()) < pool_pages
+    assert tab.size == n_pages and 0 <= tab.min() and tab.max() < pool_pages
+    d_pool_vis = torch.from_numpy(np.ascontiguousarray(tab.reshape(-1)[vis])).cuda()
     timed("indexer_score kernel, paged pool (64-row blocks)", kbytes,
           lambda: C.indexer_score_paged(sh, dev["q_idx"], dev["w"], pool, None, table, dev["start_pos"],
-                                        bufs["scores"], stream),
-          note="bytes: the key stream only (the kernel also writes 16.8 MB of scores)")
+                                        bufs["scores"], stream), note=snote)
     timed("probe: LDS-DMA stream, the paged pool through its block table", kbytes,
-          lambda: ok(P.csa_ceiling_stream_dma(pool.data_ptr(), kbytes, table.data_ptr(), pool_pages,
+          lambda: ok(P.csa_ceiling_stream_dma(pool.data_ptr(), kbytes, d_pool_vis.data_ptr(), pool_pages,
                                               sink.data_ptr(), sptr), "dma pool"))
     del pool, table, pin
 
@@ -177,7 +205,7 @@ def main():
     def score():
         C.indexer_score(sh, dev["q_idx"], dev["w"], keys, dev["start_pos"], scores, stream)
 
-    note = "after the score kernel (untimed) wrote the rows; bytes: the score rows"
+    note = "after the score kernel (untimed) wrote the rows; bytes: the whole score rows"
     timed("topk kernel", sbytes,
           lambda: C.topk(sh, scores, dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream),
           note=note, pre=score)
@@ -228,7 +256,7 @@ def main():
         ok(P.csa_ceiling_stream_vec(dev["v_cmp"].data_ptr(), half, 16384, sink.data_ptr(), sptr), "seq v")
 
     note = "bytes: distinct K and V rows the step's lists and windows name"
-    timed("attention (split + finish kernels)", distinct, attention, note=note)
+    timed("attention (the library's call)", distinct, attention, note=note)
     timed("probe: K/V row gather, the same rows, 4 rows per wave (2 launches)", distinct, gather, note=note)
     timed("probe: sequential read of as many bytes (2 launches)", 2 * half, sequential)
     torch.cuda.synchronize()
