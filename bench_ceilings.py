@@ -62,6 +62,32 @@ def load_ceilings() -> ctypes.CDLL:
     return L
 
 
+def visible_key_pages(sh, start_pos, rows_per_page: int):
+    """The key-cache pages (rows_per_page rows each, numbered b * pages_per_request
+    + i) holding the rows the score kernel reads: per request, its first nmax
+    rows, nmax the largest visible count among its tokens that do not fit
+    Top-K.  Ascending, padded with copies of the last page to whole probe
+    workgroups.  Also returns how many scores the step writes."""
+    if sh.n_cap % rows_per_page:
+        raise ValueError("n_cap must be a whole number of pages")
+    bpr = sh.n_cap // rows_per_page
+    vis, score_rows = [], 0
+    for b in range(sh.batch):
+        nmax = 0
+        for s in range(sh.q_per_req):
+            p = min(max(int(start_pos[b]) + s, 0), sh.max_len - 1)
+            nv = min((p + 1) // sh.ratio, sh.n_cap)
+            if nv > sh.topk:
+                nmax = max(nmax, nv)
+                score_rows += nv
+        vis.extend(b * bpr + i for i in range(-(-nmax // rows_per_page)))
+    if not vis:
+        raise ValueError("no token of this step is scored")
+    per_wg = DMA_WG_BYTES // DMA_PAGE_BYTES
+    vis += [vis[-1]] * (-len(vis) % per_wg)
+    return np.asarray(vis, dtype=np.int32), score_rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=40, help="timed launches per measurement and cache state")
@@ -141,24 +167,10 @@ def main():
     # reads (each request's visible rows, up to the most any of its tokens
     # that do not fit Top-K sees), padded to whole probe workgroups
     keys = dev["k_idx"]
-    B, S = sh.batch, sh.q_per_req
+    B = sh.batch
     rows_per_page = DMA_PAGE_BYTES // (sh.idx_dim * keys.element_size())
-    assert sh.n_cap % rows_per_page == 0
     bpr = sh.n_cap // rows_per_page
-    sp = inp["start_pos"].astype(np.int64)
-    vis, score_rows = [], 0
-    for b in range(B):
-        nmax = 0
-        for s in range(S):
-            p = min(max(int(sp[b]) + s, 0), sh.max_len - 1)
-            nv = min((p + 1) // sh.ratio, sh.n_cap)
-            if nv > sh.topk:
-                nmax = max(nmax, nv)
-                score_rows += nv
-        vis.extend(b * bpr + i for i in range(-(-nmax // rows_per_page)))
-    per_wg = DMA_WG_BYTES // DMA_PAGE_BYTES
-    vis += [vis[-1]] * (-len(vis) % per_wg)
-    vis = np.asarray(vis, dtype=np.int32)
+    vis, score_rows = visible_key_pages(sh, inp["start_pos"], rows_per_page)
     kbytes = vis.size * DMA_PAGE_BYTES
     d_vis = torch.from_numpy(vis).cuda()
     d_rand = torch.from_numpy(np.random.default_rng(5).permutation(vis)).cuda()

@@ -76,3 +76,18 @@ def test_stream_vec_refusals(P, args):
 ])
 def test_gather_refusals(P, args):
     assert P.csa_ceiling_gather(*args, None) == -1
+
+
+def test_visible_key_pages_cover_the_scored_rows():
+    from sparse_attention_decode_csa_amd import inputs as I
+    sh = I.CONFIGS[3].shape.replace(batch=3, n_cap=1024, topk=64, max_len=4000)
+    sp = [3999, 1000, 200]           # visible rows 1000, 250, 50 (the last fits Top-K)
+    vis, scored = BC.visible_key_pages(sh, sp, 64)
+    per_req = 1024 // 64
+    want = list(range(0, 16)) + [per_req + i for i in range(4)]   # ceil(1000/64), ceil(250/64)
+    want += [want[-1]] * (-len(want) % 8)
+    assert vis.tolist() == want
+    assert scored == 1000 + 250
+    assert vis.size % (BC.DMA_WG_BYTES // BC.DMA_PAGE_BYTES) == 0
+    with pytest.raises(ValueError):
+        BC.visible_key_pages(sh, [10, 10, 10], 64)   # nothing scored
