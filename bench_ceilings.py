@@ -17,8 +17,8 @@ that the host's launch overhead stays outside the events):
 - the paged score kernel over a pool of 64-row blocks in a seeded random
   order, and the LDS-DMA stream reading the same pages through the same table;
 - the library's Top-K kernel right after the score kernel (untimed) wrote its
-  rows, and probes that only read those rows (whole rows), one or 8
-  workgroups per row;
+  rows, and probes that only read those rows (whole rows): one 1024-thread
+  workgroup per row (the Top-K's own load), one or 8 256-thread ones;
 - the library's attention call, and a probe that gathers exactly its K and V
   rows (the step's own Top-K lists plus the window rows) 4 rows per wave and
   computes nothing, next to a sequential read of as many bytes.
@@ -55,7 +55,7 @@ def load_ceilings() -> ctypes.CDLL:
     L = ctypes.CDLL(CEILINGS_LIB)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.csa_ceiling_stream_dma.argtypes = [vp, i64, vp, i32, vp, vp]
-    L.csa_ceiling_stream_vec.argtypes = [vp, i64, i32, vp, vp]
+    L.csa_ceiling_stream_vec.argtypes = [vp, i64, i32, i32, vp, vp]
     L.csa_ceiling_gather.argtypes = [vp, vp, i64, vp, i32, vp, vp]
     for f in (L.csa_ceiling_stream_dma, L.csa_ceiling_stream_vec, L.csa_ceiling_gather):
         f.restype = ctypes.c_int
@@ -187,7 +187,7 @@ def main():
           lambda: ok(P.csa_ceiling_stream_dma(keys.data_ptr(), kbytes, d_rand.data_ptr(), n_pages,
                                               sink.data_ptr(), sptr), "dma random"))
     timed("probe: vector-load stream, 128 KiB per workgroup", kbytes,
-          lambda: ok(P.csa_ceiling_stream_vec(keys.data_ptr(), kbytes, DMA_WG_BYTES, sink.data_ptr(), sptr),
+          lambda: ok(P.csa_ceiling_stream_vec(keys.data_ptr(), kbytes, DMA_WG_BYTES, 256, sink.data_ptr(), sptr),
                      "vec"), note="as many bytes, contiguous from the start of the key cache")
 
     # the same keys in a pool of 64-row (16 KiB) blocks in a seeded random
@@ -221,12 +221,15 @@ def main():
     timed("topk kernel", sbytes,
           lambda: C.topk(sh, scores, dev["start_pos"], bufs["topk_idx"], bufs["topk_ws"], stream),
           note=note, pre=score)
-    timed("probe: vector-load read of the score rows, one workgroup per row", sbytes,
-          lambda: ok(P.csa_ceiling_stream_vec(scores.data_ptr(), sbytes, row_bytes, sink.data_ptr(), sptr),
+    timed("probe: read of the score rows, one 1024-thread workgroup per row", sbytes,
+          lambda: ok(P.csa_ceiling_stream_vec(scores.data_ptr(), sbytes, row_bytes, 1024, sink.data_ptr(), sptr),
                      "rows"), note=note, pre=score)
-    timed("probe: vector-load read of the score rows, 8 workgroups per row", sbytes,
-          lambda: ok(P.csa_ceiling_stream_vec(scores.data_ptr(), sbytes, row_bytes // 8, sink.data_ptr(), sptr),
-                     "rows/8"), note=note, pre=score)
+    timed("probe: read of the score rows, one 256-thread workgroup per row", sbytes,
+          lambda: ok(P.csa_ceiling_stream_vec(scores.data_ptr(), sbytes, row_bytes, 256, sink.data_ptr(), sptr),
+                     "rows 256"), note=note, pre=score)
+    timed("probe: read of the score rows, 8 256-thread workgroups per row", sbytes,
+          lambda: ok(P.csa_ceiling_stream_vec(scores.data_ptr(), sbytes, row_bytes // 8, 256, sink.data_ptr(),
+                                              sptr), "rows/8"), note=note, pre=score)
 
     # ---- the attention's row gather ----------------------------------------
     B, S, n_cap, w_cap, W = sh.batch, sh.q_per_req, sh.n_cap, sh.w_cap, sh.win
@@ -264,8 +267,8 @@ def main():
     half = (distinct // 2) // 16384 * 16384
 
     def sequential():
-        ok(P.csa_ceiling_stream_vec(dev["k_cmp"].data_ptr(), half, 16384, sink.data_ptr(), sptr), "seq k")
-        ok(P.csa_ceiling_stream_vec(dev["v_cmp"].data_ptr(), half, 16384, sink.data_ptr(), sptr), "seq v")
+        ok(P.csa_ceiling_stream_vec(dev["k_cmp"].data_ptr(), half, 16384, 256, sink.data_ptr(), sptr), "seq k")
+        ok(P.csa_ceiling_stream_vec(dev["v_cmp"].data_ptr(), half, 16384, 256, sink.data_ptr(), sptr), "seq v")
 
     note = "bytes: distinct K and V rows the step's lists and windows name"
     timed("attention (the library's call)", distinct, attention, note=note)

@@ -12,8 +12,9 @@
  *                           DMA (1 KiB per instruction, non-temporal), either
  *                           in address order or with 16 KiB pages taken in
  *                           the order of a page table (a paged key pool);
- *   csa_ceiling_stream_vec  the same bytes read with plain 16-byte vector
- *                           loads, one contiguous range per workgroup;
+ *   csa_ceiling_stream_vec  bytes read with plain 16-byte vector loads, one
+ *                           contiguous range per workgroup (the key stream
+ *                           without LDS DMA; the Top-K's score rows);
  *   csa_ceiling_gather      the attention's row gather: 256-byte K and V rows
  *                           named by a list of row numbers, 4 rows per wave
  *                           (16 lanes per row, one 16-byte piece per lane).
@@ -58,10 +59,13 @@ int csa_ceiling_stream_dma(const void* src, int64_t bytes, const int32_t* page_o
                            uint32_t* sink, void* stream);
 
 /* Reads `bytes` bytes from `src` with 16-byte vector loads, 8 per thread in
- * flight, one contiguous range of `bytes_per_wg` bytes per 256-thread
- * workgroup.  `bytes_per_wg` must be a positive multiple of 16 that divides
- * `bytes`; `src` 16-byte aligned. */
-int csa_ceiling_stream_vec(const void* src, int64_t bytes, int32_t bytes_per_wg, uint32_t* sink, void* stream);
+ * flight, one contiguous range of `bytes_per_wg` bytes per workgroup of
+ * `threads` threads (256 or 1024; a 1024-thread workgroup over 128 KiB loads
+ * its whole range at once, as the decode Top-K loads a row of 32768 scores).
+ * `bytes_per_wg` must be a positive multiple of 16 that divides `bytes`;
+ * `src` 16-byte aligned. */
+int csa_ceiling_stream_vec(const void* src, int64_t bytes, int32_t bytes_per_wg, int32_t threads, uint32_t* sink,
+                           void* stream);
 
 /* Reads row rows[i] (i < n_rows) of both `k` and `v`, each a cache of
  * 256-byte rows of `cache_bytes` bytes (a multiple of 256, below 2^31).  A

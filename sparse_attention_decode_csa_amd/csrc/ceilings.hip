@@ -81,18 +81,18 @@ __global__ __launch_bounds__(kDmaWaves * 64) void stream_dma_kernel(const char* 
 }
 
 // ---- plain vector-load stream ---------------------------------------------
-constexpr int kVecThreads = 256;
 constexpr int kVecInFlight = 8;
 
-__global__ __launch_bounds__(kVecThreads) void stream_vec_kernel(const char* src, int per_wg, uint32_t* sink) {
+template <int NT>
+__global__ __launch_bounds__(NT) void stream_vec_kernel(const char* src, int per_wg, uint32_t* sink) {
   const u32x4_t* p = reinterpret_cast<const u32x4_t*>(src + (size_t)blockIdx.x * per_wg);
   const int n = per_wg / 16;
   u32x4_t acc = u32x4_t{0, 0, 0, 0};
-  for (int i = threadIdx.x; i < n; i += kVecThreads * kVecInFlight) {
+  for (int i = threadIdx.x; i < n; i += NT * kVecInFlight) {
     u32x4_t v[kVecInFlight];
 #pragma unroll
     for (int u = 0; u < kVecInFlight; ++u) {
-      const int j = i + u * kVecThreads;
+      const int j = i + u * NT;
       v[u] = j < n ? p[j] : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
@@ -142,15 +142,21 @@ int csa_ceiling_stream_dma(const void* src, int64_t bytes, const int32_t* page_o
   return launched();
 }
 
-int csa_ceiling_stream_vec(const void* src, int64_t bytes, int32_t bytes_per_wg, uint32_t* sink, void* stream) {
+int csa_ceiling_stream_vec(const void* src, int64_t bytes, int32_t bytes_per_wg, int32_t threads, uint32_t* sink,
+                           void* stream) {
   using namespace csa;
   if (!src || !sink || bytes <= 0 || bytes_per_wg <= 0 || bytes_per_wg % 16 != 0 || bytes % bytes_per_wg != 0 ||
-      (reinterpret_cast<uintptr_t>(src) & 15))
+      (threads != 256 && threads != 1024) || (reinterpret_cast<uintptr_t>(src) & 15))
     return -1;
   if (bytes / bytes_per_wg > INT32_MAX) return -1;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(stream_vec_kernel, dim3((unsigned)(bytes / bytes_per_wg)), dim3(kVecThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const char*>(src), bytes_per_wg, sink);
+  const dim3 grid((unsigned)(bytes / bytes_per_wg));
+  if (threads == 256)
+    hipLaunchKernelGGL(stream_vec_kernel<256>, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const char*>(src), bytes_per_wg, sink);
+  else
+    hipLaunchKernelGGL(stream_vec_kernel<1024>, grid, dim3(1024), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const char*>(src), bytes_per_wg, sink);
   return launched();
 }
 

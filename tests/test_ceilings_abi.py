@@ -56,11 +56,12 @@ def test_stream_dma_refusals(P, args):
 
 
 @pytest.mark.parametrize("args", [
-    (None, 4096, 1024, FAKE),
-    (FAKE, 4096, 0, FAKE),
-    (FAKE, 4096, 1000, FAKE),                 # not a multiple of 16
-    (FAKE, 4096, 3072, FAKE),                 # does not divide the size
-    (MISALIGNED, 4096, 1024, FAKE),
+    (None, 4096, 1024, 256, FAKE),
+    (FAKE, 4096, 0, 256, FAKE),
+    (FAKE, 4096, 1000, 256, FAKE),            # not a multiple of 16
+    (FAKE, 4096, 3072, 256, FAKE),            # does not divide the size
+    (FAKE, 4096, 1024, 512, FAKE),            # unsupported workgroup size
+    (MISALIGNED, 4096, 1024, 256, FAKE),
 ])
 def test_stream_vec_refusals(P, args):
     assert P.csa_ceiling_stream_vec(*args, None) == -1

@@ -52,11 +52,12 @@ def test_stream_dma_covers_every_byte(P, paged, at):
     assert (int(sink[0].item()) != 0) == (at is not None), (paged, at)
 
 
+@pytest.mark.parametrize("threads", [256, 1024])
 @pytest.mark.parametrize("at", [None, 0, 65536 - 4, 65536, 5 * 65536 + 12340])
-def test_stream_vec_covers_every_byte(P, at):
+def test_stream_vec_covers_every_byte(P, at, threads):
     nbytes = 8 * 65536
     buf, sink = _planted(nbytes, at), _sink()
-    assert P.csa_ceiling_stream_vec(buf.data_ptr(), nbytes, 65536, sink.data_ptr(), _stream_ptr()) == 0
+    assert P.csa_ceiling_stream_vec(buf.data_ptr(), nbytes, 65536, threads, sink.data_ptr(), _stream_ptr()) == 0
     torch.cuda.synchronize()
     assert (int(sink[0].item()) != 0) == (at is not None), at
 
