@@ -207,7 +207,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 
 // Exclusive prefix sum of one int per thread over a block of NW waves, in
 // thread order; also returns the block total.  `red` holds one int per wave.
-template <int NW>
+template <int NW, bool TAIL = true>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int inc = wave_inclusive_scan(v);
@@ -221,7 +221,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* red, int& total)
     before += w < wave ? t : 0;
     total += t;
   }
-  __syncthreads();
+  if (TAIL) __syncthreads();  // red may be written again (callers that never do pass false)
   return before + inc - v;
 }
 
@@ -241,7 +241,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 
 // block_exclusive_scan that also reduces a maximum over the block through
 // the same barriers.  `red` holds two ints per wave.
-template <int NW>
+template <int NW, bool TAIL = true>
 __device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int* red, int& total,
                                                         uint32_t& block_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -262,7 +262,7 @@ __device__ __forceinline__ int block_exclusive_scan_max(int v, uint32_t mx, int*
     total += t;
     block_max = max(block_max, (uint32_t)red[2 * w + 1]);
   }
-  __syncthreads();
+  if (TAIL) __syncthreads();  // red may be written again (callers that never do pass false)
   return before + inc - v;
 }
 
@@ -323,7 +323,7 @@ __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red
 // prefill chunk 102 -> 97 us).  (12-bit digits were measured too: the
 // single-wave scan of 4096 bins cost more than the pass they save.)  No
 // floating point anywhere.
-template <int NW, bool PER_WAVE, int NK, bool FINISH_SMALL, typename Key, typename Valid>
+template <int NW, bool PER_WAVE, int NK, bool FINISH_SMALL, bool CLEARED = false, typename Key, typename Valid>
 __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uint32_t hi,
                                    SelectSmem<NW>& sm, uint32_t& T, int& keq, int max_passes = 4) {
   constexpr int DB = 8, kBins = 1 << DB, NT = NW * kWave;
@@ -334,9 +334,13 @@ __device__ void block_radix_select(Key key, Valid valid, int k, uint32_t lo, uin
   uint32_t pmask = nb == 32 ? 0u : ~((1u << nb) - 1u);
   uint32_t prefix = lo & pmask;
   int krem = k;
-  for (int i = tid; i < kWords; i += NT) sm.hist[0][i] = 0u;
-  if (FINISH_SMALL && tid == 0) sm.nlist = 0;
-  __syncthreads();
+  // CLEARED: the caller guarantees hist[0] is zero and nlist is 0, both
+  // behind a barrier already
+  if (!CLEARED) {
+    for (int i = tid; i < kWords; i += NT) sm.hist[0][i] = 0u;
+    if (FINISH_SMALL && tid == 0) sm.nlist = 0;
+    __syncthreads();
+  }
   int pass = 0;
   for (int top = nb; top > 0; top -= DB, ++pass) {
     const int shift = top > DB ? top - DB : 0;
@@ -452,7 +456,8 @@ __device__ __forceinline__ void emit_selection(Item item, int cnt, uint32_t T, i
   }
   int tot;
   // both counts packed in one int: each block total is at most 32768 < 2^16
-  const int before = block_exclusive_scan<NW>(gt | (eq << 16), red, tot);
+  // every caller ends its kernel after the emission: red is not written again
+  const int before = block_exclusive_scan<NW, false>(gt | (eq << 16), red, tot);
   int eq_rank = before >> 16;
   int dst = (before & 0xFFFF) + min(eq_rank, keq);
 #pragma unroll
@@ -583,8 +588,14 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
     for (int j = 0; j < KPT; ++j) mine += key[j] >= tau ? 1 : 0;
     int c;
     uint32_t row_max;
-    int pos = block_exclusive_scan_max<NW>(mine, kmax, sm.red, c, row_max);
+    // (no barrier after the scan: the candidate path passes two before
+    // sm.red is written again, the fallback one of its own)
+    int pos = block_exclusive_scan_max<NW, false>(mine, kmax, sm.red, c, row_max);
     if (c >= K && c <= kCandCap) {  // block-uniform
+      // the sample select's second (last) pass cleared hist[0], so the exact
+      // select below starts without clearing it; the barrier after the
+      // candidates makes nlist's reset visible too
+      if (tid == 0) sm.nlist = 0;
       // only candidates are written (measured a little faster than writing
       // every slot with the misses sent to a spare slot)
 #pragma unroll
@@ -598,7 +609,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
       // shared histogram
       uint32_t T;
       int keq;
-      block_radix_select<NW, false, kCandPerThread, true>(
+      block_radix_select<NW, false, kCandPerThread, true, /*CLEARED=*/true>(
           [&](int r) { return cand[min(r * NT + tid, c - 1)].x; },
           [&](int r) { return r * NT + tid < c; }, K, tau, row_max, sm, T, keq);
       // emission over the candidates only: thread t takes a contiguous run
@@ -608,6 +619,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
                                          sm.red);
       return;
     }
+    __syncthreads();  // every thread has read the scan's sm.red before the fallback writes it
   }
   // ---- whole-row selection and emission
   uint32_t kmin = 0xFFFFFFFFu;
