@@ -282,7 +282,7 @@ struct alignas(16) SelectSmem {  // 16-byte aligned: the bin scan reads uint4
 
 // Block-wide minimum and maximum of one key per thread (invalid threads pass
 // UINT32_MAX / 0).  `red` holds two ints per wave.
-template <int NW>
+template <int NW, bool TAIL = true>
 __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red, uint32_t& mn,
                                               uint32_t& mx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -303,7 +303,7 @@ __device__ __forceinline__ void block_min_max(uint32_t lo, uint32_t hi, int* red
     mn = min(mn, (uint32_t)red[2 * w]);
     mx = max(mx, (uint32_t)red[2 * w + 1]);
   }
-  __syncthreads();
+  if (TAIL) __syncthreads();  // red may be written again (callers that never do pass false)
 }
 
 // Exact selection over keys spread across the block: thread t holds NK keys,
@@ -509,6 +509,15 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
     for (int i = tid; i < K; i += NT) out[i] = i < n ? i : -1;
     return;
   }
+  // (a sampled threshold keeps somewhat more than K rows: only tried while
+  // K leaves room for that in the buffer)
+  const bool cand_path = kCandPath && n > kCandCap && 2 * K <= kCandCap;  // block-uniform
+  if (cand_path) {
+    // the sample select's first histogram, cleared while the row is still
+    // arriving, behind a barrier that does not wait for the row's loads
+    if (tid < 256) sm.hist[0][tid] = 0u;
+    block_lds_barrier();
+  }
 
   // ---- the row, in registers.  Slots past n hold a copy of a valid key of
   // the same thread (or of row n-1), so they never widen the key range.
@@ -535,9 +544,7 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 1; j < KPT; ++j) kmax = max(kmax, key[j]);
 
-  // (a sampled threshold keeps somewhat more than K rows: only tried while
-  // K leaves room for that in the buffer)
-  if constexpr (kCandPath) if (n > kCandCap && 2 * K <= kCandCap) {
+  if constexpr (kCandPath) if (cand_path) {
     __shared__ uint2 cand[kCandCap];  // (key, row index)
     constexpr int kCandPerThread = kCandCap / NT;
     // ---- threshold from a strided sample.  Thread t offers NS rows, one from
@@ -576,8 +583,8 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
     const int ks = min(m, ks0 + 3 * (int)sqrtf((float)ks0) + 4);
     uint32_t tau;
     int unused;
-    block_radix_select<NW, false, NS, false>([&](int r) { return sk[r]; }, [&](int r) { return sv[r]; },
-                                             ks, 0u, 0xFFFFFFFFu, sm, tau, unused, 2);
+    block_radix_select<NW, false, NS, false, /*CLEARED=*/true>(
+        [&](int r) { return sk[r]; }, [&](int r) { return sv[r]; }, ks, 0u, 0xFFFFFFFFu, sm, tau, unused, 2);
     // ---- rows at or above the threshold, compacted in row order; the same
     // barriers give the row maximum
     // slots past n hold key 0, and no float has key 0: against a threshold of
@@ -626,11 +633,16 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) kmin = min(kmin, valid(j) ? key[j] : 0xFFFFFFFFu);
   uint32_t row_min, row_max;
-  block_min_max<NW>(kmin, kmax, sm.red, row_min, row_max);
+  // the select's first histogram and list, cleared behind the reduction's
+  // barrier (nothing reads them before); the reduction's sm.red is written
+  // again only by the emission, behind the select's barriers
+  for (int i = tid; i < NW * kHistStride; i += NT) sm.hist[0][i] = 0u;
+  if (tid == 0) sm.nlist = 0;
+  block_min_max<NW, false>(kmin, kmax, sm.red, row_min, row_max);
   uint32_t T;
   int keq;
-  block_radix_select<NW, true, KPT, true>([&](int j) { return key[j]; }, valid, K, row_min, row_max,
-                                          sm, T, keq);
+  block_radix_select<NW, true, KPT, true, /*CLEARED=*/true>([&](int j) { return key[j]; }, valid, K, row_min,
+                                                            row_max, sm, T, keq);
   const int cnt = max(0, min(KPT, n - i0));
   emit_selection<NW, KPT>([&](int j) { return make_uint2(key[j], (uint32_t)(i0 + j)); }, cnt, T,
                           keq, out, K, sm.red);
