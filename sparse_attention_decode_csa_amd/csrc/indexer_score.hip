@@ -317,10 +317,14 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
   if constexpr (HI > 0) {
     // The block's scores of each token are staged through the tile buffers
     // (idle once every wave has left the tile loop) and written as contiguous
-    // 16-byte pieces with the streaming hint.  One scattered 64-byte write
-    // per tile and token, interleaved with the key stream, cost more than
-    // their share of the traffic.
+    // 16-byte pieces, with the streaming hint when the step's scores are many
+    // (stream_scores).  One scattered 64-byte write per tile and token,
+    // interleaved with the key stream, cost more than their share of the
+    // traffic.
     constexpr int kStageTok = (int)sizeof(tiles) / (kScoreKeysPerBlock * 4);  // tokens per pass
+    // the block's score rows (S tokens; below 2^31 bytes: S <= 64 and the
+    // host bounds n_cap)
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(srow, (int)((size_t)S * a.n_cap * 4));
     static_assert(kStageTok >= 1, "the tile buffers hold at least one token's scores");
     float* stage = reinterpret_cast<float*>(&tiles[0][0][0]);
     const bool writer = (g & (HI / 4 - 1)) == 0;  // lanes holding a finished head sum
@@ -343,15 +347,29 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         const int nv = min(n_visible(clamp_pos(sp + s, a.max_len), a.ratio), a.n_cap);
         const int j0 = key0 + 4 * q4;
         if (nv <= a.topk || j0 >= nv) continue;  // Top-K bypass, or past the visible rows
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + ts * kScoreKeysPerBlock + 4 * q4);
-        float* dst = srow + (size_t)s * a.n_cap + j0;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + ts * kScoreKeysPerBlock + 4 * q4);
+        const int off = (int)(((size_t)s * a.n_cap + j0) * 4);  // in the block's rows (srs)
+        // Buffer stores whose cache policy is an immediate: two stores that
+        // differ only in a hint would be merged into one without it.
         if (j0 + 4 <= nv && (a.n_cap & 3) == 0) {  // whole piece, 16-byte aligned row
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(dst));
+          if (a.stream_scores)
+            __builtin_amdgcn_raw_buffer_store_b128(v, srs, off, 0, kNonTemporal);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(v, srs, off, 0, 0);
         } else {
-          __builtin_nontemporal_store(v[0], dst);  // j0 < nv
-          if (j0 + 1 < nv) __builtin_nontemporal_store(v[1], dst + 1);
-          if (j0 + 2 < nv) __builtin_nontemporal_store(v[2], dst + 2);
-          if (j0 + 3 < nv) __builtin_nontemporal_store(v[3], dst + 3);
+          const uint32_t e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];  // constant indices
+          const int m = nv - j0;  // 1 .. 3
+          if (a.stream_scores) {
+            __builtin_amdgcn_raw_buffer_store_b32(e0, srs, off, 0, kNonTemporal);
+            if (m > 1) __builtin_amdgcn_raw_buffer_store_b32(e1, srs, off + 4, 0, kNonTemporal);
+            if (m > 2) __builtin_amdgcn_raw_buffer_store_b32(e2, srs, off + 8, 0, kNonTemporal);
+            if (m > 3) __builtin_amdgcn_raw_buffer_store_b32(e3, srs, off + 12, 0, kNonTemporal);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(e0, srs, off, 0, 0);
+            if (m > 1) __builtin_amdgcn_raw_buffer_store_b32(e1, srs, off + 4, 0, 0);
+            if (m > 2) __builtin_amdgcn_raw_buffer_store_b32(e2, srs, off + 8, 0, 0);
+            if (m > 3) __builtin_amdgcn_raw_buffer_store_b32(e3, srs, off + 12, 0, 0);
+          }
         }
       }
     }
@@ -781,6 +799,16 @@ hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
   // else blocks of floor(64 / Hi) tokens (prefill chunks).
   ScoreArgs a = in;
   a.tok_per_block = a.q_per_req * a.idx_heads <= 64 ? a.q_per_req : 64 / a.idx_heads;
+  // Streaming (non-temporal) score stores when the step writes many scores:
+  // they then keep the key stream's traffic in order (wide Top-K step, 16 MiB
+  // of scores: score kernel 91.9 -> 88.3 us, Top-K after it 17.1 -> 17.7 us);
+  // a few scores are better kept in the caches the Top-K reads them from
+  // (long-context step, 1 MiB: score kernel 12.9 -> 12.5 us, Top-K 12.3 ->
+  // 11.9 us with ordinary stores).
+#ifndef CSA_SCORE_STREAM_MIN_BYTES
+#define CSA_SCORE_STREAM_MIN_BYTES (4ll << 20)
+#endif
+  a.stream_scores = (long long)a.batch * a.q_per_req * n_bound * 4 >= CSA_SCORE_STREAM_MIN_BYTES;
   const int row_blocks = (a.q_per_req + a.tok_per_block - 1) / a.tok_per_block;
   if (row_blocks > 65535) return hipErrorInvalidValue;
   dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch, row_blocks);

@@ -25,6 +25,7 @@ struct ScoreArgs {
   int blocks_per_req, block_shift;
   int64_t n_blocks;
   int gemm_key_blocks, gemm_row_blocks;  // GEMM-shaped prefill grid (set by the launcher)
+  int stream_scores;        // decode-shaped kernel: non-temporal score stores (set by the launcher)
 };
 
 struct TopkArgs {
