@@ -322,9 +322,9 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
     // interleaved with the key stream, cost more than their share of the
     // traffic.
     constexpr int kStageTok = (int)sizeof(tiles) / (kScoreKeysPerBlock * 4);  // tokens per pass
-    // the block's score rows (S tokens; below 2^31 bytes: S <= 64 and the
-    // host bounds n_cap)
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(srow, (int)((size_t)S * a.n_cap * 4));
+    // the block's score rows, S tokens (the launcher takes the global-store
+    // form, stream_scores == 2, when they could reach 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(srow, a.stream_scores == 2 ? 0 : (int)((size_t)S * a.n_cap * 4));
     static_assert(kStageTok >= 1, "the tile buffers hold at least one token's scores");
     float* stage = reinterpret_cast<float*>(&tiles[0][0][0]);
     const bool writer = (g & (HI / 4 - 1)) == 0;  // lanes holding a finished head sum
@@ -348,6 +348,20 @@ __global__ __launch_bounds__(256) void indexer_score_kernel(ScoreArgs a) {
         const int j0 = key0 + 4 * q4;
         if (nv <= a.topk || j0 >= nv) continue;  // Top-K bypass, or past the visible rows
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + ts * kScoreKeysPerBlock + 4 * q4);
+        if (a.stream_scores == 2) {  // rows past 32-bit offsets: 64-bit addresses, streaming
+          float* dst = srow + (size_t)s * a.n_cap + j0;
+          const uint32_t m = (uint32_t)min(4, nv - j0);
+          if (m == 4 && (a.n_cap & 3) == 0) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
+          } else {
+            const uint32_t e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];  // constant indices
+            __builtin_nontemporal_store(e0, reinterpret_cast<uint32_t*>(dst));
+            if (m > 1) __builtin_nontemporal_store(e1, reinterpret_cast<uint32_t*>(dst + 1));
+            if (m > 2) __builtin_nontemporal_store(e2, reinterpret_cast<uint32_t*>(dst + 2));
+            if (m > 3) __builtin_nontemporal_store(e3, reinterpret_cast<uint32_t*>(dst + 3));
+          }
+          continue;
+        }
         const int off = (int)(((size_t)s * a.n_cap + j0) * 4);  // in the block's rows (srs)
         // Buffer stores whose cache policy is an immediate: two stores that
         // differ only in a hint would be merged into one without it.
@@ -809,6 +823,9 @@ hipError_t launch_indexer_score(const ScoreArgs& in, hipStream_t st) {
 #define CSA_SCORE_STREAM_MIN_BYTES (4ll << 20)
 #endif
   a.stream_scores = (long long)a.batch * a.q_per_req * n_bound * 4 >= CSA_SCORE_STREAM_MIN_BYTES;
+  // a workgroup's score rows are reached by 32-bit buffer offsets below 2^31
+  // bytes; past that (n_cap in the millions) by 64-bit streaming stores
+  if ((long long)a.tok_per_block * a.n_cap * 4 > 0x7FFFF000LL) a.stream_scores = 2;
   const int row_blocks = (a.q_per_req + a.tok_per_block - 1) / a.tok_per_block;
   if (row_blocks > 65535) return hipErrorInvalidValue;
   dim3 grid((n_bound + kScoreKeysPerBlock - 1) / kScoreKeysPerBlock, a.batch, row_blocks);

@@ -25,7 +25,9 @@ struct ScoreArgs {
   int blocks_per_req, block_shift;
   int64_t n_blocks;
   int gemm_key_blocks, gemm_row_blocks;  // GEMM-shaped prefill grid (set by the launcher)
-  int stream_scores;        // decode-shaped kernel: non-temporal score stores (set by the launcher)
+  int stream_scores;        // decode-shaped kernel's score stores (set by the launcher): 0 buffer
+                            // stores, 1 non-temporal buffer stores, 2 non-temporal global stores
+                            // (rows past 32-bit offsets)
 };
 
 struct TopkArgs {

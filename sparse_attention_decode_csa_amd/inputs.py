@@ -306,7 +306,8 @@ def _plant(part: str, g: np.random.Generator, g_tie: np.random.Generator, k_idx:
 
 def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
                 shape: Optional[Shape] = None, start_pos: Optional[np.ndarray] = None,
-                structure: Optional[str] = None, key_format: str = "bf16") -> Dict[str, np.ndarray]:
+                structure: Optional[str] = None, key_format: str = "bf16",
+                indexer_only: bool = False) -> Dict[str, np.ndarray]:
     """Draw every input of one decode step.
 
     Returns a dict of contiguous numpy arrays:
@@ -320,6 +321,8 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
     k_idx8 [B,N_cap,Di] uint8 E4M3 codes and k_scale [B,N_cap] float32, each
     row quantised from the keys drawn above (so planted rows, duplicated
     rows and poison keep their meaning); k_idx is then left out.
+    With indexer_only only start_pos, q_idx, w and the indexer keys are drawn
+    (each tensor has its own child stream, so their values do not change).
     """
     cfg = CONFIGS[cfg_id_or_cfg] if isinstance(cfg_id_or_cfg, int) else cfg_id_or_cfg
     sh = shape or cfg.shape
@@ -337,11 +340,13 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
     jobs = dict(q=(_T_Q, (B, S, H, D)), k_win=(_T_KWIN, (B, Wc, D)), v_win=(_T_VWIN, (B, Wc, D)),
                 k_cmp=(_T_KCMP, (B, Nc, D)), v_cmp=(_T_VCMP, (B, Nc, D)),
                 q_idx=(_T_QIDX, (B, S, Hi, Di)), k_idx=(_T_KIDX, (B, Nc, Di)))
+    if indexer_only:
+        jobs = {k: v for k, v in jobs.items() if k in ("q_idx", "k_idx")}
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         futs = {k: ex.submit(_normal, seed, tid, shp) for k, (tid, shp) in jobs.items()}
         drawn = {k: f.result() for k, f in futs.items()}
-    q, k_win, v_win = drawn["q"], drawn["k_win"], drawn["v_win"]
-    k_cmp, v_cmp, q_idx, k_idx = drawn["k_cmp"], drawn["v_cmp"], drawn["q_idx"], drawn["k_idx"]
+    q, k_win, v_win = drawn.get("q"), drawn.get("k_win"), drawn.get("v_win")
+    k_cmp, v_cmp, q_idx, k_idx = drawn.get("k_cmp"), drawn.get("v_cmp"), drawn["q_idx"], drawn["k_idx"]
     w = _rng(seed, _T_W).random(size=(B, S, Hi), dtype=np.float32)
 
     g = _rng(seed, _T_STRUCT)
@@ -352,10 +357,12 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
     if poison:
         for b in range(B):
             nv = int(last_vis[b])
+            k_idx[b, nv:] = POISON
+            if indexer_only:
+                continue
             if not cfg.supplied_topk:
                 k_cmp[b, nv:] = POISON
                 v_cmp[b, nv:] = POISON
-            k_idx[b, nv:] = POISON
             lo = max(0, int(sp[b]) - sh.win + 1)
             hi = int(sp[b]) + S - 1
             live = np.zeros(Wc, dtype=bool)
@@ -363,14 +370,17 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
             k_win[b, ~live] = POISON
             v_win[b, ~live] = POISON
 
-    cos, sin = rope_tables(sh.max_len, sh.rope_dim)
     raw = dict(q=q, k_win=k_win, v_win=v_win, k_cmp=k_cmp, v_cmp=v_cmp, q_idx=q_idx, k_idx=k_idx)
+    raw = {k: v for k, v in raw.items() if v is not None}
     del q, k_win, v_win, k_cmp, v_cmp, q_idx, k_idx, drawn
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(raw)) as ex:
         futs = {k: ex.submit(_store, v, dt) for k, v in raw.items()}
         out = {k: f.result() for k, f in futs.items()}
     del raw
-    out.update(start_pos=sp, w=np.ascontiguousarray(w, np.float32), rope_cos=cos, rope_sin=sin)
+    out.update(start_pos=sp, w=np.ascontiguousarray(w, np.float32))
+    if not indexer_only:
+        cos, sin = rope_tables(sh.max_len, sh.rope_dim)
+        out.update(rope_cos=cos, rope_sin=sin)
     if key_format == "fp8":
         kf = out.pop("k_idx")
         codes = np.empty(kf.shape, dtype=np.uint8)
@@ -380,7 +390,7 @@ def make_inputs(cfg_id_or_cfg, seed: Optional[int] = None, poison: bool = True,
         out.update(k_idx8=codes, k_scale=scales)
     elif key_format != "bf16":
         raise ValueError(key_format)
-    if cfg.supplied_topk:
+    if cfg.supplied_topk and not indexer_only:
         # The HCA-shaped case attends every compressed row it is given.
         K = sh.topk
         ti = np.full((B, S, K), -1, dtype=np.int32)

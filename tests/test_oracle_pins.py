@@ -655,3 +655,15 @@ def test_out_of_range_indices_are_padding():
     c = oracle.run(sh, inp, jobs=oracle.JOB_ATTN, topk_idx=ti)["out"]
     assert np.array_equal(a, b)
     assert not np.array_equal(a, c)
+
+
+def test_indexer_only_inputs_equal_the_full_draw():
+    # Each tensor has its own child stream: drawing only the indexer's
+    # tensors gives them the same values as the full draw.
+    sh = I.CONFIGS[3].shape.replace(batch=2, n_cap=2048, max_len=8192)
+    sp = np.array([8000, 5000], dtype=np.int32)
+    full = I.make_inputs(3, shape=sh, start_pos=sp)
+    part = I.make_inputs(3, shape=sh, start_pos=sp, indexer_only=True)
+    assert set(part) == {"start_pos", "q_idx", "w", "k_idx"}
+    for k in part:
+        assert np.array_equal(part[k], full[k]), k
