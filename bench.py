@@ -26,6 +26,7 @@ timed on the host as a baseline.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -307,8 +308,12 @@ def main():
 
     # timed region: exactly K steps between two synchronisations.  Flushed:
     # each step after a flush, bracketed by its own pair of events.  Hot: back
-    # to back, wall time.
+    # to back, wall time.  The garbage collector is held off while timing (a
+    # full collection of the harness's objects stalled the launch loop for
+    # tens of ms in some hot passes).
     hot_steps = args.steps
+    gc.collect()
+    gc.disable()
     step_us = []
     if args.cache == "flushed":
         sev = [ev_set() for _ in range(args.steps)]
@@ -356,6 +361,7 @@ def main():
             del g
         except Exception as e:  # reported, not fatal: the headline does not depend on it
             graph_hot = {"error": f"{type(e).__name__}: {e}"[:300]}
+    gc.enable()
     if args.cache == "flushed":
         ms_per_step = float(np.median(step_us)) * 1e-3
     else:
