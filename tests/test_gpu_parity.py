@@ -822,6 +822,40 @@ def test_random_shapes_exact_grid(seed, prefill):
     U.compare_outputs(sh, got["out"], ref["out"])
 
 
+def random_long_rows_case(seed):
+    """A seeded random decode shape whose rows run past 8192 keys (the
+    one-workgroup Top-K's sampled-threshold path), N(0,1) inputs."""
+    g = np.random.default_rng([seed, 991])
+    B, S = int(g.integers(1, 4)), int(g.integers(1, 4))
+    K = int(g.choice([64, 256, 257, 512, 1024, 2048]))
+    n_cap = int(g.integers(8193, 40001))
+    max_len = int(g.integers(4 * 8000, n_cap * 4 + 1))
+    win, heads = int(g.integers(1, 257)), int(g.integers(1, 17))
+    divs = [d for d in range(1, heads + 1) if heads % d == 0]
+    D = int(g.choice([64, 128]))
+    cfg = small_cfg(name="long", seed=seed, batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=K, win=win,
+                    w_cap=win + S - 1 + int(g.integers(0, 50)), heads=heads, head_dim=D,
+                    rope_dim=int(g.choice([0, 32, D])), idx_heads=int(g.choice([1, 4, 8, 16])),
+                    idx_dim=int(g.choice([64, 128])), out_groups=int(g.choice(divs)), max_len=max_len,
+                    dtype=I.BF16)
+    sp = g.integers(max_len // 2, max_len - S + 1, size=B).astype(np.int32)
+    return cfg.shape, I.make_inputs(cfg, start_pos=sp, structure="none")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_long_rows(seed):
+    # rows of 8k-40k keys and K from 64 to 2048: scores within the bound,
+    # unscored entries untouched, and the Top-K lists bitwise on the
+    # oracle's own scores
+    sh, inp = random_long_rows_case(seed)
+    print(f"seed {seed}: {sh}", flush=True)
+    ref = oracle_step(sh, inp, jobs=oracle.JOB_SCORE | oracle.JOB_TOPK)
+    got = gpu_step(sh, inp, jobs=("score",))
+    check_scores(sh, inp, got, ref)
+    lists = gpu_step(sh, inp, scores=ref["scores"], jobs=("topk",))["topk_idx"]
+    assert np.array_equal(lists, ref["topk_idx"])
+
+
 def test_determinism(config_inputs):
     cid = 3
     sh, inp = I.CONFIGS[cid].shape, config_inputs(cid)
