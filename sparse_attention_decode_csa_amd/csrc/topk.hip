@@ -612,18 +612,22 @@ __global__ __launch_bounds__(NW * kWave) void topk_reg_kernel(TopkArgs a) {
         pos += hit ? 1 : 0;
       }
       __syncthreads();
+      // thread t takes a contiguous run of the candidates (so the emission
+      // stays in row order) into registers, all its LDS reads in flight at
+      // once: the radix passes and the small-bin list then read no LDS
+      const int cpt = (c + NT - 1) / NT;
+      const int c0 = min(c, tid * cpt), cnt = min(c, c0 + cpt) - c0;
+      uint2 cv[kCandPerThread];
+#pragma unroll
+      for (int j = 0; j < kCandPerThread; ++j) cv[j] = j < cnt ? cand[c0 + j] : make_uint2(0u, 0u);
       // every candidate lies in [tau, row max]; few keys per thread, so one
       // shared histogram
       uint32_t T;
       int keq;
       block_radix_select<NW, false, kCandPerThread, true, /*CLEARED=*/true>(
-          [&](int r) { return cand[min(r * NT + tid, c - 1)].x; },
-          [&](int r) { return r * NT + tid < c; }, K, tau, row_max, sm, T, keq);
-      // emission over the candidates only: thread t takes a contiguous run
-      const int cpt = (c + NT - 1) / NT;
-      const int c0 = min(c, tid * cpt), cnt = min(c, c0 + cpt) - c0;
-      emit_selection<NW, kCandPerThread>([&](int j) { return cand[c0 + j]; }, cnt, T, keq, out, K,
-                                         sm.red);
+          [&](int r) { return cv[r].x; }, [&](int r) { return r < cnt; }, K, tau, row_max, sm, T, keq);
+      // emission over the candidates only
+      emit_selection<NW, kCandPerThread>([&](int j) { return cv[j]; }, cnt, T, keq, out, K, sm.red);
       return;
     }
     __syncthreads();  // every thread has read the scan's sm.red before the fallback writes it
