@@ -514,4 +514,15 @@ def random_scores(seed: int, B: int, S: int, n_cap: int, kind: str = "normal") -
         z = g.random(size=(B, S, n_cap)) < 0.5
         s[(s == 0) & z] = -0.0
         return s
+    if kind in ("sorted", "rsorted"):   # monotone rows: the winners sit at one end
+        v = np.sort(g.standard_normal(size=(B, S, n_cap), dtype=np.float32), axis=-1)
+        return v if kind == "sorted" else np.ascontiguousarray(v[..., ::-1])
+    if kind == "clustered":   # a band of 3000 high scores at a random offset in each row
+        v = g.standard_normal(size=(B, S, n_cap), dtype=np.float32)
+        for r in v.reshape(-1, n_cap):
+            a = int(g.integers(0, n_cap))
+            r[a:a + 3000] += 6.0
+        return v
+    if kind == "equal":   # one value everywhere: only the row index decides
+        return np.full((B, S, n_cap), 1.5, np.float32)
     raise ValueError(kind)

@@ -631,6 +631,55 @@ def test_topk_many_tokens(kind, n_cap, topk):
     assert np.array_equal(out.cpu().numpy(), ref["topk_idx"])
 
 
+RANDOM_KINDS = ["normal", "coarse", "signed_zero", "spiked16", "sorted", "rsorted", "clustered", "equal"]
+
+
+def _random_topk_launch(g, prefill):
+    if prefill:   # 2048 tokens or more: the small-block selection of prefill chunks
+        B, S = int(g.integers(1, 3)), int(g.integers(2048, 2600))
+        n_cap = int(g.choice([2049, 3000, 4096, 6001, 8192]))
+        topk = int(g.choice([64, 256, 512, 1000, 1024]))
+    else:         # decode launches, rows up to past the two-pass length
+        B, S = int(g.integers(1, 7)), int(g.integers(1, 4))
+        n_cap = int(g.choice([1024, 4097, 8192, 8193, 9000, 12345, 16384, 20000, 32768, 40000]))
+        topk = int(g.choice([1, 7, 64, 256, 257, 512, 1000, 1024, 2048, 4096]))
+    max_len = 4 * n_cap + int(g.integers(0, 4))
+    sh = I.Shape(batch=B, q_per_req=S, ratio=4, n_cap=n_cap, topk=topk, win=8, w_cap=S + 8, heads=1,
+                 head_dim=64, rope_dim=0, idx_heads=1, idx_dim=64, out_groups=1, max_len=max_len,
+                 dtype=I.BF16)
+    lo = max(0, max_len - S - int(g.integers(1, max_len // 2 + 2)))   # mostly long visible rows
+    sp = g.integers(lo, max_len - S + 1, size=B).astype(np.int32)
+    kind = RANDOM_KINDS[int(g.integers(0, len(RANDOM_KINDS)))]
+    scores = I.random_scores(int(g.integers(0, 1 << 30)), B, S, n_cap, kind)
+    ref = oracle.run(sh, dict(start_pos=sp), jobs=oracle.JOB_TOPK, scores=scores, nthreads=NTHREADS)
+    out = torch.full((B, S, topk), -7, dtype=torch.int32, device="cuda")
+    C.topk(sh, torch.from_numpy(scores).cuda(), torch.from_numpy(sp).cuda(), out, C.alloc_topk_workspace(sh))
+    torch.cuda.synchronize()
+    return (B, S, n_cap, topk, kind), out.cpu().numpy(), ref["topk_idx"]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_random_launches(seed):
+    # Seeded random decode launches: batch, tokens, row capacity (every
+    # selection form: bypass, whole row, sampled threshold and its fallback,
+    # two passes), K from 1 to 4096, positions mostly near the end of the
+    # cache, and row kinds from plain to adversarial (monotone rows, a band of
+    # winners, one value everywhere).  Four launches per seed; the lists must
+    # equal the oracle's bit for bit.
+    g = np.random.default_rng([seed, 77])
+    for case in range(4):
+        what, got, ref = _random_topk_launch(g, prefill=False)
+        assert np.array_equal(got, ref), (seed, case, what)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_random_prefill_launches(seed):
+    # The same for launches of 2048 to 5200 tokens (small blocks, several per CU).
+    g = np.random.default_rng([seed, 78])
+    what, got, ref = _random_topk_launch(g, prefill=True)
+    assert np.array_equal(got, ref), (seed, what)
+
+
 @pytest.mark.parametrize("topk", [256, 257, 1024])
 def test_topk_winners_past_256(topk):
     n_cap = 8192
